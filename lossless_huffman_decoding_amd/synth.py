@@ -1,0 +1,195 @@
+"""Seeded synthetic bf16 layers for the decoder's workloads.
+
+This module only draws numbers and rounds them to bf16; it holds none of the
+codec's arithmetic (no histograms, code lengths or bit packing), so both the
+CPU oracle's tests and the GPU path's tests and benchmark may use it.
+
+The shapes and distributions stand in for the real bf16 trunk bytes the pages
+measured (Kimi K3 trunk compression page, sections on background and on the
+entropy of the bf16 high byte: layers of ~1.17 GB, a high byte of ~2.8 bit);
+the heavy-tailed layer follows the ECF8 page's alpha-stable weight model
+(section 1.1). The real bytes are not available, so every config is drawn here
+from a numpy PCG64 generator with a fixed seed.
+
+Every generator returns a C-contiguous ``numpy.uint8`` array holding the layer's
+little-endian bf16 bytes (even offsets: low/mantissa byte, odd offsets: high
+sign+exponent byte).
+"""
+
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+SEED_BASE = 20260729
+
+# one "trunk layer" is 1.17 decimal GB of bf16 (93 layers make 108.81 GB)
+TRUNK_LAYER_BYTES = 1_170_000_000
+
+# repeating tensor cycle of a trunk layer: ("W", rows, cols) weight matrices with
+# a per-tensor scale, ("g", n) 1-D norm gains around 1.0
+TRUNK_CYCLE = (
+    ("W", 7168, 7168),
+    ("g", 7168),
+    ("W", 7168, 2048),
+    ("W", 2048, 7168),
+    ("W", 7168, 576),
+    ("g", 7168),
+)
+
+
+def f64_to_bf16_bytes(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 via float32, round-to-nearest-even on the
+    float32 bit pattern, and return the little-endian bf16 bytes (uint8)."""
+    f32 = np.ascontiguousarray(x, dtype=np.float32)
+    u = f32.view(np.uint32)
+    # RNE: add 0x7FFF plus the lowest kept bit, then drop the low 16 bits.
+    # Inputs are finite, so u + 0x8000 cannot wrap and no NaN case is needed.
+    r = ((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
+    return r.view(np.uint8)
+
+
+# Large layers are drawn in fixed chunks of CHUNK values; chunk c of stream
+# `key` uses numpy.random.default_rng(key + (c,)), so chunks are independent
+# and can be drawn on several threads without changing the result.
+CHUNK = 1 << 22
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _fill_chunks(out: np.ndarray, v0: int, n: int, key: tuple, draw) -> None:
+    """Write n bf16 values starting at value index v0 of ``out``; chunk c gets
+    ``draw(rng, m)`` (float64) with rng seeded by key + (c,)."""
+    def job(c):
+        p = c * CHUNK
+        m = min(CHUNK, n - p)
+        rng = np.random.default_rng(key + (c,))
+        out[2 * (v0 + p): 2 * (v0 + p + m)] = f64_to_bf16_bytes(draw(rng, m))
+    nch = -(-n // CHUNK)
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(job, range(nch)))
+
+
+def tiny(seed: int = SEED_BASE + 1) -> np.ndarray:
+    """4 MiB: 2,097,152 values iid N(0, 0.02) rounded to bf16 (one partial stripe)."""
+    rng = np.random.default_rng(seed)
+    return f64_to_bf16_bytes(rng.standard_normal(2_097_152) * 0.02)
+
+
+def trunk_layer(seed: int = SEED_BASE + 2, n_bytes: int = TRUNK_LAYER_BYTES) -> np.ndarray:
+    """A trunk-layer-sized buffer: the TRUNK_CYCLE repeated and truncated to
+    ``n_bytes``. Tensor t (counting from 0 along the layer) is drawn from
+    the streams keyed (seed, t); a weight matrix is N(0, s) with its own s
+    log-uniform in [0.005, 0.05] (drawn first from default_rng((seed, t))),
+    a gain vector is N(1.0, 0.05)."""
+    if n_bytes % 2:
+        raise ValueError("bf16 layer needs an even byte count")
+    n_vals = n_bytes // 2
+    out = np.empty(n_bytes, dtype=np.uint8)
+    pos = 0
+    t = 0
+    lo, hi = math.log(0.005), math.log(0.05)
+    while pos < n_vals:
+        spec = TRUNK_CYCLE[t % len(TRUNK_CYCLE)]
+        cnt = spec[1] * spec[2] if spec[0] == "W" else spec[1]
+        take = min(cnt, n_vals - pos)
+        if spec[0] == "W":
+            s = math.exp(np.random.default_rng((seed, t)).uniform(lo, hi))
+            _fill_chunks(out, pos, take, (seed, t, 1),
+                         lambda rng, m, s=s: rng.standard_normal(m) * s)
+        else:
+            _fill_chunks(out, pos, take, (seed, t, 1),
+                         lambda rng, m: 1.0 + 0.05 * rng.standard_normal(m))
+        pos += take
+        t += 1
+    return out
+
+
+def _alpha_stable_sym(rng: np.random.Generator, n: int, alpha: float) -> np.ndarray:
+    """Symmetric (beta = 0) alpha-stable draws, unit scale, by the
+    Chambers-Mallows-Stuck (1976) construction."""
+    v = rng.uniform(-math.pi / 2, math.pi / 2, n)
+    w = rng.exponential(1.0, n)
+    return (np.sin(alpha * v) / np.cos(v) ** (1.0 / alpha)) * (
+        np.cos(v - alpha * v) / w) ** ((1.0 - alpha) / alpha)
+
+
+def heavy(seed: int = SEED_BASE + 3, n_bytes: int = 256 << 20) -> np.ndarray:
+    """256 MiB of symmetric alpha-stable (alpha = 1.7, scale 0.01) weights
+    clipped to +-64 and rounded to bf16."""
+    out = np.empty(n_bytes, dtype=np.uint8)
+    _fill_chunks(out, 0, n_bytes // 2, (seed,),
+                 lambda rng, m: np.clip(_alpha_stable_sym(rng, m, 1.7) * 0.01, -64.0, 64.0))
+    return out
+
+
+def _fibonacci(k: int) -> list[int]:
+    f = [1, 1]
+    while len(f) < k:
+        f.append(f[-1] + f[-2])
+    return f[:k]
+
+
+def edge_fib40(seed: int = SEED_BASE + 41, n_bytes: int = 16 << 20) -> np.ndarray:
+    """High bytes over 40 seeded distinct values with Fibonacci-like counts
+    c_k = max(1, floor(F_k * n / sum F)), the residual going to the largest;
+    a seeded shuffle orders them. Low bytes uniform. Unlimited Huffman depth
+    on these counts is far above 12."""
+    n = n_bytes // 2
+    rng = np.random.default_rng(seed)
+    vals = rng.permutation(256)[:40].astype(np.uint8)
+    fib = _fibonacci(40)
+    tot = sum(fib)
+    counts = [max(1, (f * n) // tot) for f in fib]
+    counts[-1] += n - sum(counts)
+    hi = np.repeat(vals, counts)
+    rng.shuffle(hi)
+    out = np.empty(n_bytes, dtype=np.uint8)
+    out[1::2] = hi
+    out[0::2] = rng.integers(0, 256, n, dtype=np.uint8)
+    return out
+
+
+def edge_single(seed: int = SEED_BASE + 42, n_bytes: int = 16 << 20) -> np.ndarray:
+    """Every high byte 0x3C (a one-symbol alphabet); low bytes uniform."""
+    rng = np.random.default_rng(seed)
+    out = np.empty(n_bytes, dtype=np.uint8)
+    out[1::2] = 0x3C
+    out[0::2] = rng.integers(0, 256, n_bytes // 2, dtype=np.uint8)
+    return out
+
+
+def edge_uniform(seed: int = SEED_BASE + 43, n_bytes: int = (64 << 20) + 2) -> np.ndarray:
+    """High and low bytes uniform over 0..255; 64 MiB + 2 B, so the second
+    64 MiB stripe holds a single bf16 value."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 256, n_bytes, dtype=np.uint8)
+
+
+def streamed_layer(k: int, n_bytes: int = TRUNK_LAYER_BYTES) -> np.ndarray:
+    """Layer k of the 93-layer streamed trunk: a trunk layer with seed
+    SEED_BASE + 5000 + k."""
+    return trunk_layer(SEED_BASE + 5000 + k, n_bytes)
+
+
+# name -> list of (layer name, zero-argument generator)
+CONFIGS = {
+    "tiny": [("tiny", tiny)],
+    "trunk": [("trunk", trunk_layer)],
+    "heavy": [("heavy", heavy)],
+    "edge": [("edge_fib40", edge_fib40), ("edge_single", edge_single),
+             ("edge_uniform", edge_uniform)],
+}
+
+
+def small_random(seed: int, n_bytes: int, sigma: float = 0.02) -> np.ndarray:
+    """Small N(0, sigma) bf16 buffers for quick tests of odd sizes."""
+    rng = np.random.default_rng(seed)
+    if n_bytes % 2:
+        raise ValueError("bf16 layer needs an even byte count")
+    return f64_to_bf16_bytes(rng.standard_normal(n_bytes // 2) * sigma)

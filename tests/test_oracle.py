@@ -1,0 +1,375 @@
+"""Pins for the CPU oracle: what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: hand-derived
+fixtures (tests/golden), exhaustive search over prefix codes, closed forms for
+the bitstream size, textbook special cases, and the round-trip identity of a
+lossless codec (K3 trunk-compression page, "core idea" and "verification
+results" sections).
+"""
+
+import itertools
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+
+import oracle as O
+from lossless_huffman_decoding_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _cost(counts, lens):
+    return sum(int(c) * int(l) for c, l in zip(counts, lens))
+
+
+# ---------------------------------------------------------------------------
+# container field access, written from the format description (test-side)
+
+def hdr(blob):
+    b = bytes(blob[:304])
+    magic = b[:4]
+    ver, maxlen, stripe, sub, lane, ns = struct.unpack_from("<HHIIII", b, 4)
+    raw, nsb, _, cbytes = struct.unpack_from("<QIIQ", b, 24)
+    return dict(magic=magic, ver=ver, maxlen=maxlen, stripe=stripe, sub=sub, lane=lane, ns=ns,
+                raw=raw, nsb=nsb, cbytes=cbytes, codelen=np.frombuffer(b[48:304], np.uint8))
+
+
+def stripe(blob, s):
+    off = int(np.frombuffer(bytes(blob[304 + 8 * s: 312 + 8 * s]), "<u8")[0])
+    f = struct.unpack_from("<8I", bytes(blob[off: off + 32]))
+    keys = ("raw", "n", "n_bits", "bit_bytes", "first_sb", "nsb", "bits_off", "even_off")
+    d = dict(zip(keys, f))
+    d["off"] = off
+    return d
+
+
+def sub_rec(blob, st, j):
+    o = st["off"] + 32 + 136 * j
+    start, n = struct.unpack_from("<II", bytes(blob[o: o + 8]))
+    lanes = np.frombuffer(bytes(blob[o + 8: o + 136]), "<u2")
+    return start, n, lanes
+
+
+# ---------------------------------------------------------------------------
+# P2: Huffman optimality by exhaustive search over prefix codes
+
+def _best_prefix_cost_exhaustive(counts):
+    """Minimum of sum c_i l_i over every length vector (l_i in 1..n-1) that
+    satisfies Kraft's inequality -- exactly the set of prefix-code length
+    vectors (Kraft-McMillan). Plain enumeration."""
+    n = len(counts)
+    best = None
+    for lens in itertools.product(range(1, n), repeat=n):
+        if sum(2.0 ** -l for l in lens) <= 1.0 + 1e-12:
+            c = _cost(counts, lens)
+            best = c if best is None else min(best, c)
+    return best
+
+
+def _best_prefix_cost_sorted(counts):
+    """Same minimum, enumerating multisets of lengths and pairing the largest
+    counts with the shortest lengths (rearrangement inequality)."""
+    n = len(counts)
+    cs = sorted(counts, reverse=True)
+    best = None
+    for lens in itertools.combinations_with_replacement(range(1, n), n):
+        if sum(2.0 ** -l for l in lens) <= 1.0 + 1e-12:
+            c = _cost(cs, lens)
+            best = c if best is None else min(best, c)
+    return best
+
+
+def _alphabets(n, rng, k):
+    out = [[1] * n, list(range(1, n + 1)), [2 ** i for i in range(n)],
+           [1] * (n - 1) + [1000], synth._fibonacci(n)]
+    for _ in range(k):
+        out.append(list(rng.integers(1, 50, n)))
+        out.append(list(rng.integers(1, 10 ** 6, n)))
+        out.append([int(x) for x in np.sort(rng.geometric(0.3, n) ** 3)])
+    return out
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 6])
+def test_huffman_optimal_exhaustive(n):
+    rng = np.random.default_rng(100 + n)
+    for counts in _alphabets(n, rng, 6 if n <= 5 else 2):
+        d = O.huffman_depths(counts)[:n]
+        want = _best_prefix_cost_exhaustive(counts)
+        assert _cost(counts, d) == want, (counts, d)
+        # the encoder's full path (limit + repay) leaves short alphabets alone
+        assert list(O.code_lengths(counts)[:n]) == list(d)
+
+
+@pytest.mark.parametrize("n", [6, 7, 8])
+def test_huffman_optimal_sorted_search(n):
+    rng = np.random.default_rng(200 + n)
+    for counts in _alphabets(n, rng, 25):
+        d = O.huffman_depths(counts)[:n]
+        assert _cost(counts, d) == _best_prefix_cost_sorted(counts), (counts, d)
+        assert O.kraft(d) == 4096  # a Huffman code is complete
+
+
+# ---------------------------------------------------------------------------
+# P3: length limit + repay invariants
+
+def _package_merge(counts, L):
+    """Optimal length-limited code cost (Larmore-Hirschberg package-merge),
+    a lower bound for any code with max length L."""
+    items = sorted(((c, (i,)) for i, c in enumerate(counts) if c), key=lambda t: t[0])
+    n = len(items)
+    if n == 1:
+        return counts[[i for i, c in enumerate(counts) if c][0]]
+    prev = []
+    for _ in range(L - 1):
+        merged = sorted(items + prev, key=lambda t: t[0])
+        prev = [(merged[i][0] + merged[i + 1][0], merged[i][1] + merged[i + 1][1])
+                for i in range(0, len(merged) - 1, 2)]
+    final = sorted(items + [p for p in prev], key=lambda t: t[0])  # noqa: C416
+    # the last merge list is items + packages of level L-1
+    lens = [0] * len(counts)
+    for w, syms in final[: 2 * n - 2]:
+        for s in syms:
+            lens[s] += 1
+    return _cost(counts, lens)
+
+
+def _check_limited(counts):
+    lens = O.code_lengths(counts)
+    live = [i for i, c in enumerate(counts) if c]
+    assert all(lens[i] >= 1 for i in live)
+    assert all(lens[i] == 0 for i in range(256) if i >= len(counts) or not counts[i])
+    assert max(lens) <= 12
+    if len(live) >= 2:
+        assert O.kraft(lens) == 4096
+    assert O.check_table(lens) == O.OK
+    c = _cost(counts, lens[: len(counts)])
+    huff = _cost(counts, O.huffman_depths(counts)[: len(counts)])
+    assert c >= huff
+    return lens, c
+
+
+def test_limiter_fibonacci40_forces_limit():
+    fib = synth._fibonacci(40)
+    d = O.huffman_depths(fib)
+    assert d.max() > 12
+    lens, c = _check_limited(fib)
+    assert lens.max() == 12
+    assert c >= _package_merge(fib, 12)
+
+
+def test_limiter_random_sweep():
+    rng = np.random.default_rng(7)
+    forced = 0
+    for trial in range(300):
+        n = int(rng.integers(2, 257))
+        kind = trial % 3
+        if kind == 0:
+            counts = list(rng.geometric(rng.uniform(0.05, 0.6), n) ** 4)
+        elif kind == 1:
+            counts = [int(2 ** rng.uniform(0, 40)) for _ in range(n)]
+        else:
+            counts = list(rng.integers(1, 1000, n))
+        counts = [max(1, int(c)) for c in counts]
+        lens, c = _check_limited(counts)
+        forced += int(O.huffman_depths(counts).max() > 12)
+        if trial % 10 == 0:
+            assert c >= _package_merge(counts, 12)
+    assert forced > 50  # the sweep really exercises the limiter
+
+
+def test_package_merge_matches_huffman_when_unconstrained():
+    # sanity of the test's own lower bound: with L large it equals Huffman
+    counts = [5, 9, 12, 13, 16, 45]
+    assert _package_merge(counts, 12) == _cost(counts, O.huffman_depths(counts)[:6])
+
+
+# ---------------------------------------------------------------------------
+# P4: canonical assignment (golden, hand-derived) and the Kraft rule
+
+def test_canonical_golden():
+    rows = [l.split() for l in open(os.path.join(GOLD, "canonical_example.txt"))
+            if l.strip() and not l.startswith("#")]
+    lens = [int(r[1]) for r in rows]
+    codes = O.canonical(lens)
+    for (sym, l, bits) in rows:
+        assert format(int(codes[int(sym)]), "0%db" % int(l)) == bits
+
+
+def test_canonical_prefix_free_and_fills_space():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        n = int(rng.integers(2, 257))
+        counts = [max(1, int(x)) for x in rng.geometric(0.2, n) ** 3]
+        lens = O.code_lengths(counts)
+        codes = O.canonical(lens)
+        # expand every code to its 12-bit prefix range: the ranges tile 0..4095
+        cover = np.zeros(4096, np.int32)
+        for s in range(256):
+            l = int(lens[s])
+            if l:
+                lo = int(codes[s]) << (12 - l)
+                cover[lo: lo + (1 << (12 - l))] += 1
+        assert (cover == 1).all()
+
+
+def test_kraft_rule_and_rejections():
+    z = [0] * 256
+    assert O.check_table(z) == O.E_EMPTY
+    assert O.check_table([1, 1, 1]) == O.E_OVERSUB
+    assert O.check_table([13, 1]) == O.E_BADLEN
+    # under-full with two lengths: the floor recurrence gives A=0, B=00
+    assert list(O.canonical([1, 2])[:2]) == [0, 0]
+    assert O.check_table([1, 2]) == O.E_OVERLAP
+    # under-full but prefix-free cases are accepted
+    assert O.check_table([1]) == O.OK            # lone symbol, Kraft 2048
+    assert O.check_table([2, 2, 2]) == O.OK      # 00 01 10, Kraft 3072
+    assert O.check_table([1, 1]) == O.OK
+    assert O.kraft([1, 1]) == 4096
+    assert O.kraft([12] * 256) == 256
+
+
+def test_decode_prefix_against_codes():
+    counts = [50, 30, 10, 5, 3, 1, 1]
+    lens = O.code_lengths(counts)
+    codes = O.canonical(lens)
+    for s in range(7):
+        l = int(lens[s])
+        pref = int(codes[s]) << (12 - l)
+        for tail in (0, (1 << (12 - l)) - 1):
+            assert O.decode_prefix(lens, pref | tail) == (s, l)
+
+
+# ---------------------------------------------------------------------------
+# P8: special cases
+
+def test_special_cases():
+    assert list(O.code_lengths([7] * 256)) == [8] * 256          # uniform 256
+    dy = [2 ** (10 - i) for i in range(10)] + [1]                # 1/2, 1/4, ... dyadic
+    d = O.code_lengths(dy)[:11]
+    total = sum(dy)
+    for c, l in zip(dy[:-1], d[:-1]):
+        assert l == round(-math.log2(c / total))
+    assert list(O.code_lengths([5, 9])[:2]) == [1, 1]            # two symbols
+    one = O.code_lengths([0, 0, 17])
+    assert one[2] == 1 and one.sum() == 1                         # lone symbol
+
+
+# ---------------------------------------------------------------------------
+# the hand-encoded four-value layer (golden)
+
+def test_four_value_layer_golden():
+    g = {}
+    for line in open(os.path.join(GOLD, "four_value_layer.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            g[k] = v
+    raw = np.frombuffer(bytes.fromhex(g["raw"][0]), np.uint8)
+    blob = O.encode_layer(raw)
+    h = hdr(blob)
+    assert h["magic"] == b"K3HF" and h["ver"] == 1 and h["maxlen"] == 12
+    assert h["raw"] == 8 and h["ns"] == 1 and h["nsb"] == 1 and h["cbytes"] == blob.size
+    want_len = np.zeros(256, np.uint8)
+    for kv in g["codelen"]:
+        k, v = kv.split("=")
+        want_len[int(k, 16)] = int(v)
+    assert (h["codelen"] == want_len).all()
+    st = stripe(blob, 0)
+    assert st["n_bits"] == int(g["n_bits"][0])
+    assert blob[st["off"] + st["bits_off"]] == int(g["bitstream_byte0"][0], 16)
+    start, n, lanes = sub_rec(blob, st, 0)
+    assert start == int(g["subblock0_start"][0]) and n == int(g["subblock0_nsyms"][0])
+    assert lanes[0] == int(g["lane0_bits"][0]) and (lanes[1:] == 0).all()
+    ev = bytes(blob[st["off"] + st["even_off"]: st["off"] + st["even_off"] + 4])
+    assert ev == bytes.fromhex(g["even"][0])
+    assert (O.decode_layer(blob) == raw).all()
+
+
+# ---------------------------------------------------------------------------
+# P1/P5/P6: round trip, closed-form bit counts, index replay
+
+def _roundtrip_checks(x):
+    blob = O.encode_layer(x)
+    h = hdr(blob)
+    assert h["raw"] == x.size and h["cbytes"] == blob.size
+    assert h["ns"] == -(-x.size // (1 << 26))
+    counts_layer = np.bincount(x[1::2], minlength=256)
+    lens = h["codelen"]
+    assert (lens[counts_layer == 0] == 0).all() and (lens[counts_layer > 0] > 0).all()
+    nsb_total = 0
+    for s in range(h["ns"]):
+        st = stripe(blob, s)
+        lo = s << 26
+        hi = min(x.size, lo + (1 << 26))
+        sym = x[lo + 1: hi: 2]
+        # P5: closed form for the code bits of the stripe
+        cs = np.bincount(sym, minlength=256).astype(np.int64)
+        assert st["n_bits"] == int((cs * lens.astype(np.int64)).sum())
+        assert st["first_sb"] == nsb_total
+        nsb_total += st["nsb"]
+        # the subblock records' lane counts add up to the stripe's bits
+        tot = 0
+        for j in range(st["nsb"]):
+            start, n, lanes = sub_rec(blob, st, j)
+            assert start == tot
+            tot += int(lanes.sum())
+        assert tot == st["n_bits"]
+    assert nsb_total == h["nsb"]
+    assert O.check_index(blob) == O.OK
+    y = O.decode_layer(blob)
+    assert y.size == x.size and (y == x).all()
+    return blob
+
+
+def test_roundtrip_tiny():
+    x = synth.tiny()
+    blob = _roundtrip_checks(x)
+    ratio = blob.size / x.size
+    assert 0.64 < ratio < 0.70  # the pages measure ~0.689 on a real trunk sample
+
+
+@pytest.mark.parametrize("n_bytes", [2, 4, 1022, 1024, 1026, 65534, 65536, 65538, 3 * 65536 + 514])
+def test_roundtrip_small_sizes(n_bytes):
+    _roundtrip_checks(synth.small_random(n_bytes, n_bytes))
+
+
+def test_roundtrip_edge_layers():
+    for name, gen in synth.CONFIGS["edge"]:
+        x = gen()
+        blob = _roundtrip_checks(x)
+        h = hdr(blob)
+        if name == "edge_fib40":
+            assert h["codelen"].max() == 12
+        if name == "edge_single":
+            assert (h["codelen"] > 0).sum() == 1 and h["codelen"][0x3C] == 1
+            assert stripe(blob, 0)["n_bits"] == x.size // 2
+        if name == "edge_uniform":
+            assert h["ns"] == 2 and stripe(blob, 1)["raw"] == 2
+            assert set(h["codelen"].tolist()) == {8}
+
+
+@pytest.mark.slow
+def test_roundtrip_heavy():
+    x = synth.heavy()
+    blob = _roundtrip_checks(x)
+    h = hdr(blob)
+    live = int((h["codelen"] > 0).sum())
+    assert 25 <= live <= 80
+    assert 0.62 < blob.size / x.size < 0.72
+
+
+def test_index_checker_detects_tampering():
+    x = synth.small_random(5, 3 * 65536)
+    blob = O.encode_layer(x).copy()
+    st = stripe(blob, 0)
+    o = st["off"] + 32 + 136 * 1 + 8 + 2 * 5      # lane 5 of subblock 1
+    blob[o] ^= 1
+    assert O.check_index(blob) == O.E_INDEX
+    assert O.decode_layer_rc(blob) == O.OK         # the decoder ignores the index
+    blob2 = O.encode_layer(x).copy()
+    blob2[st["off"] + st["bits_off"] + 100] ^= 0x10  # flip a code bit
+    # a flipped code bit is either rejected or decodes to different bytes
+    rc = O.decode_layer_rc(blob2)
+    assert rc != O.OK or not (O.decode_layer(blob2) == x).all()
