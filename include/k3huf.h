@@ -1,0 +1,194 @@
+/*
+ * k3huf.h -- C ABI of the MI355X (gfx950) decoder for bf16 layers whose high
+ * (sign + exponent) byte plane is coded with a 12-bit length-limited canonical
+ * Huffman code.
+ *
+ * Sources. "K3 page" is the page "Kimi K3 纯 CPU 推理中的无损 Trunk 压缩：一次被解码
+ * 速度判死刑的 Huffman 压缩实验" (yfxerp.com/news/153994). "ECF8 page" is the
+ * pwwt.cn page on exponent-concentration FP8 (pwwt.cn/news/2030120). "K3
+ * TUNING page" is zwxr.cn/news/188695.
+ *
+ * All functions are plain C: pointers and sizes only. A "stream" argument is
+ * a hipStream_t passed as void* (NULL = the null stream). Functions return
+ * K3HUF_OK (0) or a negative K3HUF_E_* code and never throw.
+ *
+ * ---------------------------------------------------------------------------
+ * Container ("layer blob") layout, all integers little-endian.
+ * K3 page, "what was implemented": [layer header holding codelen[256]], then
+ * per stripe [stripe header][odd-plane Huffman bitstream][even plane raw].
+ * K3 page, "key design points": 64 MiB of raw layer bytes per stripe; the odd
+ * offsets of a little-endian bf16 layer (high bytes) are coded, the even
+ * offsets (mantissa bytes) are copied raw; code length at most 12.
+ * The subblock/lane index is an addition for parallel decoding (after the
+ * per-thread bit offsets of the ECF8 page, section 2.1), counted in the size.
+ *
+ *   layer header (K3HUF_HDR_BYTES = 304):
+ *     0   char[4] magic "K3HF"         4  u16 version = 1
+ *     6   u16 maxlen = 12               8  u32 stripe_bytes = 2^26
+ *     12  u32 subblock_bytes = 2^16     16 u32 lane_syms = 512
+ *     20  u32 n_stripes = ceil(raw_bytes / 2^26)
+ *     24  u64 raw_bytes (even, > 0)     32 u32 n_subblocks (total)
+ *     36  u32 reserved = 0              40 u64 container_bytes
+ *     48  u8  codelen[256]
+ *   304   u64 stripe_off[n_stripes]: byte offset of each stripe record from
+ *         the blob start, 16-byte aligned; zero pad to 16.
+ *   stripe record (at stripe_off[s]):
+ *     0 u32 raw_bytes   4 u32 n_syms = raw_bytes / 2   8 u32 n_bits
+ *     12 u32 bit_bytes = ceil(n_bits / 8) rounded up to 16
+ *     16 u32 first_subblock = s * 1024   20 u32 n_subblocks = ceil(n_syms / 32768)
+ *     24 u32 bits_off   28 u32 even_off  (both from the record start, 16-aligned)
+ *     32 subblock records, K3HUF_SUBBLOCK_REC_BYTES = 136 each:
+ *          u32 start_bit (stripe-relative bit index of the subblock's first code)
+ *          u32 n_syms    (32768, or fewer in the stripe's last subblock)
+ *          u16 lane_bits[64] (code bits of each 512-symbol lane chunk; 0 if empty)
+ *        zero pad to 16
+ *     bits_off: the stripe's codes, most-significant bit first (K3 page,
+ *        "decode loop": the stream head sits at the top of the bit window),
+ *        zero padded to bit_bytes
+ *     even_off: the even-offset bytes of the stripe (n_syms), zero padded to 16
+ *   Stripe s covers raw bytes [s * 2^26, min((s + 1) * 2^26, raw_bytes)).
+ *   Global subblock k covers raw bytes [k * 2^16, min((k + 1) * 2^16, raw_bytes)).
+ */
+#ifndef K3HUF_H
+#define K3HUF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define K3HUF_MAXLEN 12
+#define K3HUF_LUT_ENTRIES 4096
+#define K3HUF_STRIPE_BYTES (1u << 26)
+#define K3HUF_SUBBLOCK_BYTES (1u << 16)
+#define K3HUF_SUBBLOCK_SYMS (K3HUF_SUBBLOCK_BYTES / 2)
+#define K3HUF_LANE_SYMS 512u
+#define K3HUF_LANES (K3HUF_SUBBLOCK_SYMS / K3HUF_LANE_SYMS)
+#define K3HUF_HDR_BYTES 304u
+#define K3HUF_STRIPE_HDR_BYTES 32u
+#define K3HUF_SUBBLOCK_REC_BYTES (8u + 2u * K3HUF_LANES)
+
+/* return codes */
+#define K3HUF_OK 0
+#define K3HUF_E_ARG (-1)      /* bad argument (null, size, alignment) */
+#define K3HUF_E_EMPTY (-2)    /* code table codes no symbol */
+#define K3HUF_E_OVERSUB (-3)  /* Kraft sum over-fills the 12-bit code space */
+#define K3HUF_E_BADLEN (-4)   /* a code length above 12 */
+#define K3HUF_E_OVERLAP (-5)  /* canonical codes are not prefix-free */
+#define K3HUF_E_FORMAT (-6)   /* container header or stripe record malformed */
+#define K3HUF_E_CORRUPT (-7)  /* data inconsistent with its index or table */
+#define K3HUF_E_HIP (-8)      /* a HIP runtime call failed */
+
+/* device status bits, OR-ed into *d_status by the decode kernel */
+#define K3HUF_DEV_HEADER 1u   /* layer header does not match the call */
+#define K3HUF_DEV_STRIPE 2u   /* a stripe record is out of bounds or inconsistent */
+#define K3HUF_DEV_INDEX 4u    /* a subblock record or lane bit count is inconsistent */
+#define K3HUF_DEV_CODE 8u     /* the decode hit an unused lookup-table slot */
+#define K3HUF_DEV_LANE_END 16u /* a lane chunk's codes did not end where its index says */
+
+/*
+ * k3huf_build_table -- 4096-entry decode table from codelen[256].
+ * K3 page, "key design points": a table of 1 << 12 entries, each entry packs
+ * (symbol << 4) | code_length, so one lookup yields both. K3 page, "canonical
+ * code assignment and Kraft check": the Kraft sum sum_l count[l] << (12 - l)
+ * must fill the 12-bit space exactly or under-fill it (over-full or empty =
+ * corrupt); codes are assigned longest length first with first[l] = code;
+ * code = (code + count[l]) >> 1, symbols in ascending order within a length,
+ * and each code is expanded over all 12-bit indices it prefixes.
+ * Entry 0 marks an index no code covers (possible only for under-full tables).
+ * Host memory in, host memory out; pure, no allocation, thread-safe.
+ * Errors: K3HUF_E_ARG (null), K3HUF_E_BADLEN, K3HUF_E_EMPTY, K3HUF_E_OVERSUB,
+ * K3HUF_E_OVERLAP (a slot would be written twice: an under-full table whose
+ * canonical codes are not prefix-free). On error lut[] is left zeroed.
+ */
+int k3huf_build_table(const uint8_t codelen[256], uint16_t lut[4096]);
+
+typedef struct k3huf_info {
+    uint64_t raw_bytes;       /* decoded size */
+    uint64_t container_bytes; /* blob size recorded in the header */
+    uint32_t n_stripes;
+    uint32_t n_subblocks;
+    uint8_t codelen[256];
+} k3huf_info;
+
+/*
+ * k3huf_layer_info -- parse and check a layer header held in host memory.
+ * h_blob/h_bytes: at least the first K3HUF_HDR_BYTES bytes of a blob.
+ * Checks magic, version, geometry constants, raw size and stripe count.
+ * Errors: K3HUF_E_ARG, K3HUF_E_FORMAT.
+ */
+int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out);
+
+/*
+ * k3huf_decode_layer -- decode one layer blob on the GPU.
+ * d_blob: device pointer, 16-byte aligned, blob_bytes long (the whole blob).
+ * d_lut: device pointer to the 4096 u16 entries k3huf_build_table made from
+ *   this blob's codelen[256] (the caller uploads it once per layer).
+ * d_out: device pointer, 16-byte aligned, out_bytes = the blob's raw_bytes;
+ *   receives the bf16 layer bytes.
+ * stream: hipStream_t (as void*) the work is queued on; the call returns
+ *   after queuing, without synchronizing and without allocating.
+ * d_status: device u32 (nullable). The kernel ORs K3HUF_DEV_* bits into it
+ *   when it meets a malformed header, stripe or index, an unused table slot,
+ *   or a lane whose codes end off its index; the caller clears it beforehand
+ *   and reads it after the stream synchronizes. Subblocks with bad records
+ *   are left unwritten; no read ever leaves [d_blob, d_blob + blob_bytes).
+ * Returns K3HUF_OK once queued, K3HUF_E_ARG for bad sizes or alignment,
+ * K3HUF_E_HIP if the launch fails. Decoding follows the K3 page's "decode
+ * loop" (MSB-first bit window, one table lookup per symbol) and "key design
+ * points" (even plane interleaved back at even offsets).
+ */
+int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut,
+                       void* d_out, size_t out_bytes, void* stream, uint32_t* d_status);
+
+/*
+ * k3huf_decode_ring -- decode layers 0..n_layers-1 in order into a ring of
+ * device slots (K3 TUNING page, section 2: a trunk ring whose default of two
+ * slots lets one layer be consumed while the next one is produced; K3 page,
+ * "background": layers are visited in the fixed order 0..92).
+ * Layer k goes to slot k % n_slots on stream k % n_streams, after the previous
+ * user of that slot has released it (event wait); then cb (nullable) is called
+ * to queue the consumer's work on that stream, and the slot is released behind
+ * it. All queued asynchronously; the call returns without synchronizing.
+ * layers[k]: device blob, its size, its device LUT, its raw size (<= slot_bytes).
+ * d_slots[n_slots], streams[n_streams] (hipStream_t as void*): caller-owned.
+ * d_status: as for k3huf_decode_layer (shared by all layers).
+ * Errors: K3HUF_E_ARG, K3HUF_E_HIP.
+ */
+typedef struct k3huf_ring_layer {
+    const void* d_blob;
+    size_t blob_bytes;
+    const uint16_t* d_lut;
+    size_t raw_bytes;
+} k3huf_ring_layer;
+
+typedef void (*k3huf_ring_cb)(int layer, void* d_slot, size_t raw_bytes, void* stream, void* user);
+
+int k3huf_decode_ring(const k3huf_ring_layer* layers, int n_layers, void* const* d_slots,
+                      int n_slots, size_t slot_bytes, void* const* streams, int n_streams,
+                      k3huf_ring_cb cb, void* user, uint32_t* d_status);
+
+/*
+ * k3huf_encode_bound -- container size upper bound for raw_bytes of layer data.
+ * k3huf_encode_layer -- host packer: one histogram and codelen[256] over the
+ * whole layer's odd bytes (K3 page, "what was implemented"), Huffman depths
+ * limited to 12 bits (K3 page, "canonical code assignment and Kraft check"),
+ * longest-first canonical codes, stripes and the subblock/lane index.
+ * h_raw: host bf16 layer bytes (raw_bytes even, > 0). h_out: host buffer of
+ * cap >= k3huf_encode_bound(raw_bytes). n_threads <= 0 picks the core count.
+ * Returns the container size, or K3HUF_E_ARG.
+ */
+int64_t k3huf_encode_bound(uint64_t raw_bytes);
+int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, uint64_t cap,
+                           int n_threads);
+
+/* Static text for a return code. */
+const char* k3huf_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K3HUF_H */

@@ -1,0 +1,50 @@
+"""Compile the k3huf HIP library for gfx950, in-tree.
+
+Produces lossless_huffman_decoding_amd/_lib/libk3huf.so from csrc/ with hipcc.
+Always recompiles when called (the build check wants a real compile).
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT_DIR = os.path.join(PKG, "_lib")
+LIB = os.path.join(OUT_DIR, "libk3huf.so")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# packed fp32 instructions stay off for all device code
+HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I" + os.path.join(ROOT, "include")]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-pthread",
+              "-I" + os.path.join(ROOT, "include")]
+
+
+def _run(cmd):
+    subprocess.check_call(cmd)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    bdir = os.path.join(OUT_DIR, "_obj")
+    os.makedirs(bdir, exist_ok=True)
+    objs = []
+    o = os.path.join(bdir, "k3huf_decode.o")
+    _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "k3huf_decode.hip"), "-o", o])
+    objs.append(o)
+    o = os.path.join(bdir, "k3huf_host.o")
+    _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "k3huf_host.cpp"), "-o", o])
+    objs.append(o)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-pthread", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,185 @@
+"""Thin Python binding of libk3huf.so (ctypes): argument marshalling only.
+
+Every step of decoding runs in the library's HIP kernels; this module only
+passes pointers, sizes and stream handles. PyTorch supplies device memory and
+streams. If the library has not been built, every call raises -- there is no
+fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libk3huf.so")
+
+OK = 0
+E_ARG, E_EMPTY, E_OVERSUB, E_BADLEN, E_OVERLAP, E_FORMAT, E_CORRUPT, E_HIP = range(-1, -9, -1)
+DEV_HEADER, DEV_STRIPE, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 2, 4, 8, 16
+
+# names the C header declares, checked by the ABI test
+EXPORTS = ("k3huf_build_table", "k3huf_layer_info", "k3huf_decode_layer", "k3huf_decode_ring",
+           "k3huf_encode_bound", "k3huf_encode_layer", "k3huf_strerror")
+
+
+class K3HufError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__("%s: %s (%d)" % (what, strerror(code) if _lib else "error", code))
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("raw_bytes", ctypes.c_uint64), ("container_bytes", ctypes.c_uint64),
+                ("n_stripes", ctypes.c_uint32), ("n_subblocks", ctypes.c_uint32),
+                ("codelen", ctypes.c_uint8 * 256)]
+
+
+class RingLayer(ctypes.Structure):
+    _fields_ = [("d_blob", ctypes.c_void_p), ("blob_bytes", ctypes.c_size_t),
+                ("d_lut", ctypes.c_void_p), ("raw_bytes", ctypes.c_size_t)]
+
+
+RING_CB = ctypes.CFUNCTYPE(None, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                           ctypes.c_void_p)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library; raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libk3huf.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.k3huf_build_table.argtypes = [vp, vp]
+        L.k3huf_build_table.restype = ctypes.c_int
+        L.k3huf_layer_info.argtypes = [vp, sz, ctypes.POINTER(Info)]
+        L.k3huf_layer_info.restype = ctypes.c_int
+        L.k3huf_decode_layer.argtypes = [vp, sz, vp, vp, sz, vp, vp]
+        L.k3huf_decode_layer.restype = ctypes.c_int
+        L.k3huf_decode_ring.argtypes = [ctypes.POINTER(RingLayer), ctypes.c_int,
+                                        ctypes.POINTER(vp), ctypes.c_int, sz,
+                                        ctypes.POINTER(vp), ctypes.c_int, RING_CB, vp, vp]
+        L.k3huf_decode_ring.restype = ctypes.c_int
+        L.k3huf_encode_bound.argtypes = [ctypes.c_uint64]
+        L.k3huf_encode_bound.restype = ctypes.c_int64
+        L.k3huf_encode_layer.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, ctypes.c_int]
+        L.k3huf_encode_layer.restype = ctypes.c_int64
+        L.k3huf_strerror.argtypes = [ctypes.c_int]
+        L.k3huf_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().k3huf_strerror(code).decode()
+
+
+def _check(rc: int, what: str) -> int:
+    if rc < 0:
+        raise K3HufError(int(rc), what)
+    return rc
+
+
+def _u8(a) -> np.ndarray:
+    if isinstance(a, (bytes, bytearray, memoryview)):
+        return np.frombuffer(a, dtype=np.uint8)
+    return np.ascontiguousarray(a, dtype=np.uint8)
+
+
+def build_table(codelen) -> np.ndarray:
+    """4096-entry u16 decode table ((symbol << 4) | length) for codelen[256]."""
+    cl = np.zeros(256, np.uint8)
+    c = np.asarray(codelen, dtype=np.uint8)
+    cl[: c.size] = c
+    lut = np.zeros(4096, np.uint16)
+    _check(lib().k3huf_build_table(cl.ctypes.data, lut.ctypes.data), "k3huf_build_table")
+    return lut
+
+
+def build_table_rc(codelen) -> int:
+    """Return code of k3huf_build_table (0 or a negative error)."""
+    cl = np.zeros(256, np.uint8)
+    c = np.asarray(codelen, dtype=np.uint8)
+    cl[: c.size] = c
+    lut = np.zeros(4096, np.uint16)
+    return lib().k3huf_build_table(cl.ctypes.data, lut.ctypes.data)
+
+
+def layer_info(blob) -> dict:
+    b = _u8(blob)
+    info = Info()
+    _check(lib().k3huf_layer_info(b.ctypes.data, b.size, ctypes.byref(info)), "k3huf_layer_info")
+    return dict(raw_bytes=info.raw_bytes, container_bytes=info.container_bytes,
+                n_stripes=info.n_stripes, n_subblocks=info.n_subblocks,
+                codelen=np.frombuffer(bytes(info.codelen), np.uint8).copy())
+
+
+def encode_bound(raw_bytes: int) -> int:
+    return _check(lib().k3huf_encode_bound(raw_bytes), "k3huf_encode_bound")
+
+
+def encode_layer(raw, n_threads: int = 0) -> np.ndarray:
+    """Pack one bf16 layer (bytes) into a container (numpy uint8)."""
+    r = _u8(raw)
+    cap = encode_bound(r.size)
+    out = np.empty(cap, np.uint8)
+    n = _check(lib().k3huf_encode_layer(r.ctypes.data, r.size, out.ctypes.data, cap, n_threads),
+               "k3huf_encode_layer")
+    return out[:n]
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def decode_layer(d_blob, d_lut, d_out, d_status=None, stream=None) -> None:
+    """Queue the decode of one layer. Tensors: d_blob uint8 (the blob),
+    d_lut 4096 16-bit entries, d_out uint8 of the layer's raw size, d_status
+    a 32-bit device word or None. Runs on ``stream`` (default: torch's
+    current stream)."""
+    rc = lib().k3huf_decode_layer(
+        d_blob.data_ptr(), d_blob.numel() * d_blob.element_size(), d_lut.data_ptr(),
+        d_out.data_ptr(), d_out.numel() * d_out.element_size(), _stream_handle(stream),
+        d_status.data_ptr() if d_status is not None else None)
+    _check(rc, "k3huf_decode_layer")
+
+
+def decode_layer_raw(blob_ptr: int, blob_bytes: int, lut_ptr: int, out_ptr: int, out_bytes: int,
+                     stream: int, status_ptr) -> int:
+    """Unchecked pointer-level call; returns the C return code."""
+    return lib().k3huf_decode_layer(blob_ptr, blob_bytes, lut_ptr, out_ptr, out_bytes, stream,
+                                    status_ptr)
+
+
+def decode_ring(layers, slots, streams, cb=None, d_status=None) -> None:
+    """Decode ``layers`` (a list of (d_blob, d_lut, raw_bytes)) in order into
+    the ring of ``slots`` (uint8 tensors of equal size) on ``streams``. ``cb``
+    (optional) is called as cb(k, slot_index, stream_handle) right after layer
+    k is queued, to queue its consumer."""
+    n = len(layers)
+    arr = (RingLayer * max(n, 1))()
+    for k, (blob, lut, raw) in enumerate(layers):
+        arr[k] = RingLayer(blob.data_ptr(), blob.numel(), lut.data_ptr(), raw)
+    slot_ptrs = (ctypes.c_void_p * len(slots))(*[s.data_ptr() for s in slots])
+    stream_ptrs = (ctypes.c_void_p * len(streams))(*[_stream_handle(s) for s in streams])
+    slot_bytes = min(s.numel() for s in slots)
+    index = {s.data_ptr(): i for i, s in enumerate(slots)}
+    if cb is not None:
+        def _tramp(k, slot, raw, stream, user):
+            cb(k, index[slot], stream)
+        c_cb = RING_CB(_tramp)
+    else:
+        c_cb = RING_CB()
+    rc = lib().k3huf_decode_ring(arr, n, slot_ptrs, len(slots), slot_bytes, stream_ptrs,
+                                 len(streams), c_cb, None,
+                                 d_status.data_ptr() if d_status is not None else None)
+    _check(rc, "k3huf_decode_ring")

@@ -1,0 +1,111 @@
+"""CPU-side checks of the C-ABI library: it loads, exports what include/k3huf.h
+declares, and its host functions (decode-table build, header parse, packer)
+agree with the oracle. No GPU compute is called here."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from lossless_huffman_decoding_amd import k3huf, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    txt = open(os.path.join(ROOT, "include", "k3huf.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(k3huf_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = k3huf.lib()
+    names = _declared_functions()
+    assert set(names) == set(k3huf.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _tables():
+    rng = np.random.default_rng(11)
+    yield [1]                                  # lone symbol (Kraft 2048)
+    yield [1, 1]
+    yield [2, 2, 2]                            # under-full, prefix-free
+    yield [8] * 256
+    yield list(O.code_lengths(synth._fibonacci(40)))
+    for _ in range(40):
+        n = int(rng.integers(2, 257))
+        counts = np.zeros(256, np.int64)
+        idx = rng.permutation(256)[:n]
+        counts[idx] = np.maximum(1, rng.geometric(rng.uniform(0.05, 0.5), n) ** 3)
+        yield list(O.code_lengths(counts))
+
+
+def test_build_table_matches_oracle_bit_by_bit_decode():
+    """Every one of the 4096 slots equals the oracle's bit-by-bit decode of
+    that 12-bit string (symbol << 4 | length), or 0 where no code applies."""
+    for lens in _tables():
+        lut = k3huf.build_table(lens)
+        want = np.zeros(4096, np.uint16)
+        for i in range(4096):
+            r = O.decode_prefix(lens, i)
+            if r is not None:
+                want[i] = (r[0] << 4) | r[1]
+        assert (lut == want).all(), lens[:16]
+
+
+def test_build_table_rejections_match_page_rules():
+    assert k3huf.build_table_rc([0] * 256) == k3huf.E_EMPTY
+    assert k3huf.build_table_rc([1, 1, 1]) == k3huf.E_OVERSUB
+    assert k3huf.build_table_rc([13, 1]) == k3huf.E_BADLEN
+    assert k3huf.build_table_rc([1, 2]) == k3huf.E_OVERLAP
+    for lens in ([1, 1, 1], [13, 1], [1, 2], [0] * 256, [1], [2, 2, 2]):
+        rc = k3huf.build_table_rc(lens)
+        orc = O.check_table(lens)
+        assert (rc == 0) == (orc == 0)
+    with pytest.raises(k3huf.K3HufError):
+        k3huf.build_table([1, 1, 1])
+
+
+def test_layer_info_parses_oracle_container():
+    x = synth.small_random(3, 3 * 65536 + 514)
+    blob = O.encode_layer(x)
+    info = k3huf.layer_info(blob)
+    assert info["raw_bytes"] == x.size
+    assert info["container_bytes"] == blob.size
+    assert info["n_stripes"] == 1 and info["n_subblocks"] == 4
+    bad = blob.copy()
+    bad[0] ^= 1
+    with pytest.raises(k3huf.K3HufError):
+        k3huf.layer_info(bad)
+    bad = blob.copy()
+    bad[26] ^= 0x10                                 # raw_bytes no longer matches n_subblocks
+    with pytest.raises(k3huf.K3HufError):
+        k3huf.layer_info(bad)
+
+
+@pytest.mark.parametrize("n_bytes", [2, 1026, 65536, 3 * 65536 + 514])
+def test_packer_matches_oracle_encoder(n_bytes):
+    x = synth.small_random(n_bytes + 7, n_bytes)
+    a = O.encode_layer(x)
+    b = k3huf.encode_layer(x)
+    assert a.size == b.size and (a == b).all()
+    assert O.check_index(b) == O.OK
+
+
+def test_packer_edge_layers_decode_with_oracle():
+    for name, gen in synth.CONFIGS["edge"]:
+        x = gen()
+        b = k3huf.encode_layer(x)
+        assert O.check_index(b) == O.OK, name
+        assert (O.decode_layer(b) == x).all(), name
+        a = O.encode_layer(x)
+        assert a.size == b.size and (a == b).all(), name
+
+
+def test_packer_bad_args():
+    assert k3huf.lib().k3huf_encode_bound(3) == k3huf.E_ARG
+    assert k3huf.lib().k3huf_encode_bound(0) == k3huf.E_ARG
+    assert k3huf.encode_bound(2) == O.encode_bound(2)

@@ -1,0 +1,243 @@
+"""GPU parity: k3huf_decode_layer (HIP, gfx950) against the CPU oracle.
+
+Containers come from the oracle's encoder; the expected bytes are the
+generated layer itself (decode(encode(x)) = x, K3 trunk-compression page,
+"verification results") and the oracle's bit-by-bit decode. The bar is byte
+equality. Every case prints its name before touching the GPU.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from lossless_huffman_decoding_amd import k3huf, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+_cache = {}
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+def oracle_container(name, gen):
+    if name not in _cache:
+        x = gen()
+        _cache[name] = (x, O.encode_layer(x))
+    return _cache[name]
+
+
+def to_dev(blob, lut):
+    d_blob = torch.from_numpy(np.ascontiguousarray(blob)).to(DEV)
+    d_lut = torch.from_numpy(np.ascontiguousarray(lut).view(np.int16)).to(DEV)
+    return d_blob, d_lut
+
+
+def gpu_decode(blob, lut=None, out_bytes=None, stream=None):
+    if lut is None or out_bytes is None:
+        info = k3huf.layer_info(blob)
+        lut = k3huf.build_table(info["codelen"]) if lut is None else lut
+        out_bytes = info["raw_bytes"] if out_bytes is None else out_bytes
+    d_blob, d_lut = to_dev(blob, lut)
+    n = out_bytes
+    d_out = torch.full((n,), 0xA5, dtype=torch.uint8, device=DEV)  # poison
+    d_status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    k3huf.decode_layer(d_blob, d_lut, d_out, d_status, stream)
+    torch.cuda.synchronize()
+    return d_out.cpu().numpy(), int(d_status.item())
+
+
+@pytest.mark.parametrize("n_bytes", [2, 4, 16, 1022, 1024, 1026, 1040, 65534, 65536, 65538,
+                                     3 * 65536 + 514, 64 * 65536 - 2, (1 << 26), (1 << 26) + 2])
+def test_sizes_parity(n_bytes):
+    x = synth.small_random(n_bytes, n_bytes)
+    blob = O.encode_layer(x)
+    say("sizes", n_bytes)
+    got, st = gpu_decode(blob)
+    assert st == 0
+    want = O.decode_layer(blob)
+    assert (want == x).all()
+    assert (got == want).all()
+
+
+def test_tiny_parity():
+    x, blob = oracle_container("tiny", synth.tiny)
+    say("tiny", x.size)
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got == O.decode_layer(blob)).all()
+
+
+@pytest.mark.parametrize("layer", ["edge_fib40", "edge_single", "edge_uniform"])
+def test_edge_parity(layer):
+    gen = dict(synth.CONFIGS["edge"])[layer]
+    x, blob = oracle_container(layer, gen)
+    say("edge", layer, x.size)
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got == x).all()
+    want = O.decode_layer(blob)
+    assert (got == want).all()
+
+
+def test_heavy_parity():
+    x, blob = oracle_container("heavy", synth.heavy)
+    say("heavy", x.size)
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got == x).all()
+    # oracle bit-by-bit decode of the first and last stripes, compared in place
+    first = O.decode_stripes(blob, 0, 1, 1 << 26)
+    last = O.decode_stripes(blob, 3, 1, 1 << 26)
+    assert (got[: 1 << 26] == first).all() and (got[3 << 26:] == last).all()
+
+
+def test_trunk_layer_parity():
+    x, blob = oracle_container("trunk", synth.trunk_layer)
+    say("trunk", x.size)
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got == x).all()
+    n_str = -(-x.size // (1 << 26))
+    for s in (0, n_str - 1):
+        size = min(1 << 26, x.size - (s << 26))
+        want = O.decode_stripes(blob, s, 1, size)
+        assert (got[s << 26: (s << 26) + size] == want).all()
+
+
+def test_packer_containers_decode_on_gpu():
+    for name, gen in (("tiny", synth.tiny), ("edge_fib40", synth.edge_fib40)):
+        x = gen()
+        blob = k3huf.encode_layer(x)
+        say("packer", name)
+        got, st = gpu_decode(blob)
+        assert st == 0 and (got == x).all()
+
+
+def test_repeat_and_stream_invariance():
+    x, blob = oracle_container("tiny", synth.tiny)
+    s = torch.cuda.Stream()
+    say("stream invariance")
+    a, sa = gpu_decode(blob)
+    b, sb = gpu_decode(blob, stream=s)
+    c, sc = gpu_decode(blob, stream=s)
+    assert sa == sb == sc == 0
+    assert (a == b).all() and (b == c).all() and (a == x).all()
+
+
+# ---------------------------------------------------------------------------
+# corrupted containers: flagged through d_status, never a fault
+
+def _hdr_field_off(blob, s):
+    return int(np.frombuffer(bytes(blob[304 + 8 * s: 312 + 8 * s]), "<u8")[0])
+
+
+def test_corrupt_header_is_flagged_and_nothing_written():
+    x = synth.small_random(9, 3 * 65536 + 514)
+    good = O.encode_layer(x)
+    lut = k3huf.build_table(k3huf.layer_info(good)["codelen"])
+    blob = good.copy()
+    blob[0] ^= 0xFF
+    say("corrupt header")
+    got, st = gpu_decode(blob, lut=lut, out_bytes=x.size)
+    assert st & k3huf.DEV_HEADER
+    assert (got == 0xA5).all()
+
+
+def test_wrong_out_size_is_flagged():
+    x = synth.small_random(10, 65536 * 2)
+    blob = O.encode_layer(x)
+    lut = k3huf.build_table(k3huf.layer_info(blob)["codelen"])
+    say("wrong out size")
+    got, st = gpu_decode(blob, lut=lut, out_bytes=65536 * 2 + 2)
+    assert st & k3huf.DEV_HEADER
+
+
+def test_corrupt_index_and_stripe_are_flagged():
+    x = synth.small_random(11, 3 * 65536)
+    blob = O.encode_layer(x)
+    off = _hdr_field_off(blob, 0)
+    b1 = blob.copy()
+    b1[off + 32 + 136 * 1 + 8 + 2 * 5] ^= 1        # lane 5 of subblock 1
+    say("corrupt lane bits")
+    got, st = gpu_decode(b1)
+    assert st & k3huf.DEV_INDEX
+    assert (got[:65536] == x[:65536]).all()          # the other subblocks still decode
+    assert (got[2 * 65536:] == x[2 * 65536:]).all()
+    b2 = blob.copy()
+    b2[304: 312] = np.frombuffer(np.uint64(b2.size + 4096).tobytes(), np.uint8)
+    say("corrupt stripe offset")
+    got, st = gpu_decode(b2, lut=k3huf.build_table(k3huf.layer_info(blob)["codelen"]),
+                         out_bytes=x.size)
+    assert st & k3huf.DEV_STRIPE
+
+
+def test_corrupt_bits_are_detectable():
+    x = synth.small_random(12, 2 * 65536)
+    blob = O.encode_layer(x)
+    st0 = blob.copy()
+    off = _hdr_field_off(blob, 0)
+    bits_off = int(np.frombuffer(bytes(blob[off + 24: off + 28]), "<u4")[0])
+    st0[off + bits_off + 333] ^= 0x24
+    say("corrupt bits")
+    got, st = gpu_decode(st0)
+    assert st != 0 or not (got == x).all()
+
+
+def test_unused_slot_is_flagged():
+    # one-symbol table: codes are '0'; a '1' bit hits an unused slot
+    x = synth.edge_single(n_bytes=65536)
+    blob = O.encode_layer(x).copy()
+    off = _hdr_field_off(blob, 0)
+    bits_off = int(np.frombuffer(bytes(blob[off + 24: off + 28]), "<u4")[0])
+    blob[off + bits_off] = 0x80
+    say("unused slot")
+    got, st = gpu_decode(blob)
+    assert st & k3huf.DEV_CODE
+
+
+def test_bad_arguments_raise_before_launch():
+    x = synth.small_random(13, 4096)
+    blob = O.encode_layer(x)
+    lut = k3huf.build_table(k3huf.layer_info(blob)["codelen"])
+    d_blob, d_lut = to_dev(blob, lut)
+    d_out = torch.empty(4096 + 16, dtype=torch.uint8, device=DEV)
+    say("bad args")
+    with pytest.raises(k3huf.K3HufError):
+        k3huf.decode_layer(d_blob, d_lut, d_out[1: 4097])       # misaligned output
+    with pytest.raises(k3huf.K3HufError):
+        k3huf.decode_layer(d_blob, d_lut, d_out[:4095])         # odd size
+    with pytest.raises(k3huf.K3HufError):
+        k3huf.decode_layer(d_blob[:100], d_lut, d_out[:4096])   # blob shorter than a header
+
+
+# ---------------------------------------------------------------------------
+# layer ring (K3 TUNING page, section 2: a two-slot trunk ring)
+
+@pytest.mark.parametrize("n_slots,n_streams", [(2, 2), (1, 1), (3, 2), (2, 1)])
+def test_ring_decodes_layers_in_order(n_slots, n_streams):
+    sizes = [3 * 65536 + 514, 65536, 2 * 65536 + 2, 5 * 65536, 1026, 4 * 65536 + 100]
+    xs = [synth.small_random(100 + k, n) for k, n in enumerate(sizes)]
+    blobs = [O.encode_layer(x) for x in xs]
+    luts = [k3huf.build_table(k3huf.layer_info(b)["codelen"]) for b in blobs]
+    dev = [to_dev(b, l) for b, l in zip(blobs, luts)]
+    layers = [(db, dl, x.size) for (db, dl), x in zip(dev, xs)]
+    slot_bytes = max(sizes)
+    slots = [torch.empty(slot_bytes, dtype=torch.uint8, device=DEV) for _ in range(n_slots)]
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]
+    by_handle = {s.cuda_stream: s for s in streams}
+    results = [torch.empty(n, dtype=torch.uint8, device=DEV) for n in sizes]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+
+    def consume(k, slot, handle):
+        with torch.cuda.stream(by_handle[handle]):
+            results[k].copy_(slots[slot][: sizes[k]])
+
+    say("ring", n_slots, n_streams)
+    k3huf.decode_ring(layers, slots, streams, consume, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for k in range(len(xs)):
+        assert (results[k].cpu().numpy() == xs[k]).all(), k
