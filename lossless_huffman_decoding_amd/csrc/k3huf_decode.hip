@@ -23,18 +23,36 @@
 
 namespace {
 
-constexpr int kWaves = 4;                       // waves (subblocks in flight) per workgroup
+// One workgroup per CU; each wave decodes whole subblocks, one lane chunk per
+// lane. Every global load is issued at least one phase before its data is
+// used: the bitstream reaches the decoder through a per-lane ring in LDS that
+// is topped up a phase ahead, and the even-plane bytes a phase writes out are
+// requested when the phase starts.
+constexpr int kWaves = 12;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPhase = 64;                      // symbols per lane between write-outs
-constexpr int kPhases = K3HUF_LANE_SYMS / kPhase;
-constexpr int kGroups = kPhase / 4;             // window refills per phase (4 symbols each)
-constexpr int kStageStride = 80;                // LDS bytes per lane chunk (64 + 16 pad)
+constexpr int kPhase = 32;                            // symbols per lane per phase
+constexpr int kPhases = K3HUF_LANE_SYMS / kPhase;    // 16
+constexpr int kGroups = kPhase / 4;                   // window refills per phase
+constexpr int kRing = 32;                             // ring capacity in dwords
+constexpr int kRingStride = 36;                       // dwords per lane: 32 slots, 3 mirror, 1 pad
+// dwords a phase may read at or after the dword holding its first bit:
+// 28 symbols of at most 12 bits before the last window, plus a 64-bit window
+constexpr int kNeed = 14;
+constexpr int kPre = 2;                               // 16-byte units requested ahead per phase
+constexpr int kStageStride = 48;                      // LDS bytes per lane chunk (32 + 16 pad)
 constexpr uint32_t kSubPerStripe = K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES;
 
-// LDS table entry: bits 3:0 code length, 15:8 symbol, bit 24 "unused slot".
-// Unused slots decode as length 12 so a lane always advances; the flag bit
-// surfaces as K3HUF_DEV_CODE.
-constexpr uint32_t kBadEntry = (1u << 24) | 12u;
+// LDS decode table, derived per workgroup from the 4096-entry
+// (symbol << 4 | length) table: one lookup of the top 12 window bits yields
+// the first code and, when the next code also lies inside those 12 bits, the
+// second one too (the "double-symbol table" the K3 page names under "if
+// revisited"; the container format is unchanged).
+//   [4:0]   bits consumed by the entry's symbols (T)
+//   [15:8]  first symbol      [23:16] second symbol (if kFit)
+//   [27:24] length of the first code
+constexpr uint32_t kT = 31u;
+constexpr uint32_t kFit = 1u << 28;   // entry holds two symbols
+constexpr uint32_t kBad = 1u << 29;   // index no code covers (decoded as 12 bits)
 
 struct DecodeArgs {
     const uint8_t* blob;
@@ -67,78 +85,164 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// byte t of the result = symbol byte (byte 1) of e, other bytes from w
-__device__ __forceinline__ uint32_t put_sym(uint32_t w, uint32_t e, int t) {
-    constexpr uint32_t sel[4] = {0x03020105u, 0x03020500u, 0x03050100u, 0x05020100u};
-    return __builtin_amdgcn_perm(e, w, sel[t]);
+// Table entry for 12-bit index i from the (symbol << 4 | length) table.
+__device__ uint32_t make_entry(const uint16_t* lut, uint32_t i) {
+    const uint32_t a = lut[i];
+    const uint32_t l1 = a & 15u;
+    if (l1 == 0 || l1 > K3HUF_MAXLEN) return kBad | kFit | (12u << 24) | 12u;
+    uint32_t e = (l1 << 24) | (((a >> 4) & 0xFFu) << 8) | l1;
+    if (l1 < K3HUF_MAXLEN) {
+        const uint32_t b = lut[(i << l1) & 0xFFFu];
+        const uint32_t l2 = b & 15u;
+        if (l2 && l1 + l2 <= K3HUF_MAXLEN)
+            e = (e & ~kT) | kFit | (((b >> 4) & 0xFFu) << 16) | (l1 + l2);
+    }
+    return e;
+}
+
+// Two symbols from the top of the window, then shift them out. An entry that
+// holds one symbol is completed with a second lookup after its first code.
+__device__ __forceinline__ uint32_t step2(const uint32_t* tab, uint64_t& acc) {
+    uint32_t e = tab[uint32_t(acc >> 52)];
+    if (!(e & kFit)) {
+        const uint32_t t = e & kT;
+        const uint32_t e2 = tab[uint32_t((acc << t) >> 52)];
+        e = (e & 0xFF00u) | (((e2 >> 8) & 0xFFu) << 16) | (t + ((e2 >> 24) & 15u)) | kFit |
+            ((e | e2) & kBad);
+    }
+    acc <<= (e & kT);
+    return e;
+}
+
+// 64-bit window starting at stream bit `pos` from the lane's ring (dwords
+// held byte-swapped, dword d at slot d mod 32, slots 32..34 mirror 0..2):
+// dwords j..j+2 with j = floor((pos - 1) / 32), shifted right by (-pos) mod 32.
+__device__ __forceinline__ uint64_t window(const uint32_t* ring, uint32_t pos) {
+    const int j = (int(pos) - 1) >> 5;
+    const uint32_t* rp = ring + (uint32_t(j) & (kRing - 1));
+    const uint32_t d0 = rp[0], d1 = rp[1], d2 = rp[2];
+    const uint32_t r = 0u - pos;
+    return (uint64_t(__builtin_amdgcn_alignbit(d0, d1, r)) << 32) |
+           __builtin_amdgcn_alignbit(d1, d2, r);
+}
+
+// 16-byte unit of the bitstream starting at dword d (a multiple of 4), read
+// from at most dword dmax so the read stays inside the blob.
+__device__ __forceinline__ uint4 load_unit(const uint8_t* bits, int d, int dmax) {
+    return *reinterpret_cast<const uint4*>(bits + 4 * min(d, dmax));
+}
+__device__ __forceinline__ void put_unit(uint32_t* ring, int d, uint4 v) {
+    const uint4 b = make_uint4(bswap32(v.x), bswap32(v.y), bswap32(v.z), bswap32(v.w));
+    const uint32_t s = uint32_t(d) & (kRing - 1);
+    *reinterpret_cast<uint4*>(ring + s) = b;
+    if (s == 0) *reinterpret_cast<uint4*>(ring + kRing) = b;
 }
 
 // Decode one subblock with one wave. FULL: all 64 lane chunks hold 512
-// symbols; otherwise lane t holds clamp(nsyms - 512 t, 0, 512).
+// symbols (two symbols per table step); otherwise lane t holds
+// clamp(nsyms - 512 t, 0, 512) and decodes one symbol per step.
 template <bool FULL>
-__device__ __forceinline__ void decode_subblock(const DecodeArgs& a, const uint32_t* lut_s, uint8_t* stage,
-                                const uint8_t* bits, uint32_t jmax, const uint8_t* even_sb,
-                                uint8_t* out_sb, uint32_t lane_start, uint32_t lane_bits,
-                                uint32_t nsyms, int lane) {
-    const uint32_t* bits32 = reinterpret_cast<const uint32_t*>(bits);
+__device__ __forceinline__ void decode_subblock(const DecodeArgs& a, const uint32_t* tab,
+                                                uint32_t* ring, uint8_t* stage,
+                                                const uint8_t* bits, int dmax,
+                                                const uint8_t* even_sb, uint8_t* out_sb,
+                                                uint32_t lane_start, uint32_t lane_bits,
+                                                uint32_t nsyms, int lane) {
     const int lane_cnt = FULL ? int(K3HUF_LANE_SYMS)
                               : min(max(int(nsyms) - lane * int(K3HUF_LANE_SYMS), 0),
                                     int(K3HUF_LANE_SYMS));
     uint32_t pos = lane_start;
     uint32_t bad = 0;
-    uint8_t* my_stage = stage + lane * kStageStride;
-    const int sub_line = lane >> 3, part = lane & 7;
+    // fill the ring with the 32 dwords from the 16-byte unit holding the
+    // lane's first window dword
+    int hi = ((int(pos) - 1) >> 5) & ~3;
+    {
+        uint4 u[kRing / 4];
+#pragma unroll
+        for (int q = 0; q < kRing / 4; ++q) u[q] = load_unit(bits, hi + 4 * q, dmax);
+#pragma unroll
+        for (int q = 0; q < kRing / 4; ++q) put_unit(ring, hi + 4 * q, u[q]);
+        hi += kRing;
+    }
+    const int sub_line = lane >> 2, part = lane & 3;
 
     for (int ph = 0; ph < kPhases; ++ph) {
+        // request the next units while there is room behind the live window
+        const int j0 = (int(pos) - 1) >> 5;
+        const int room = (j0 + kRing - hi) >> 2;
+        uint4 pre[kPre];
+#pragma unroll
+        for (int q = 0; q < kPre; ++q)
+            if (q < room) pre[q] = load_unit(bits, hi + 4 * q, dmax);
+        // even-plane bytes this phase writes out
+        uint2 ev[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t u = uint32_t(rr * 16 + sub_line) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
+            if (FULL || u < nsyms) ev[rr] = *reinterpret_cast<const uint2*>(even_sb + u);
+        }
+
         uint32_t w[kGroups];
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-            // 64-bit window starting at bit `pos`: dwords j..j+2 with
-            // j = floor((pos - 1) / 32), right-aligned by (-pos) mod 32
-            const int j = min((int(pos) - 1) >> 5, int(jmax));
-            const uint32_t d0 = bswap32(bits32[j]);
-            const uint32_t d1 = bswap32(bits32[j + 1]);
-            const uint32_t d2 = bswap32(bits32[j + 2]);
-            const uint32_t r = 0u - pos;
-            uint64_t acc = (uint64_t(__builtin_amdgcn_alignbit(d0, d1, r)) << 32) |
-                           __builtin_amdgcn_alignbit(d1, d2, r);
-            uint32_t sum = 0, ww = 0;
+            uint64_t acc = window(ring, pos);
+            if (FULL) {
+                const uint32_t e1 = step2(tab, acc);
+                const uint32_t e2 = step2(tab, acc);
+                pos += (e1 + e2) & 0xFFu;
+                bad |= e1 | e2;
+                w[g] = __builtin_amdgcn_perm(e2, e1, 0x06050201u);
+            } else {
+                uint32_t ww = 0;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                uint32_t e = lut_s[uint32_t(acc >> 52)];
-                if (!FULL && ph * kPhase + g * 4 + t >= lane_cnt) e = 0;
-                acc <<= (e & 15u);
-                sum += e;
-                ww = put_sym(ww, e, t);
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t e = tab[uint32_t(acc >> 52)];
+                    const bool live = ph * kPhase + g * 4 + t < lane_cnt;
+                    const uint32_t l = live ? (e >> 24) & 15u : 0u;
+                    if (live) bad |= e;
+                    acc <<= l;
+                    pos += l;
+                    constexpr uint32_t sel[4] = {0x03020105u, 0x03020500u, 0x03050100u, 0x05020100u};
+                    ww = __builtin_amdgcn_perm(e, ww, sel[t]);
+                }
+                w[g] = ww;
             }
-            pos += sum & 0xFFu;
-            bad |= sum;
-            w[g] = ww;
         }
+
+        // ring upkeep for the next phase
 #pragma unroll
-        for (int q = 0; q < kGroups / 4; ++q)
-            *reinterpret_cast<uint4*>(my_stage + 16 * q) =
-                make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+        for (int q = 0; q < kPre; ++q)
+            if (q < room) put_unit(ring, hi + 4 * q, pre[q]);
+        hi += 4 * max(min(room, kPre), 0);
+        const int j1 = (int(pos) - 1) >> 5;
+        while (__any(hi < j1 + kNeed)) {  // at most 3 rounds: hi >= j1 + 2 here
+            if (hi < j1 + kNeed) {
+                put_unit(ring, hi, load_unit(bits, hi, dmax));
+                hi += 4;
+            }
+        }
+
+        // stage this phase's symbols, then interleave with the even plane
+        uint8_t* my_stage = stage + lane * kStageStride;
+        *reinterpret_cast<uint4*>(my_stage) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(my_stage + 16) = make_uint4(w[4], w[5], w[6], w[7]);
         wave_sync();
-        // write-out: 8 lanes per lane chunk, 8 symbols (16 output bytes) per lane
 #pragma unroll
-        for (int rr = 0; rr < 64 / 8; ++rr) {
-            const int line = rr * 8 + sub_line;
+        for (int rr = 0; rr < 4; ++rr) {
+            const int line = rr * 16 + sub_line;
             const uint2 sy = *reinterpret_cast<const uint2*>(stage + line * kStageStride + part * 8);
             const uint32_t u = uint32_t(line) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
             if (FULL || u + 8 <= nsyms) {
-                const uint2 ev = *reinterpret_cast<const uint2*>(even_sb + u);
                 uint4 o;
-                o.x = __builtin_amdgcn_perm(sy.x, ev.x, 0x05010400u);
-                o.y = __builtin_amdgcn_perm(sy.x, ev.x, 0x07030602u);
-                o.z = __builtin_amdgcn_perm(sy.y, ev.y, 0x05010400u);
-                o.w = __builtin_amdgcn_perm(sy.y, ev.y, 0x07030602u);
+                o.x = __builtin_amdgcn_perm(sy.x, ev[rr].x, 0x05010400u);
+                o.y = __builtin_amdgcn_perm(sy.x, ev[rr].x, 0x07030602u);
+                o.z = __builtin_amdgcn_perm(sy.y, ev[rr].y, 0x05010400u);
+                o.w = __builtin_amdgcn_perm(sy.y, ev[rr].y, 0x07030602u);
                 *reinterpret_cast<uint4*>(out_sb + 2 * u) = o;
             } else if (u < nsyms) {
-                const uint2 ev = *reinterpret_cast<const uint2*>(even_sb + u);
                 const uint32_t m = nsyms - u;
                 for (uint32_t i = 0; i < m; ++i) {
-                    const uint32_t e8 = i < 4 ? (ev.x >> (8 * i)) : (ev.y >> (8 * (i - 4)));
+                    const uint32_t e8 = i < 4 ? (ev[rr].x >> (8 * i)) : (ev[rr].y >> (8 * (i - 4)));
                     const uint32_t s8 = i < 4 ? (sy.x >> (8 * i)) : (sy.y >> (8 * (i - 4)));
                     *reinterpret_cast<uint16_t*>(out_sb + 2 * (u + i)) =
                         uint16_t((e8 & 0xFFu) | ((s8 & 0xFFu) << 8));
@@ -147,12 +251,13 @@ __device__ __forceinline__ void decode_subblock(const DecodeArgs& a, const uint3
         }
         wave_sync();
     }
-    if (bad & 0xFF000000u) flag(a.status, K3HUF_DEV_CODE);
+    if (bad & kBad) flag(a.status, K3HUF_DEV_CODE);
     if (pos != lane_start + lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
 }
 
 __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
-    __shared__ uint32_t lut_s[K3HUF_LUT_ENTRIES];
+    __shared__ uint32_t tab[K3HUF_LUT_ENTRIES];
+    __shared__ __attribute__((aligned(16))) uint32_t ring_all[kWaves * 64 * kRingStride];
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * 64 * kStageStride];
 
     // layer header must describe exactly this call (uniform over the grid)
@@ -167,14 +272,12 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         return;
     }
 
-    for (int i = threadIdx.x; i < K3HUF_LUT_ENTRIES; i += kThreads) {
-        const uint32_t v = a.lut[i];
-        lut_s[i] = v ? (((v >> 4) & 0xFFu) << 8) | (v & 15u) : kBadEntry;
-    }
+    for (int i = threadIdx.x; i < K3HUF_LUT_ENTRIES; i += kThreads) tab[i] = make_entry(a.lut, i);
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const uint32_t wave = uniform(threadIdx.x >> 6);
+    uint32_t* ring = ring_all + (wave * 64 + lane) * kRingStride;
     uint8_t* stage = stage_all + wave * (64 * kStageStride);
 
     for (uint32_t k = blockIdx.x * kWaves + wave; k < a.n_sub; k += gridDim.x * kWaves) {
@@ -224,16 +327,16 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
             continue;
         }
         const uint8_t* bits = st + bits_off;
-        // last dword index whose 3-dword window stays inside the blob
-        const uint32_t jmax = uint32_t((a.blob_bytes - (soff + bits_off) - 12) / 4);
+        // last 16-byte unit (in dwords from the bitstream start) inside the blob
+        const int dmax = int(((a.blob_bytes - (soff + bits_off) - 16) / 4) & ~3ull);
         const uint8_t* even_sb = st + even_off + uint64_t(jsb) * K3HUF_SUBBLOCK_SYMS;
         uint8_t* out_sb = a.out + uint64_t(k) * K3HUF_SUBBLOCK_BYTES;
         const uint32_t lane_start = start_bit + incl - lb;
         if (nsyms == K3HUF_SUBBLOCK_SYMS)
-            decode_subblock<true>(a, lut_s, stage, bits, jmax, even_sb, out_sb, lane_start, lb,
+            decode_subblock<true>(a, tab, ring, stage, bits, dmax, even_sb, out_sb, lane_start, lb,
                                   nsyms, lane);
         else
-            decode_subblock<false>(a, lut_s, stage, bits, jmax, even_sb, out_sb, lane_start, lb,
+            decode_subblock<false>(a, tab, ring, stage, bits, dmax, even_sb, out_sb, lane_start, lb,
                                    nsyms, lane);
     }
 }
