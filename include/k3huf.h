@@ -25,7 +25,7 @@
  *   layer header (K3HUF_HDR_BYTES = 304):
  *     0   char[4] magic "K3HF"         4  u16 version = 1
  *     6   u16 maxlen = 12               8  u32 stripe_bytes = 2^26
- *     12  u32 subblock_bytes = 2^16     16 u32 lane_syms = 512
+ *     12  u32 subblock_bytes = 2^16     16 u32 lane_syms = 256
  *     20  u32 n_stripes = ceil(raw_bytes / 2^26)
  *     24  u64 raw_bytes (even, > 0)     32 u32 n_subblocks (total)
  *     36  u32 reserved = 0              40 u64 container_bytes
@@ -37,10 +37,10 @@
  *     12 u32 bit_bytes = ceil(n_bits / 8) rounded up to 16
  *     16 u32 first_subblock = s * 1024   20 u32 n_subblocks = ceil(n_syms / 32768)
  *     24 u32 bits_off   28 u32 even_off  (both from the record start, 16-aligned)
- *     32 subblock records, K3HUF_SUBBLOCK_REC_BYTES = 136 each:
+ *     32 subblock records, K3HUF_SUBBLOCK_REC_BYTES = 264 each:
  *          u32 start_bit (stripe-relative bit index of the subblock's first code)
  *          u32 n_syms    (32768, or fewer in the stripe's last subblock)
- *          u16 lane_bits[64] (code bits of each 512-symbol lane chunk; 0 if empty)
+ *          u16 lane_bits[128] (code bits of each 256-symbol lane chunk; 0 if empty)
  *        zero pad to 16
  *     bits_off: the stripe's codes, most-significant bit first (K3 page,
  *        "decode loop": the stream head sits at the top of the bit window),
@@ -64,7 +64,7 @@ extern "C" {
 #define K3HUF_STRIPE_BYTES (1u << 26)
 #define K3HUF_SUBBLOCK_BYTES (1u << 16)
 #define K3HUF_SUBBLOCK_SYMS (K3HUF_SUBBLOCK_BYTES / 2)
-#define K3HUF_LANE_SYMS 512u
+#define K3HUF_LANE_SYMS 256u
 #define K3HUF_LANES (K3HUF_SUBBLOCK_SYMS / K3HUF_LANE_SYMS)
 #define K3HUF_HDR_BYTES 304u
 #define K3HUF_STRIPE_HDR_BYTES 32u

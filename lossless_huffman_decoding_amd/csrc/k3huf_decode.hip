@@ -23,36 +23,47 @@
 
 namespace {
 
-// One workgroup per CU; each wave decodes whole subblocks, one lane chunk per
-// lane. Every global load is issued at least one phase before its data is
-// used: the bitstream reaches the decoder through a per-lane ring in LDS that
-// is topped up a phase ahead, and the even-plane bytes a phase writes out are
-// requested when the phase starts.
+// One 12-wave workgroup per CU. A work unit is half a subblock: 64 lane
+// chunks of 256 symbols, lane t decoding chunk t. Every HBM line is read or
+// written in one burst:
+//   - the unit's bitstream is copied into the wave's LDS buffer with
+//     coalesced 16-byte loads before its lanes decode (a unit whose codes
+//     exceed the buffer is decoded in passes over consecutive lane ranges);
+//   - the even-plane bytes of two phases (a whole 128-byte line per chunk)
+//     are requested together into registers;
+//   - each phase's 64 symbols per chunk are staged in LDS, so every output
+//     store instruction writes whole 128-byte lines.
 constexpr int kWaves = 12;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPhase = 32;                            // symbols per lane per phase
-constexpr int kPhases = K3HUF_LANE_SYMS / kPhase;    // 16
-constexpr int kGroups = kPhase / 4;                   // window refills per phase
-constexpr int kRing = 32;                             // ring capacity in dwords
-constexpr int kRingStride = 36;                       // dwords per lane: 32 slots, 3 mirror, 1 pad
-// dwords a phase may read at or after the dword holding its first bit:
-// 28 symbols of at most 12 bits before the last window, plus a 64-bit window
-constexpr int kNeed = 14;
-constexpr int kPre = 2;                               // 16-byte units requested ahead per phase
-constexpr int kStageStride = 48;                      // LDS bytes per lane chunk (32 + 16 pad)
+constexpr int kUnitLanes = 64;                        // lane chunks per work unit
+constexpr int kUnitSyms = kUnitLanes * K3HUF_LANE_SYMS;  // 16384
+constexpr int kUnitsPerSub = K3HUF_LANES / kUnitLanes;   // 2
+constexpr int kPhase = 64;                            // symbols per lane per phase
+constexpr int kPhases = K3HUF_LANE_SYMS / kPhase;    // 4
+constexpr int kSuper = 2;                             // phases per even-plane prefetch
+constexpr int kGroups = kPhase / 4;                   // 4-symbol groups per phase
+constexpr int kRounds = 64 / 8;                       // write-out rounds (8 chunks each)
+constexpr int kBufBytes = 8192;                       // per-wave bitstream buffer
+constexpr int kBufUnits = kBufBytes / 16;
+constexpr int kStageStride = kPhase;                  // LDS bytes per chunk per phase
+constexpr int kWaveLds = kBufBytes + 64 * kStageStride;
+constexpr int kTabBytes = K3HUF_LUT_ENTRIES * 4;
+constexpr int kLdsBytes = kTabBytes + kWaves * kWaveLds;
 constexpr uint32_t kSubPerStripe = K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES;
+static_assert(kLdsBytes <= 163840, "LDS budget");
 
 // LDS decode table, derived per workgroup from the 4096-entry
 // (symbol << 4 | length) table: one lookup of the top 12 window bits yields
 // the first code and, when the next code also lies inside those 12 bits, the
 // second one too (the "double-symbol table" the K3 page names under "if
 // revisited"; the container format is unchanged).
-//   [4:0]   bits consumed by the entry's symbols (T)
-//   [15:8]  first symbol      [23:16] second symbol (if kFit)
+//   [4:0]   bits consumed by the entry's symbols (T); [7:5] zero
+//   [15:8]  first symbol      [23:16] second symbol
 //   [27:24] length of the first code
-constexpr uint32_t kT = 31u;
-constexpr uint32_t kFit = 1u << 28;   // entry holds two symbols
-constexpr uint32_t kBad = 1u << 29;   // index no code covers (decoded as 12 bits)
+//   [29]    index no code covers (decoded as a 12-bit code)
+//   [31]    entry holds only the first symbol
+constexpr uint32_t kBad = 1u << 29;
+constexpr uint32_t kOne = 1u << 31;
 
 struct DecodeArgs {
     const uint8_t* blob;
@@ -84,181 +95,233 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
 }
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
 
 // Table entry for 12-bit index i from the (symbol << 4 | length) table.
 __device__ uint32_t make_entry(const uint16_t* lut, uint32_t i) {
     const uint32_t a = lut[i];
     const uint32_t l1 = a & 15u;
-    if (l1 == 0 || l1 > K3HUF_MAXLEN) return kBad | kFit | (12u << 24) | 12u;
-    uint32_t e = (l1 << 24) | (((a >> 4) & 0xFFu) << 8) | l1;
+    if (l1 == 0 || l1 > K3HUF_MAXLEN) return kBad | (12u << 24) | 12u;
+    const uint32_t e = (l1 << 24) | (((a >> 4) & 0xFFu) << 8) | l1;
     if (l1 < K3HUF_MAXLEN) {
         const uint32_t b = lut[(i << l1) & 0xFFFu];
         const uint32_t l2 = b & 15u;
-        if (l2 && l1 + l2 <= K3HUF_MAXLEN)
-            e = (e & ~kT) | kFit | (((b >> 4) & 0xFFu) << 16) | (l1 + l2);
+        if (l2 && l1 + l2 <= K3HUF_MAXLEN) return e + (((b >> 4) & 0xFFu) << 16) + l2;
     }
-    return e;
+    return e | kOne;
 }
 
-// Two symbols from the top of the window, then shift them out. An entry that
-// holds one symbol is completed with a second lookup after its first code.
+__device__ __forceinline__ uint32_t peek(const uint32_t* tab, uint64_t acc) {
+    return tab[uint32_t(acc >> 52)];
+}
+
+// Two symbols from the top of the window, then shift them out. An entry
+// holding one symbol is completed with a second lookup after its first code.
 __device__ __forceinline__ uint32_t step2(const uint32_t* tab, uint64_t& acc) {
-    uint32_t e = tab[uint32_t(acc >> 52)];
-    if (!(e & kFit)) {
-        const uint32_t t = e & kT;
-        const uint32_t e2 = tab[uint32_t((acc << t) >> 52)];
-        e = (e & 0xFF00u) | (((e2 >> 8) & 0xFFu) << 16) | (t + ((e2 >> 24) & 15u)) | kFit |
-            ((e | e2) & kBad);
+    uint32_t e = peek(tab, acc);
+    if (int32_t(e) < 0) {
+        const uint32_t e2 = peek(tab, acc << (e & 63u));
+        e = e + (((e2 >> 8) & 0xFFu) << 16) + ((e2 >> 24) & 15u) + kOne;
+        e |= e2 & kBad;
     }
-    acc <<= (e & kT);
+    acc <<= (e & 63u);
     return e;
 }
 
-// 64-bit window starting at stream bit `pos` from the lane's ring (dwords
-// held byte-swapped, dword d at slot d mod 32, slots 32..34 mirror 0..2):
-// dwords j..j+2 with j = floor((pos - 1) / 32), shifted right by (-pos) mod 32.
-__device__ __forceinline__ uint64_t window(const uint32_t* ring, uint32_t pos) {
-    const int j = (int(pos) - 1) >> 5;
-    const uint32_t* rp = ring + (uint32_t(j) & (kRing - 1));
-    const uint32_t d0 = rp[0], d1 = rp[1], d2 = rp[2];
-    const uint32_t r = 0u - pos;
+// 64-bit window whose top bit is the bit after buffer bit pm1: buffer dwords
+// q..q+2 (q = pm1 / 32, held byte-swapped), shifted right by 31 - pm1 mod 32.
+__device__ __forceinline__ uint64_t window(const uint32_t* buf, uint32_t pm1) {
+    const uint32_t* p = buf + (pm1 >> 5);
+    const uint32_t d0 = p[0], d1 = p[1], d2 = p[2];
+    const uint32_t r = ~pm1;
     return (uint64_t(__builtin_amdgcn_alignbit(d0, d1, r)) << 32) |
            __builtin_amdgcn_alignbit(d1, d2, r);
 }
 
-// 16-byte unit of the bitstream starting at dword d (a multiple of 4), read
-// from at most dword dmax so the read stays inside the blob.
-__device__ __forceinline__ uint4 load_unit(const uint8_t* bits, int d, int dmax) {
-    return *reinterpret_cast<const uint4*>(bits + 4 * min(d, dmax));
-}
-__device__ __forceinline__ void put_unit(uint32_t* ring, int d, uint4 v) {
-    const uint4 b = make_uint4(bswap32(v.x), bswap32(v.y), bswap32(v.z), bswap32(v.w));
-    const uint32_t s = uint32_t(d) & (kRing - 1);
-    *reinterpret_cast<uint4*>(ring + s) = b;
-    if (s == 0) *reinterpret_cast<uint4*>(ring + kRing) = b;
+// staged 16-byte unit q of chunk c's phase symbols, swizzled so that 8
+// consecutive lanes writing or 32 lanes reading hit distinct LDS banks
+__device__ __forceinline__ int stage_off(int c, int q) {
+    return c * kStageStride + ((q ^ ((c >> 2) & 3)) << 4);
 }
 
-// Decode one subblock with one wave. FULL: all 64 lane chunks hold 512
-// symbols (two symbols per table step); otherwise lane t holds
-// clamp(nsyms - 512 t, 0, 512) and decodes one symbol per step.
-template <bool FULL>
-__device__ __forceinline__ void decode_subblock(const DecodeArgs& a, const uint32_t* tab,
-                                                uint32_t* ring, uint8_t* stage,
-                                                const uint8_t* bits, int dmax,
-                                                const uint8_t* even_sb, uint8_t* out_sb,
-                                                uint32_t lane_start, uint32_t lane_bits,
-                                                uint32_t nsyms, int lane) {
-    const int lane_cnt = FULL ? int(K3HUF_LANE_SYMS)
-                              : min(max(int(nsyms) - lane * int(K3HUF_LANE_SYMS), 0),
-                                    int(K3HUF_LANE_SYMS));
-    uint32_t pos = lane_start;
+struct Unit {
+    const uint8_t* bits;   // stripe bitstream
+    const uint8_t* even;   // this unit's even-plane bytes
+    uint8_t* out;          // this unit's output bytes
+    int dmax;              // last readable 16-byte unit (dwords from `bits`)
+    uint32_t nsyms;        // symbols in this unit (16384 unless last in stripe)
+};
+
+// Decode lanes [l0, l1) of a full unit (64 chunks of 256 symbols) whose
+// bitstream dwords [j0, ...) the caller has placed in `buf`.
+__device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t* tab,
+                                             const uint32_t* buf, uint8_t* stage, const Unit& un,
+                                             int j0, uint32_t lane_start, uint32_t lane_bits,
+                                             int l0, int l1, int lane) {
+    const bool mine = lane >= l0 && lane < l1;
+    // buffer bit index of the lane's first code, minus one (>= 0: the buffer
+    // starts at least one dword before it)
+    uint32_t pm1 = lane_start - 32u * uint32_t(j0) - 1u;
+    const uint32_t pm1_0 = pm1;
     uint32_t bad = 0;
-    // fill the ring with the 32 dwords from the 16-byte unit holding the
-    // lane's first window dword
-    int hi = ((int(pos) - 1) >> 5) & ~3;
-    {
-        uint4 u[kRing / 4];
-#pragma unroll
-        for (int q = 0; q < kRing / 4; ++q) u[q] = load_unit(bits, hi + 4 * q, dmax);
-#pragma unroll
-        for (int q = 0; q < kRing / 4; ++q) put_unit(ring, hi + 4 * q, u[q]);
-        hi += kRing;
-    }
-    const int sub_line = lane >> 2, part = lane & 3;
+    const int sub_line = lane >> 3, part = lane & 7;
+    uint2 ev[kRounds][kSuper];
 
-    for (int ph = 0; ph < kPhases; ++ph) {
-        // request the next units while there is room behind the live window
-        const int j0 = (int(pos) - 1) >> 5;
-        const int room = (j0 + kRing - hi) >> 2;
-        uint4 pre[kPre];
+    for (int sp = 0; sp < kPhases; sp += kSuper) {
+        // the next two phases' even-plane bytes: a whole line per chunk
 #pragma unroll
-        for (int q = 0; q < kPre; ++q)
-            if (q < room) pre[q] = load_unit(bits, hi + 4 * q, dmax);
-        // even-plane bytes this phase writes out
-        uint2 ev[4];
+        for (int rr = 0; rr < kRounds; ++rr) {
+            const int c = rr * 8 + sub_line;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const uint32_t u = uint32_t(rr * 16 + sub_line) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
-            if (FULL || u < nsyms) ev[rr] = *reinterpret_cast<const uint2*>(even_sb + u);
+            for (int f = 0; f < kSuper; ++f) {
+                const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t((sp + f) * kPhase + part * 8);
+                if (c >= l0 && c < l1) ev[rr][f] = *reinterpret_cast<const uint2*>(un.even + u);
+            }
         }
-
-        uint32_t w[kGroups];
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-            uint64_t acc = window(ring, pos);
-            if (FULL) {
-                const uint32_t e1 = step2(tab, acc);
-                const uint32_t e2 = step2(tab, acc);
-                pos += (e1 + e2) & 0xFFu;
-                bad |= e1 | e2;
-                w[g] = __builtin_amdgcn_perm(e2, e1, 0x06050201u);
-            } else {
-                uint32_t ww = 0;
+        for (int q = 0; q < kSuper; ++q) {
+            const int ph = sp + q;
+            if (mine) {
+                // 16 symbols (one staged 16-byte unit) per iteration
+#pragma unroll 1
+                for (int u4 = 0; u4 < kGroups / 4; ++u4) {
+                    uint32_t w[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const uint32_t e = tab[uint32_t(acc >> 52)];
-                    const bool live = ph * kPhase + g * 4 + t < lane_cnt;
-                    const uint32_t l = live ? (e >> 24) & 15u : 0u;
-                    if (live) bad |= e;
-                    acc <<= l;
-                    pos += l;
-                    constexpr uint32_t sel[4] = {0x03020105u, 0x03020500u, 0x03050100u, 0x05020100u};
-                    ww = __builtin_amdgcn_perm(e, ww, sel[t]);
+                    for (int g = 0; g < 4; ++g) {
+                        uint64_t acc = window(buf, pm1);
+                        const uint32_t e1 = step2(tab, acc);
+                        const uint32_t e2 = step2(tab, acc);
+                        pm1 += (e1 + e2) & 0xFFu;
+                        bad |= e1 | e2;
+                        w[g] = __builtin_amdgcn_perm(e2, e1, 0x06050201u);
+                    }
+                    *reinterpret_cast<uint4*>(stage + stage_off(lane, u4)) =
+                        make_uint4(w[0], w[1], w[2], w[3]);
                 }
-                w[g] = ww;
             }
-        }
-
-        // ring upkeep for the next phase
+            wave_sync();
 #pragma unroll
-        for (int q = 0; q < kPre; ++q)
-            if (q < room) put_unit(ring, hi + 4 * q, pre[q]);
-        hi += 4 * max(min(room, kPre), 0);
-        const int j1 = (int(pos) - 1) >> 5;
-        while (__any(hi < j1 + kNeed)) {  // at most 3 rounds: hi >= j1 + 2 here
-            if (hi < j1 + kNeed) {
-                put_unit(ring, hi, load_unit(bits, hi, dmax));
-                hi += 4;
-            }
-        }
-
-        // stage this phase's symbols, then interleave with the even plane
-        uint8_t* my_stage = stage + lane * kStageStride;
-        *reinterpret_cast<uint4*>(my_stage) = make_uint4(w[0], w[1], w[2], w[3]);
-        *reinterpret_cast<uint4*>(my_stage + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-        wave_sync();
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int line = rr * 16 + sub_line;
-            const uint2 sy = *reinterpret_cast<const uint2*>(stage + line * kStageStride + part * 8);
-            const uint32_t u = uint32_t(line) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
-            if (FULL || u + 8 <= nsyms) {
+            for (int rr = 0; rr < kRounds; ++rr) {
+                const int c = rr * 8 + sub_line;
+                if (c < l0 || c >= l1) continue;
+                const uint2 sy = *reinterpret_cast<const uint2*>(stage + stage_off(c, part >> 1) +
+                                                                 (part & 1) * 8);
+                const uint2 e = ev[rr][q];
+                const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
                 uint4 o;
-                o.x = __builtin_amdgcn_perm(sy.x, ev[rr].x, 0x05010400u);
-                o.y = __builtin_amdgcn_perm(sy.x, ev[rr].x, 0x07030602u);
-                o.z = __builtin_amdgcn_perm(sy.y, ev[rr].y, 0x05010400u);
-                o.w = __builtin_amdgcn_perm(sy.y, ev[rr].y, 0x07030602u);
-                *reinterpret_cast<uint4*>(out_sb + 2 * u) = o;
-            } else if (u < nsyms) {
-                const uint32_t m = nsyms - u;
-                for (uint32_t i = 0; i < m; ++i) {
-                    const uint32_t e8 = i < 4 ? (ev[rr].x >> (8 * i)) : (ev[rr].y >> (8 * (i - 4)));
-                    const uint32_t s8 = i < 4 ? (sy.x >> (8 * i)) : (sy.y >> (8 * (i - 4)));
-                    *reinterpret_cast<uint16_t*>(out_sb + 2 * (u + i)) =
-                        uint16_t((e8 & 0xFFu) | ((s8 & 0xFFu) << 8));
+                o.x = __builtin_amdgcn_perm(sy.x, e.x, 0x05010400u);
+                o.y = __builtin_amdgcn_perm(sy.x, e.x, 0x07030602u);
+                o.z = __builtin_amdgcn_perm(sy.y, e.y, 0x05010400u);
+                o.w = __builtin_amdgcn_perm(sy.y, e.y, 0x07030602u);
+                *reinterpret_cast<uint4*>(un.out + 2 * u) = o;
+            }
+            wave_sync();
+        }
+    }
+    if (mine) {
+        if (bad & kBad) flag(a.status, K3HUF_DEV_CODE);
+        if (pm1 - pm1_0 != lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
+    }
+}
+
+// The same for the layer's last unit when it holds fewer than 16384 symbols:
+// lane t decodes clamp(nsyms - 256 t, 0, 256) symbols one table step per
+// symbol; kept plain (it runs at most once per layer).
+__device__ __attribute__((noinline)) void decode_lanes_tail(const DecodeArgs& a, const uint32_t* tab,
+                                                            const uint32_t* buf, uint8_t* stage,
+                                                            const Unit& un, int j0,
+                                                            uint32_t lane_start, uint32_t lane_bits,
+                                                            int l0, int l1, int lane) {
+    const bool mine = lane >= l0 && lane < l1;
+    const int lane_cnt = min(max(int(un.nsyms) - lane * int(K3HUF_LANE_SYMS), 0), int(K3HUF_LANE_SYMS));
+    uint32_t pm1 = lane_start - 32u * uint32_t(j0) - 1u;
+    const uint32_t pm1_0 = pm1;
+    uint32_t bad = 0;
+    const int sub_line = lane >> 3, part = lane & 7;
+#pragma unroll 1
+    for (int ph = 0; ph < kPhases; ++ph) {
+        if (mine) {
+#pragma unroll 1
+            for (int u4 = 0; u4 < kGroups / 4; ++u4) {
+                uint32_t w[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint64_t acc = window(buf, pm1);
+                    uint32_t ww = 0;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t e = peek(tab, acc);
+                        const bool live = ph * kPhase + (u4 * 4 + g) * 4 + t < lane_cnt;
+                        const uint32_t l = live ? (e >> 24) & 15u : 0u;
+                        if (live) bad |= e;
+                        acc <<= l;
+                        pm1 += l;
+                        constexpr uint32_t sel[4] = {0x03020105u, 0x03020500u, 0x03050100u, 0x05020100u};
+                        ww = __builtin_amdgcn_perm(e, ww, sel[t]);
+                    }
+                    w[g] = ww;
                 }
+                *reinterpret_cast<uint4*>(stage + stage_off(lane, u4)) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        wave_sync();
+#pragma unroll 1
+        for (int rr = 0; rr < kRounds; ++rr) {
+            const int c = rr * 8 + sub_line;
+            const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
+            if (c < l0 || c >= l1 || u >= un.nsyms) continue;
+            const uint2 sy = *reinterpret_cast<const uint2*>(stage + stage_off(c, part >> 1) + (part & 1) * 8);
+            const uint2 e = *reinterpret_cast<const uint2*>(un.even + u);
+            const uint32_t m = min(un.nsyms - u, 8u);
+            for (uint32_t i = 0; i < m; ++i) {
+                const uint32_t e8 = i < 4 ? (e.x >> (8 * i)) : (e.y >> (8 * (i - 4)));
+                const uint32_t s8 = i < 4 ? (sy.x >> (8 * i)) : (sy.y >> (8 * (i - 4)));
+                *reinterpret_cast<uint16_t*>(un.out + 2 * (u + i)) = uint16_t((e8 & 0xFFu) | ((s8 & 0xFFu) << 8));
             }
         }
         wave_sync();
     }
-    if (bad & kBad) flag(a.status, K3HUF_DEV_CODE);
-    if (pos != lane_start + lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
+    if (mine) {
+        if (bad & kBad) flag(a.status, K3HUF_DEV_CODE);
+        if (pm1 - pm1_0 != lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
+    }
 }
+
+// Copy bitstream dwords [j0, j0 + 4 * units) into `buf`, byte-swapped so
+// that bit 31 of each dword is the earliest stream bit.
+__device__ __forceinline__ void fill_buffer(uint32_t* buf, const Unit& un, int j0, int units, int lane) {
+    constexpr int kPer = kBufUnits / 64;
+    uint4 v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int u = lane + 64 * i;
+        if (u < units)
+            v[i] = *reinterpret_cast<const uint4*>(un.bits + 4 * min(j0 + 4 * u, un.dmax));
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int u = lane + 64 * i;
+        if (u < units)
+            *reinterpret_cast<uint4*>(buf + 4 * u) =
+                make_uint4(bswap32(v[i].x), bswap32(v[i].y), bswap32(v[i].z), bswap32(v[i].w));
+    }
+    wave_sync();
+}
+
+// first buffer dword for codes starting at stripe bit p: the 16-byte unit
+// holding the dword before bit p
+__device__ __forceinline__ int first_dword(uint32_t p) { return ((int(p) - 1) >> 5) & ~3; }
+// end (exclusive, 16-byte aligned) of the dwords windows may read for codes
+// ending at stripe bit p
+__device__ __forceinline__ int end_dword(uint32_t p) { return (((int(p) - 1) >> 5) + 3 + 3) & ~3; }
 
 __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
-    __shared__ uint32_t tab[K3HUF_LUT_ENTRIES];
-    __shared__ __attribute__((aligned(16))) uint32_t ring_all[kWaves * 64 * kRingStride];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves * 64 * kStageStride];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    uint32_t* tab = reinterpret_cast<uint32_t*>(lds);  // at LDS address 0
 
     // layer header must describe exactly this call (uniform over the grid)
     const uint8_t* b = a.blob;
@@ -277,10 +340,13 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
 
     const int lane = threadIdx.x & 63;
     const uint32_t wave = uniform(threadIdx.x >> 6);
-    uint32_t* ring = ring_all + (wave * 64 + lane) * kRingStride;
-    uint8_t* stage = stage_all + wave * (64 * kStageStride);
+    uint8_t* wl = lds + kTabBytes + wave * kWaveLds;
+    uint32_t* buf = reinterpret_cast<uint32_t*>(wl);
+    uint8_t* stage = wl + kBufBytes;
+    const uint32_t n_units = a.n_sub * kUnitsPerSub;
 
-    for (uint32_t k = blockIdx.x * kWaves + wave; k < a.n_sub; k += gridDim.x * kWaves) {
+    for (uint32_t h = blockIdx.x * kWaves + wave; h < n_units; h += gridDim.x * kWaves) {
+        const uint32_t k = h / kUnitsPerSub, half = h % kUnitsPerSub;
         const uint32_t s = k / kSubPerStripe, jsb = k % kSubPerStripe;
         const uint64_t soff = ld64(b + K3HUF_HDR_BYTES + 8ull * s);
         const uint64_t raw_s = min(uint64_t(K3HUF_STRIPE_BYTES), a.out_bytes - uint64_t(s) * K3HUF_STRIPE_BYTES);
@@ -302,23 +368,20 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
                  soff + even_off + ((uint64_t(n) + 15) & ~15ull) <= a.blob_bytes;
         }
         if (!ok) {
-            if (lane == 0) flag(a.status, K3HUF_DEV_STRIPE);
+            if (lane == 0 && half == 0) flag(a.status, K3HUF_DEV_STRIPE);
             continue;
         }
         const uint8_t* rec = st + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jsb;
         const uint32_t start_bit = ld32(rec);
         const uint32_t nsyms = min(uint32_t(K3HUF_SUBBLOCK_SYMS), n - jsb * K3HUF_SUBBLOCK_SYMS);
         const uint32_t next_start = jsb + 1 < nsb ? ld32(rec + K3HUF_SUBBLOCK_REC_BYTES) : n_bits;
-        const uint32_t lb = *reinterpret_cast<const uint16_t*>(rec + 8 + 2 * lane);
-        // inclusive prefix sum of the lane chunks' bit counts over the wave
-        uint32_t incl = lb;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t v = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += v;
-        }
-        const uint32_t total = uniform(__shfl(incl, 63, 64));
-        const int cnt = min(max(int(nsyms) - lane * int(K3HUF_LANE_SYMS), 0), int(K3HUF_LANE_SYMS));
+        const uint16_t* lbits = reinterpret_cast<const uint16_t*>(rec + 8);
+        const uint32_t lb_lo = lbits[lane], lb_hi = lbits[kUnitLanes + lane];
+        const uint32_t sum_lo = uniform(wave_sum(lb_lo));
+        const uint32_t total = sum_lo + uniform(wave_sum(lb_hi));
+        const uint32_t lb = half ? lb_hi : lb_lo;
+        const int gl = int(half) * kUnitLanes + lane;    // lane chunk within the subblock
+        const int cnt = min(max(int(nsyms) - gl * int(K3HUF_LANE_SYMS), 0), int(K3HUF_LANE_SYMS));
         const bool lane_ok = lb >= uint32_t(cnt) && lb <= uint32_t(cnt) * K3HUF_MAXLEN;
         const bool sb_ok = ld32(rec + 4) == nsyms && start_bit <= n_bits &&
                            uint64_t(start_bit) + total == next_start && next_start <= n_bits;
@@ -326,18 +389,40 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
             if (lane == 0) flag(a.status, K3HUF_DEV_INDEX);
             continue;
         }
-        const uint8_t* bits = st + bits_off;
-        // last 16-byte unit (in dwords from the bitstream start) inside the blob
-        const int dmax = int(((a.blob_bytes - (soff + bits_off) - 16) / 4) & ~3ull);
-        const uint8_t* even_sb = st + even_off + uint64_t(jsb) * K3HUF_SUBBLOCK_SYMS;
-        uint8_t* out_sb = a.out + uint64_t(k) * K3HUF_SUBBLOCK_BYTES;
-        const uint32_t lane_start = start_bit + incl - lb;
-        if (nsyms == K3HUF_SUBBLOCK_SYMS)
-            decode_subblock<true>(a, tab, ring, stage, bits, dmax, even_sb, out_sb, lane_start, lb,
-                                  nsyms, lane);
-        else
-            decode_subblock<false>(a, tab, ring, stage, bits, dmax, even_sb, out_sb, lane_start, lb,
-                                   nsyms, lane);
+        Unit un;
+        un.nsyms = uint32_t(min(max(int(nsyms) - int(half) * kUnitSyms, 0), kUnitSyms));
+        if (un.nsyms == 0) continue;
+        // inclusive prefix sum of this unit's lane chunk bit counts
+        uint32_t incl = lb;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
+        }
+        const uint32_t unit_start = start_bit + (half ? sum_lo : 0u);
+        un.bits = st + bits_off;
+        un.dmax = int(((a.blob_bytes - (soff + bits_off) - 16) / 4) & ~3ull);
+        un.even = st + even_off + uint64_t(jsb) * K3HUF_SUBBLOCK_SYMS + uint64_t(half) * kUnitSyms;
+        un.out = a.out + uint64_t(k) * K3HUF_SUBBLOCK_BYTES + 2ull * half * kUnitSyms;
+        const uint32_t lane_start = unit_start + incl - lb;
+        const uint32_t lane_end = unit_start + incl;
+        const bool full = un.nsyms == uint32_t(kUnitSyms);
+
+        // passes over consecutive lane ranges whose codes fit the buffer
+        // (one pass unless the unit's codes exceed kBufBytes)
+        for (int l0 = 0; l0 < 64;) {
+            const int j0 = first_dword(uniform(__shfl(lane_start, l0, 64)));
+            const bool over = lane >= l0 && (end_dword(lane_end) - j0) * 4 > kBufBytes;
+            const uint64_t m = __ballot(over);
+            const int l1 = m ? int(__builtin_ctzll(m)) : 64;   // > l0: one chunk always fits
+            const int units = (end_dword(uniform(__shfl(lane_end, l1 - 1, 64))) - j0) / 4;
+            fill_buffer(buf, un, j0, units, lane);
+            if (full)
+                decode_lanes(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
+            else
+                decode_lanes_tail(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
+            l0 = l1;
+        }
     }
 }
 

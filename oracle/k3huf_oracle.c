@@ -33,7 +33,7 @@
  * give one code as a prefix of another, so this encoder adds a "repay" pass
  * that shortens codes until the table is exactly full, and the decoder rejects
  * any table whose codes are not prefix-free. The per-subblock index (start bit
- * per 65,536-byte subblock, code bits per 512-symbol lane chunk) is an addition
+ * per 65,536-byte subblock, code bits per 256-symbol lane chunk) is an addition
  * for parallel decoding, counted in the container size.
  *
  * The decoder here ignores the index entirely: it reads the stripe bitstream
@@ -41,13 +41,13 @@
  *
  * Container layout (all little-endian), restated from the format description:
  *   layer header, 304 bytes: magic "K3HF", u16 version 1, u16 maxlen 12,
- *     u32 stripe_bytes 2^26, u32 subblock_bytes 2^16, u32 lane_syms 512,
+ *     u32 stripe_bytes 2^26, u32 subblock_bytes 2^16, u32 lane_syms 256,
  *     u32 n_stripes, u64 raw_bytes, u32 n_subblocks, u32 0, u64 container_bytes,
  *     u8 codelen[256]; then u64 stripe_off[n_stripes]; zero pad to 16.
  *   stripe record at stripe_off[s] (16-aligned): u32 raw_bytes, u32 n_syms,
  *     u32 n_bits, u32 bit_bytes, u32 first_subblock, u32 n_subblocks,
- *     u32 bits_off, u32 even_off; then n_subblocks records of 136 bytes
- *     {u32 start_bit, u32 n_syms, u16 lane_bits[64]}; zero pad to 16; the
+ *     u32 bits_off, u32 even_off; then n_subblocks records of 264 bytes
+ *     {u32 start_bit, u32 n_syms, u16 lane_bits[128]}; zero pad to 16; the
  *     bitstream (bit_bytes = ceil(n_bits/8) rounded up to 16, zero padded) at
  *     bits_off; the even plane (n_syms bytes, zero padded to 16) at even_off.
  *     bits_off and even_off count from the stripe record's first byte.
@@ -60,7 +60,7 @@
 #define OH_STRIPE (1u << 26)
 #define OH_SUBBLOCK (1u << 16)
 #define OH_SB_SYMS (OH_SUBBLOCK / 2)
-#define OH_LANE_SYMS 512u
+#define OH_LANE_SYMS 256u
 #define OH_LANES (OH_SB_SYMS / OH_LANE_SYMS)
 #define OH_HDR 304u
 #define OH_STRIPE_HDR 32u

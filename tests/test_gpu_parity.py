@@ -160,7 +160,7 @@ def test_corrupt_index_and_stripe_are_flagged():
     blob = O.encode_layer(x)
     off = _hdr_field_off(blob, 0)
     b1 = blob.copy()
-    b1[off + 32 + 136 * 1 + 8 + 2 * 5] ^= 1        # lane 5 of subblock 1
+    b1[off + 32 + 264 * 1 + 8 + 2 * 5] ^= 1        # lane 5 of subblock 1
     say("corrupt lane bits")
     got, st = gpu_decode(b1)
     assert st & k3huf.DEV_INDEX

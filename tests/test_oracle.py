@@ -47,9 +47,9 @@ def stripe(blob, s):
 
 
 def sub_rec(blob, st, j):
-    o = st["off"] + 32 + 136 * j
+    o = st["off"] + 32 + 264 * j
     start, n = struct.unpack_from("<II", bytes(blob[o: o + 8]))
-    lanes = np.frombuffer(bytes(blob[o + 8: o + 136]), "<u2")
+    lanes = np.frombuffer(bytes(blob[o + 8: o + 264]), "<u2")
     return start, n, lanes
 
 
@@ -364,7 +364,7 @@ def test_index_checker_detects_tampering():
     x = synth.small_random(5, 3 * 65536)
     blob = O.encode_layer(x).copy()
     st = stripe(blob, 0)
-    o = st["off"] + 32 + 136 * 1 + 8 + 2 * 5      # lane 5 of subblock 1
+    o = st["off"] + 32 + 264 * 1 + 8 + 2 * 5      # lane 5 of subblock 1
     blob[o] ^= 1
     assert O.check_index(blob) == O.E_INDEX
     assert O.decode_layer_rc(blob) == O.OK         # the decoder ignores the index
