@@ -31,21 +31,24 @@
  *     36  u32 reserved = 0              40 u64 container_bytes
  *     48  u8  codelen[256]
  *   304   u64 stripe_off[n_stripes]: byte offset of each stripe record from
- *         the blob start, 16-byte aligned; zero pad to 16.
+ *         the blob start, a multiple of 256; zero pad to 256.
  *   stripe record (at stripe_off[s]):
  *     0 u32 raw_bytes   4 u32 n_syms = raw_bytes / 2   8 u32 n_bits
  *     12 u32 bit_bytes = ceil(n_bits / 8) rounded up to 16
  *     16 u32 first_subblock = s * 1024   20 u32 n_subblocks = ceil(n_syms / 32768)
- *     24 u32 bits_off   28 u32 even_off  (both from the record start, 16-aligned)
+ *     24 u32 bits_off   28 u32 even_off  (both from the record start,
+ *          multiples of 256; decoders require only 16-byte alignment)
  *     32 subblock records, K3HUF_SUBBLOCK_REC_BYTES = 264 each:
  *          u32 start_bit (stripe-relative bit index of the subblock's first code)
  *          u32 n_syms    (32768, or fewer in the stripe's last subblock)
  *          u16 lane_bits[128] (code bits of each 256-symbol lane chunk; 0 if empty)
- *        zero pad to 16
+ *        zero pad to 256
  *     bits_off: the stripe's codes, most-significant bit first (K3 page,
  *        "decode loop": the stream head sits at the top of the bit window),
- *        zero padded to bit_bytes
- *     even_off: the even-offset bytes of the stripe (n_syms), zero padded to 16
+ *        zero padded to bit_bytes, then to a multiple of 256
+ *     even_off: the even-offset bytes of the stripe (n_syms), zero padded to 256
+ *   The 256-byte boundaries keep each plane on whole cache lines, so the
+ *   GPU's line-sized reads of a lane chunk's even bytes touch one line each.
  *   Stripe s covers raw bytes [s * 2^26, min((s + 1) * 2^26, raw_bytes)).
  *   Global subblock k covers raw bytes [k * 2^16, min((k + 1) * 2^16, raw_bytes)).
  */

@@ -65,6 +65,8 @@ static_assert(kLdsBytes <= 163840, "LDS budget");
 constexpr uint32_t kBad = 1u << 29;
 constexpr uint32_t kOne = 1u << 31;
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
 struct DecodeArgs {
     const uint8_t* blob;
     uint64_t blob_bytes;
@@ -212,12 +214,13 @@ __device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t
                                                                  (part & 1) * 8);
                 const uint2 e = ev[rr][q];
                 const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
-                uint4 o;
-                o.x = __builtin_amdgcn_perm(sy.x, e.x, 0x05010400u);
-                o.y = __builtin_amdgcn_perm(sy.x, e.x, 0x07030602u);
-                o.z = __builtin_amdgcn_perm(sy.y, e.y, 0x05010400u);
-                o.w = __builtin_amdgcn_perm(sy.y, e.y, 0x07030602u);
-                *reinterpret_cast<uint4*>(un.out + 2 * u) = o;
+                // the output is written once and not read back here: stream
+                // it past the caches (non-temporal store)
+                const v4u o = {__builtin_amdgcn_perm(sy.x, e.x, 0x05010400u),
+                               __builtin_amdgcn_perm(sy.x, e.x, 0x07030602u),
+                               __builtin_amdgcn_perm(sy.y, e.y, 0x05010400u),
+                               __builtin_amdgcn_perm(sy.y, e.y, 0x07030602u)};
+                __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(un.out + 2 * u));
             }
             wave_sync();
         }
@@ -231,7 +234,7 @@ __device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t
 // The same for the layer's last unit when it holds fewer than 16384 symbols:
 // lane t decodes clamp(nsyms - 256 t, 0, 256) symbols one table step per
 // symbol; kept plain (it runs at most once per layer).
-__device__ __attribute__((noinline)) void decode_lanes_tail(const DecodeArgs& a, const uint32_t* tab,
+__device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uint32_t* tab,
                                                             const uint32_t* buf, uint8_t* stage,
                                                             const Unit& un, int j0,
                                                             uint32_t lane_start, uint32_t lane_bits,

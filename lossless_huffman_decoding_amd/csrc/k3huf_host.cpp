@@ -19,6 +19,8 @@ inline void wr(uint8_t* p, uint64_t v, int n) {
     for (int i = 0; i < n; ++i, v >>= 8) p[i] = uint8_t(v);
 }
 inline uint64_t pad16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
+// planes and stripe records start on 256-byte boundaries (whole cache lines)
+inline uint64_t pad256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 inline uint32_t stripes_for(uint64_t raw) {
     return uint32_t((raw + K3HUF_STRIPE_BYTES - 1) / K3HUF_STRIPE_BYTES);
@@ -214,12 +216,12 @@ int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out) {
 int64_t k3huf_encode_bound(uint64_t raw) {
     if (!raw || (raw & 1)) return K3HUF_E_ARG;
     const uint64_t ns = stripes_for(raw);
-    uint64_t b = pad16(K3HUF_HDR_BYTES + 8 * ns);
+    uint64_t b = pad256(K3HUF_HDR_BYTES + 8 * ns);
     for (uint64_t s = 0; s < ns; ++s) {
         const uint64_t rb = std::min<uint64_t>(K3HUF_STRIPE_BYTES, raw - s * K3HUF_STRIPE_BYTES);
         const uint64_t n = rb / 2, nsb = (n + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
-        b += pad16(K3HUF_STRIPE_HDR_BYTES + K3HUF_SUBBLOCK_REC_BYTES * nsb) +
-             pad16((n * K3HUF_MAXLEN + 7) / 8) + pad16(n);
+        b += pad256(K3HUF_STRIPE_HDR_BYTES + K3HUF_SUBBLOCK_REC_BYTES * nsb) +
+             pad256(pad16((n * K3HUF_MAXLEN + 7) / 8)) + pad256(n);
     }
     return int64_t(b);
 }
@@ -262,22 +264,22 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
     canonical_codes(len, code);
 
     // layout: every stripe's size is known from its histogram
-    uint64_t o = pad16(K3HUF_HDR_BYTES + 8ull * ns);
+    uint64_t o = pad256(K3HUF_HDR_BYTES + 8ull * ns);
     uint32_t nsb_total = 0;
     for (uint32_t s = 0; s < ns; ++s) {
         uint64_t nbits = 0;
         for (int v = 0; v < 256; ++v) nbits += hist[size_t(s) * 256 + v] * len[v];
         g[s].nbits = uint32_t(nbits);
         g[s].bit_bytes = uint32_t(pad16((nbits + 7) / 8));
-        g[s].bits_off = uint32_t(pad16(K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * g[s].nsb));
-        g[s].even_off = g[s].bits_off + g[s].bit_bytes;
+        g[s].bits_off = uint32_t(pad256(K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * g[s].nsb));
+        g[s].even_off = uint32_t(pad256(uint64_t(g[s].bits_off) + g[s].bit_bytes));
         g[s].off = o;
-        o += pad16(uint64_t(g[s].even_off) + g[s].n);
+        o += pad256(uint64_t(g[s].even_off) + g[s].n);
         nsb_total += g[s].nsb;
     }
     const uint64_t total = o;
 
-    std::memset(out, 0, pad16(K3HUF_HDR_BYTES + 8ull * ns));
+    std::memset(out, 0, pad256(K3HUF_HDR_BYTES + 8ull * ns));
     std::memcpy(out, "K3HF", 4);
     wr(out + 4, 1, 2);
     wr(out + 6, K3HUF_MAXLEN, 2);
@@ -296,7 +298,7 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
     parallel_for(int(ns), threads, [&](int s) {
         const StripeGeom& G = g[s];
         uint8_t* st = out + G.off;
-        const uint64_t span = pad16(uint64_t(G.even_off) + G.n);
+        const uint64_t span = pad256(uint64_t(G.even_off) + G.n);
         std::memset(st, 0, span);
         wr(st + 0, G.raw, 4);
         wr(st + 4, G.n, 4);

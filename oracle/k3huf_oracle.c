@@ -43,14 +43,17 @@
  *   layer header, 304 bytes: magic "K3HF", u16 version 1, u16 maxlen 12,
  *     u32 stripe_bytes 2^26, u32 subblock_bytes 2^16, u32 lane_syms 256,
  *     u32 n_stripes, u64 raw_bytes, u32 n_subblocks, u32 0, u64 container_bytes,
- *     u8 codelen[256]; then u64 stripe_off[n_stripes]; zero pad to 16.
- *   stripe record at stripe_off[s] (16-aligned): u32 raw_bytes, u32 n_syms,
+ *     u8 codelen[256]; then u64 stripe_off[n_stripes]; zero pad to 256.
+ *   stripe record at stripe_off[s] (256-aligned): u32 raw_bytes, u32 n_syms,
  *     u32 n_bits, u32 bit_bytes, u32 first_subblock, u32 n_subblocks,
  *     u32 bits_off, u32 even_off; then n_subblocks records of 264 bytes
- *     {u32 start_bit, u32 n_syms, u16 lane_bits[128]}; zero pad to 16; the
+ *     {u32 start_bit, u32 n_syms, u16 lane_bits[128]}; zero pad to 256; the
  *     bitstream (bit_bytes = ceil(n_bits/8) rounded up to 16, zero padded) at
- *     bits_off; the even plane (n_syms bytes, zero padded to 16) at even_off.
- *     bits_off and even_off count from the stripe record's first byte.
+ *     bits_off; zero pad to 256; the even plane (n_syms bytes, zero padded to
+ *     256) at even_off. bits_off and even_off count from the stripe record's
+ *     first byte and are multiples of 256. (Decoders need only 16-byte
+ *     alignment; the 256-byte padding keeps the planes on cache-line
+ *     boundaries.)
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -87,6 +90,7 @@ static void wr_le(uint8_t *p, uint64_t v, int n) {
     for (int i = 0; i < n; i++) { p[i] = (uint8_t)(v & 0xff); v >>= 8; }
 }
 static uint64_t up16(uint64_t x) { return (x + 15) & ~(uint64_t)15; }
+static uint64_t up256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
 
 /* ---------------------------------------------------------------------------
  * Code lengths (K3 page, "canonical code assignment and Kraft check": lengths
@@ -294,12 +298,12 @@ static uint32_t n_stripes_of(uint64_t raw) { return (uint32_t)((raw + OH_STRIPE 
  * every code 12 bits long). */
 int64_t oh_encode_bound(uint64_t raw) {
     uint64_t ns = n_stripes_of(raw);
-    uint64_t b = up16(OH_HDR + 8 * ns);
+    uint64_t b = up256(OH_HDR + 8 * ns);
     for (uint64_t s = 0; s < ns; s++) {
         uint64_t rb = raw - s * OH_STRIPE;
         if (rb > OH_STRIPE) rb = OH_STRIPE;
         uint64_t n = rb / 2, nsb = (n + OH_SB_SYMS - 1) / OH_SB_SYMS;
-        b += up16(OH_STRIPE_HDR + OH_REC * nsb) + up16((n * OH_MAXLEN + 7) / 8) + up16(n);
+        b += up256(OH_STRIPE_HDR + OH_REC * nsb) + up256(up16((n * OH_MAXLEN + 7) / 8)) + up256(n);
     }
     return (int64_t)b;
 }
@@ -328,7 +332,7 @@ int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64
 
     uint32_t ns = n_stripes_of(n_raw);
     memset(out, 0, cap);
-    uint64_t o = up16(OH_HDR + 8ull * ns);
+    uint64_t o = up256(OH_HDR + 8ull * ns);
     uint32_t sb_total = 0;
     for (uint32_t s = 0; s < ns; s++) {
         uint64_t base = (uint64_t)s * OH_STRIPE;
@@ -338,7 +342,7 @@ int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64
         uint32_t nsb = (n + OH_SB_SYMS - 1) / OH_SB_SYMS;
         uint8_t *st = out + o;
         wr_le(out + OH_HDR + 8ull * s, o, 8);
-        uint64_t bits_off = up16(OH_STRIPE_HDR + (uint64_t)OH_REC * nsb);
+        uint64_t bits_off = up256(OH_STRIPE_HDR + (uint64_t)OH_REC * nsb);
         uint8_t *bits = st + bits_off;
         uint64_t pos = 0;
         uint64_t lane_start = 0;
@@ -366,7 +370,7 @@ int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64
             wr_le(rec + 8 + 2 * (pl % OH_LANES), pos - lane_start, 2);
         }
         uint64_t bit_bytes = up16((pos + 7) / 8);
-        uint64_t even_off = bits_off + bit_bytes;
+        uint64_t even_off = up256(bits_off + bit_bytes);
         for (uint32_t i = 0; i < n; i++) st[even_off + i] = raw[base + 2ull * i];
         wr_le(st + 0, rb, 4);
         wr_le(st + 4, n, 4);
@@ -377,7 +381,7 @@ int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64
         wr_le(st + 24, bits_off, 4);
         wr_le(st + 28, even_off, 4);
         sb_total += nsb;
-        o += up16(even_off + n);
+        o += up256(even_off + n);
     }
     memcpy(out, "K3HF", 4);
     wr_le(out + 4, 1, 2);
