@@ -16,6 +16,7 @@
 // stores of a wave cover whole 128-byte lines.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -67,6 +68,22 @@ constexpr uint32_t kOne = 1u << 31;
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
+// Work distribution. With T waves in the grid and n units, wave w first
+// decodes units w, w + T, ... for R = floor(n / T) rounds. The n - R T
+// leftover units are handed out on demand, so the waves that finished their
+// R units first take them and the grid ends close together: leftover unit
+// R T + x + G i goes to whichever wave of workgroup group x (block mod G,
+// G = min(8, blocks): one group per XCD) takes ticket i from group x's
+// counter. With R = 0 every wave has at most one unit. Launches in
+// flight use different counter slots (the host cycles through kSchedSlots);
+// the last workgroup of a launch clears its slot. The counters live in this
+// array, which exists once per device for the life of the process; at most
+// kSchedSlots decodes may run at the same time on a device.
+constexpr uint32_t kSchedSlots = 256;
+constexpr uint32_t kGroupsPerSlot = 8;
+constexpr uint32_t kSlotWords = kGroupsPerSlot + 1;   // tickets per group, workgroups done
+__device__ uint32_t g_sched[kSlotWords * kSchedSlots];
+
 struct DecodeArgs {
     const uint8_t* blob;
     uint64_t blob_bytes;
@@ -76,6 +93,7 @@ struct DecodeArgs {
     uint32_t n_sub;
     uint32_t n_stripes;
     uint32_t* status;
+    uint32_t slot;        // work-counter slot of this launch
 };
 
 __device__ __forceinline__ uint32_t ld32(const uint8_t* p) {
@@ -347,8 +365,20 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     uint32_t* buf = reinterpret_cast<uint32_t*>(wl);
     uint8_t* stage = wl + kBufBytes;
     const uint32_t n_units = a.n_sub * kUnitsPerSub;
+    const uint32_t T = gridDim.x * kWaves;
+    const uint32_t rounds = n_units / T;
+    const uint32_t groups = min(kGroupsPerSlot, gridDim.x);
+    const uint32_t group = blockIdx.x % groups;
+    uint32_t* slot = &g_sched[kSlotWords * a.slot];
+    uint32_t round = 0;
 
-    for (uint32_t h = blockIdx.x * kWaves + wave; h < n_units; h += gridDim.x * kWaves) {
+    for (uint32_t h = blockIdx.x * kWaves + wave; h < n_units;) {
+        // on the last static round, ask for a leftover unit now; the answer
+        // is needed only when this unit is done
+        const bool ask = rounds > 0 && round + 1 >= rounds;
+        uint32_t ticket = 0;
+        if (ask && lane == 0) ticket = atomicAdd(&slot[group], 1u);
+        do {
         const uint32_t k = h / kUnitsPerSub, half = h % kUnitsPerSub;
         const uint32_t s = k / kSubPerStripe, jsb = k % kSubPerStripe;
         const uint64_t soff = ld64(b + K3HUF_HDR_BYTES + 8ull * s);
@@ -426,6 +456,22 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
                 decode_lanes_tail(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
             l0 = l1;
         }
+        } while (false);   // the checks above leave a bad unit with `continue`
+        ++round;
+        if (round < rounds)
+            h += T;
+        else if (ask)
+            h = rounds * T + group + groups * __builtin_amdgcn_readlane(ticket, 0);
+        else
+            h = n_units;
+    }
+
+    // the last workgroup to finish clears this launch's counter slot
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t done = atomicAdd(&slot[kGroupsPerSlot], 1u);
+        if (done == gridDim.x - 1)
+            for (uint32_t g = 0; g <= kGroupsPerSlot; ++g) atomicExch(&slot[g], 0u);
     }
 }
 
@@ -436,6 +482,7 @@ struct DevInfo {
 
 std::mutex g_mu;
 std::vector<DevInfo> g_dev;
+std::atomic<uint32_t> g_launches{0};
 
 int device_info(DevInfo* out) {
     int dev = 0;
@@ -483,7 +530,8 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     a.n_sub = uint32_t(n_sub);
     a.n_stripes = uint32_t(n_stripes);
     a.status = d_status;
-    const uint64_t want = (n_sub + kWaves - 1) / kWaves;
+    a.slot = g_launches.fetch_add(1, std::memory_order_relaxed) % kSchedSlots;
+    const uint64_t want = (n_sub * kUnitsPerSub + kWaves - 1) / kWaves;
     const uint64_t resident = uint64_t(di.cus) * uint64_t(di.wg_per_cu);
     const unsigned grid = unsigned(want < resident ? want : resident);
     hipLaunchKernelGGL(k3huf_decode_kernel, dim3(grid), dim3(kThreads), 0,
