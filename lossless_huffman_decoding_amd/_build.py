@@ -17,9 +17,13 @@ LIB = os.path.join(OUT_DIR, "libk3huf.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# packed fp32 instructions stay off for all device code
+# packed fp32 instructions stay off for all device code. The atomic
+# optimizer is off so that the decode kernel's work-ticket atomic (one lane,
+# answer needed a whole work unit later) is not turned into a wave-wide
+# reduction that waits for the answer at once.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
              "-I" + os.path.join(ROOT, "include")]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-pthread",
               "-I" + os.path.join(ROOT, "include")]

@@ -115,10 +115,26 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
 }
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    return v;
+// Inclusive prefix sum over the 64 lanes with DPP row moves: a scan within
+// each 16-lane row (shifts 1, 2, 4, 8, zero fill), then the last lane of
+// row 0 added into row 1 and of row 2 into row 3, then lane 31 into rows 2-3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);    // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);    // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);    // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);    // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return x;
+}
+// s_waitcnt vmcnt(0), the other counters left alone. Placed where the
+// counter is about to be drained anyway, it tells the compiler's wait
+// analysis that nothing is outstanding there; without it, merging paths
+// (the multi-pass decode, a record loaded without prefetch) makes the
+// compiler wait for every outstanding store at later loop heads.
+__device__ __forceinline__ void drain_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) {
+    return __builtin_amdgcn_readlane(v, l);
 }
 
 // Table entry for 12-bit index i from the (symbol << 4 | length) table.
@@ -177,12 +193,17 @@ struct Unit {
 };
 
 // Decode lanes [l0, l1) of a full unit (64 chunks of 256 symbols) whose
-// bitstream dwords [j0, ...) the caller has placed in `buf`.
+// bitstream dwords [j0, ...) the caller has placed in `buf`. kAll: the pass
+// covers all 64 lanes (l0 = 0, l1 = 64), the common case; its loads and
+// stores then carry no per-chunk condition, so no store waits for the ones
+// before it to complete (vmcnt counts stores too, and a store behind a
+// branch makes the compiler wait for everything outstanding).
+template <bool kAll>
 __device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t* tab,
                                              const uint32_t* buf, uint8_t* stage, const Unit& un,
                                              int j0, uint32_t lane_start, uint32_t lane_bits,
                                              int l0, int l1, int lane) {
-    const bool mine = lane >= l0 && lane < l1;
+    const bool mine = kAll || (lane >= l0 && lane < l1);
     // buffer bit index of the lane's first code, minus one (>= 0: the buffer
     // starts at least one dword before it)
     uint32_t pm1 = lane_start - 32u * uint32_t(j0) - 1u;
@@ -191,6 +212,7 @@ __device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t
     const int sub_line = lane >> 3, part = lane & 7;
     uint2 ev[kRounds][kSuper];
 
+#pragma unroll 1
     for (int sp = 0; sp < kPhases; sp += kSuper) {
         // the next two phases' even-plane bytes: a whole line per chunk
 #pragma unroll
@@ -199,7 +221,8 @@ __device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t
 #pragma unroll
             for (int f = 0; f < kSuper; ++f) {
                 const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t((sp + f) * kPhase + part * 8);
-                if (c >= l0 && c < l1) ev[rr][f] = *reinterpret_cast<const uint2*>(un.even + u);
+                // in bounds for every chunk of a full unit, so not conditional
+                ev[rr][f] = *reinterpret_cast<const uint2*>(un.even + u);
             }
         }
 #pragma unroll
@@ -227,7 +250,7 @@ __device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t
 #pragma unroll
             for (int rr = 0; rr < kRounds; ++rr) {
                 const int c = rr * 8 + sub_line;
-                if (c < l0 || c >= l1) continue;
+                if (!kAll && (c < l0 || c >= l1)) continue;
                 const uint2 sy = *reinterpret_cast<const uint2*>(stage + stage_off(c, part >> 1) +
                                                                  (part & 1) * 8);
                 const uint2 e = ev[rr][q];
@@ -313,23 +336,23 @@ __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uin
 }
 
 // Copy bitstream dwords [j0, j0 + 4 * units) into `buf`, byte-swapped so
-// that bit 31 of each dword is the earliest stream bit.
+// that bit 31 of each dword is the earliest stream bit. Every slot of the
+// buffer is written: slots past `units` repeat the last 16-byte unit (the
+// same address, so no extra line is fetched). Keeping the loads and stores
+// unconditional lets the compiler count outstanding loads exactly instead of
+// waiting for all memory operations at later register reuse.
 __device__ __forceinline__ void fill_buffer(uint32_t* buf, const Unit& un, int j0, int units, int lane) {
     constexpr int kPer = kBufUnits / 64;
     uint4 v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const int u = lane + 64 * i;
-        if (u < units)
-            v[i] = *reinterpret_cast<const uint4*>(un.bits + 4 * min(j0 + 4 * u, un.dmax));
+        const int u = min(lane + 64 * i, units - 1);
+        v[i] = *reinterpret_cast<const uint4*>(un.bits + 4 * min(j0 + 4 * u, un.dmax));
     }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int u = lane + 64 * i;
-        if (u < units)
-            *reinterpret_cast<uint4*>(buf + 4 * u) =
-                make_uint4(bswap32(v[i].x), bswap32(v[i].y), bswap32(v[i].z), bswap32(v[i].w));
-    }
+    for (int i = 0; i < kPer; ++i)
+        *reinterpret_cast<uint4*>(buf + 4 * (lane + 64 * i)) =
+            make_uint4(bswap32(v[i].x), bswap32(v[i].y), bswap32(v[i].z), bswap32(v[i].w));
     wave_sync();
 }
 
@@ -339,6 +362,72 @@ __device__ __forceinline__ int first_dword(uint32_t p) { return ((int(p) - 1) >>
 // end (exclusive, 16-byte aligned) of the dwords windows may read for codes
 // ending at stripe bit p
 __device__ __forceinline__ int end_dword(uint32_t p) { return (((int(p) - 1) >> 5) + 3 + 3) & ~3; }
+
+// Stripe values of the 64 stripes 64 blk .. 64 blk + 63, lane l holding stripe
+// 64 blk + l: the record offset in 16-byte units, both plane offsets and the
+// bit count, or n_bits = kNoStripe where the stripe does not exist or its
+// record fails the checks (bounds, geometry, n_bits <= 12 n_syms, which keeps
+// valid counts below kNoStripe). Offsets below 2^36 fit the 16-byte unit
+// count; the launcher rejects larger blobs.
+constexpr uint32_t kNoStripe = 0xFFFFFFFFu;
+struct StripeLane {
+    uint32_t off16, bits_off, even_off, n_bits;
+};
+
+__device__ __forceinline__ uint64_t stripe_raw(const DecodeArgs& a, uint32_t s) {
+    return min(uint64_t(K3HUF_STRIPE_BYTES), a.out_bytes - uint64_t(s) * K3HUF_STRIPE_BYTES);
+}
+__device__ __forceinline__ uint32_t stripe_subblocks(uint32_t n_syms) {
+    return (n_syms + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
+}
+
+__device__ __forceinline__ StripeLane load_stripes(const DecodeArgs& a, uint32_t blk, int lane) {
+    StripeLane t = {0u, 0u, 0u, kNoStripe};
+    const uint32_t s = blk * 64u + uint32_t(lane);
+    if (s < a.n_stripes) {
+        const uint64_t soff = ld64(a.blob + K3HUF_HDR_BYTES + 8ull * s);
+        const uint64_t raw_s = stripe_raw(a, s);
+        const uint32_t n = uint32_t(raw_s / 2);
+        const uint32_t nsb = stripe_subblocks(n);
+        if ((soff & 15) == 0 && soff + K3HUF_STRIPE_HDR_BYTES <= a.blob_bytes) {
+            const uint4 r0 = *reinterpret_cast<const uint4*>(a.blob + soff);
+            const uint4 r1 = *reinterpret_cast<const uint4*>(a.blob + soff + 16);
+            const uint32_t n_bits = r0.z, bit_bytes = r0.w, bits_off = r1.z, even_off = r1.w;
+            const bool ok = r0.x == uint32_t(raw_s) && r0.y == n && r1.x == s * kSubPerStripe &&
+                            r1.y == nsb && (bits_off & 15) == 0 && (even_off & 15) == 0 &&
+                            bits_off >= K3HUF_STRIPE_HDR_BYTES + K3HUF_SUBBLOCK_REC_BYTES * nsb &&
+                            uint64_t(n_bits) <= 8ull * bit_bytes &&
+                            uint64_t(n_bits) <= uint64_t(K3HUF_MAXLEN) * n &&
+                            uint64_t(even_off) >= uint64_t(bits_off) + bit_bytes &&
+                            soff + even_off + ((uint64_t(n) + 15) & ~15ull) <= a.blob_bytes;
+            if (ok) {
+                t.off16 = uint32_t(soff >> 4);
+                t.bits_off = bits_off;
+                t.even_off = even_off;
+                t.n_bits = n_bits;
+            }
+        }
+    }
+    return t;
+}
+
+// A subblock record as vector registers: lanes 0 and 1 hold start_bit and
+// n_syms, lane 2 the next record's start_bit (when the stripe has one), and
+// lane t holds lane bit counts t and 64 + t. Vector loads, so the record of
+// the next unit can be requested a whole unit before it is used.
+struct RecLanes {
+    uint32_t hd, lo, hi;
+};
+
+__device__ __forceinline__ RecLanes load_rec(const uint8_t* rec, bool has_next, int lane) {
+    const uint32_t off = lane == 2 ? (has_next ? K3HUF_SUBBLOCK_REC_BYTES : 0u) : 4u * uint32_t(lane & 1);
+    const uint16_t* lbits = reinterpret_cast<const uint16_t*>(rec + 8);
+    RecLanes r;
+    r.hd = ld32(rec + off);
+    r.lo = lbits[lane];
+    r.hi = lbits[kUnitLanes + lane];
+    return r;
+}
 
 __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
@@ -356,67 +445,89 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         return;
     }
 
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+    const uint32_t n_units = a.n_sub * kUnitsPerSub;
+    const uint32_t T = gridDim.x * kWaves;
+    uint32_t h = blockIdx.x * kWaves + wave;
+    // stripe values of the block holding this wave's first unit, requested
+    // before the table build so that their latency overlaps it
+    uint32_t blk = h < n_units ? h / (kUnitsPerSub * kSubPerStripe * 64u) : 0u;
+    StripeLane sl = load_stripes(a, blk, lane);
+
     for (int i = threadIdx.x; i < K3HUF_LUT_ENTRIES; i += kThreads) tab[i] = make_entry(a.lut, i);
     __syncthreads();
 
-    const int lane = threadIdx.x & 63;
-    const uint32_t wave = uniform(threadIdx.x >> 6);
     uint8_t* wl = lds + kTabBytes + wave * kWaveLds;
     uint32_t* buf = reinterpret_cast<uint32_t*>(wl);
     uint8_t* stage = wl + kBufBytes;
-    const uint32_t n_units = a.n_sub * kUnitsPerSub;
-    const uint32_t T = gridDim.x * kWaves;
     const uint32_t rounds = n_units / T;
     const uint32_t groups = min(kGroupsPerSlot, gridDim.x);
     const uint32_t group = blockIdx.x % groups;
     uint32_t* slot = &g_sched[kSlotWords * a.slot];
     uint32_t round = 0;
+    uint32_t pf_h = 0xFFFFFFFFu;   // unit whose record `pf` holds
+    RecLanes pf = {0u, 0u, 0u};
 
-    for (uint32_t h = blockIdx.x * kWaves + wave; h < n_units;) {
+    while (h < n_units) {
         // on the last static round, ask for a leftover unit now; the answer
         // is needed only when this unit is done
         const bool ask = rounds > 0 && round + 1 >= rounds;
         uint32_t ticket = 0;
         if (ask && lane == 0) ticket = atomicAdd(&slot[group], 1u);
-        do {
         const uint32_t k = h / kUnitsPerSub, half = h % kUnitsPerSub;
         const uint32_t s = k / kSubPerStripe, jsb = k % kSubPerStripe;
-        const uint64_t soff = ld64(b + K3HUF_HDR_BYTES + 8ull * s);
-        const uint64_t raw_s = min(uint64_t(K3HUF_STRIPE_BYTES), a.out_bytes - uint64_t(s) * K3HUF_STRIPE_BYTES);
-        const uint32_t n = uint32_t(raw_s / 2);
-        const uint32_t nsb = (n + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
-        bool ok = (soff & 15) == 0 && soff + K3HUF_STRIPE_HDR_BYTES <= a.blob_bytes;
-        const uint8_t* st = b + soff;
-        uint32_t n_bits = 0, bit_bytes = 0, bits_off = 0, even_off = 0;
-        if (ok) {
-            n_bits = ld32(st + 8);
-            bit_bytes = ld32(st + 12);
-            bits_off = ld32(st + 24);
-            even_off = ld32(st + 28);
-            ok = ld32(st) == uint32_t(raw_s) && ld32(st + 4) == n && ld32(st + 16) == s * kSubPerStripe &&
-                 ld32(st + 20) == nsb && (bits_off & 15) == 0 && (even_off & 15) == 0 &&
-                 bits_off >= K3HUF_STRIPE_HDR_BYTES + K3HUF_SUBBLOCK_REC_BYTES * nsb &&
-                 uint64_t(n_bits) <= 8ull * bit_bytes &&
-                 uint64_t(even_off) >= uint64_t(bits_off) + bit_bytes &&
-                 soff + even_off + ((uint64_t(n) + 15) & ~15ull) <= a.blob_bytes;
+        if ((s >> 6) != blk) {
+            blk = s >> 6;
+            sl = load_stripes(a, blk, lane);
         }
-        if (!ok) {
+        const uint32_t n_bits = lane_value(sl.n_bits, s & 63u);
+        const uint64_t soff = uint64_t(lane_value(sl.off16, s & 63u)) << 4;
+        const uint32_t bits_off = lane_value(sl.bits_off, s & 63u);
+        const uint32_t even_off = lane_value(sl.even_off, s & 63u);
+        const uint32_t n = uint32_t(stripe_raw(a, s) / 2);
+        const uint32_t nsb = stripe_subblocks(n);
+        const uint8_t* st = b + soff;
+        if (pf_h != h && n_bits != kNoStripe) {
+            pf = load_rec(st + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jsb,
+                          jsb + 1 < nsb, lane);
+            drain_vm();
+        }
+        // everything this unit needs from its record, read before the
+        // registers are refilled with the next unit's record
+        const uint32_t start_bit = lane_value(pf.hd, 0);
+        const uint32_t rec_syms = lane_value(pf.hd, 1);
+        const uint32_t next_start = jsb + 1 < nsb ? lane_value(pf.hd, 2) : n_bits;
+        const uint32_t lb = half ? pf.hi : pf.lo;
+        const uint32_t incl = wave_incl_scan(lb);   // prefix within this unit
+        const uint32_t unit_bits = lane_value(incl, 63);
+        const uint32_t other_bits = lane_value(wave_incl_scan(half ? pf.lo : pf.hi), 63);
+        // request the record of this wave's next static unit
+        pf_h = 0xFFFFFFFFu;
+        if (round + 1 < rounds) {
+            const uint32_t hn = h + T, kn = hn / kUnitsPerSub;
+            const uint32_t sn = kn / kSubPerStripe, jn = kn % kSubPerStripe;
+            if ((sn >> 6) == blk && lane_value(sl.n_bits, sn & 63u) != kNoStripe) {
+                const uint8_t* stn = b + (uint64_t(lane_value(sl.off16, sn & 63u)) << 4);
+                pf = load_rec(stn + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jn,
+                              jn + 1 < stripe_subblocks(uint32_t(stripe_raw(a, sn) / 2)), lane);
+                pf_h = hn;
+            }
+        }
+        do {
+        if (n_bits == kNoStripe) {
             if (lane == 0 && half == 0) flag(a.status, K3HUF_DEV_STRIPE);
             continue;
         }
-        const uint8_t* rec = st + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jsb;
-        const uint32_t start_bit = ld32(rec);
         const uint32_t nsyms = min(uint32_t(K3HUF_SUBBLOCK_SYMS), n - jsb * K3HUF_SUBBLOCK_SYMS);
-        const uint32_t next_start = jsb + 1 < nsb ? ld32(rec + K3HUF_SUBBLOCK_REC_BYTES) : n_bits;
-        const uint16_t* lbits = reinterpret_cast<const uint16_t*>(rec + 8);
-        const uint32_t lb_lo = lbits[lane], lb_hi = lbits[kUnitLanes + lane];
-        const uint32_t sum_lo = uniform(wave_sum(lb_lo));
-        const uint32_t total = sum_lo + uniform(wave_sum(lb_hi));
-        const uint32_t lb = half ? lb_hi : lb_lo;
+        const uint32_t total = unit_bits + other_bits;
         const int gl = int(half) * kUnitLanes + lane;    // lane chunk within the subblock
         const int cnt = min(max(int(nsyms) - gl * int(K3HUF_LANE_SYMS), 0), int(K3HUF_LANE_SYMS));
-        const bool lane_ok = lb >= uint32_t(cnt) && lb <= uint32_t(cnt) * K3HUF_MAXLEN;
-        const bool sb_ok = ld32(rec + 4) == nsyms && start_bit <= n_bits &&
+        // the prefix must also be monotone and end at the unit's sum, which
+        // keeps every lane's bit range inside the unit's codes
+        const bool lane_ok = lb >= uint32_t(cnt) && lb <= uint32_t(cnt) * K3HUF_MAXLEN &&
+                             incl >= lb && incl <= unit_bits;
+        const bool sb_ok = rec_syms == nsyms && start_bit <= n_bits &&
                            uint64_t(start_bit) + total == next_start && next_start <= n_bits;
         if (!sb_ok || __any(!lane_ok)) {
             if (lane == 0) flag(a.status, K3HUF_DEV_INDEX);
@@ -425,14 +536,7 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         Unit un;
         un.nsyms = uint32_t(min(max(int(nsyms) - int(half) * kUnitSyms, 0), kUnitSyms));
         if (un.nsyms == 0) continue;
-        // inclusive prefix sum of this unit's lane chunk bit counts
-        uint32_t incl = lb;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t v = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += v;
-        }
-        const uint32_t unit_start = start_bit + (half ? sum_lo : 0u);
+        const uint32_t unit_start = start_bit + (half ? other_bits : 0u);
         un.bits = st + bits_off;
         un.dmax = int(((a.blob_bytes - (soff + bits_off) - 16) / 4) & ~3ull);
         un.even = st + even_off + uint64_t(jsb) * K3HUF_SUBBLOCK_SYMS + uint64_t(half) * kUnitSyms;
@@ -441,17 +545,20 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         const uint32_t lane_end = unit_start + incl;
         const bool full = un.nsyms == uint32_t(kUnitSyms);
 
-        // passes over consecutive lane ranges whose codes fit the buffer
+    // passes over consecutive lane ranges whose codes fit the buffer
         // (one pass unless the unit's codes exceed kBufBytes)
         for (int l0 = 0; l0 < 64;) {
-            const int j0 = first_dword(uniform(__shfl(lane_start, l0, 64)));
+            const int j0 = first_dword(lane_value(lane_start, l0));
             const bool over = lane >= l0 && (end_dword(lane_end) - j0) * 4 > kBufBytes;
             const uint64_t m = __ballot(over);
             const int l1 = m ? int(__builtin_ctzll(m)) : 64;   // > l0: one chunk always fits
-            const int units = (end_dword(uniform(__shfl(lane_end, l1 - 1, 64))) - j0) / 4;
+            const int units = (end_dword(lane_value(lane_end, l1 - 1)) - j0) / 4;
             fill_buffer(buf, un, j0, units, lane);
-            if (full)
-                decode_lanes(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
+            if (full && l0 == 0 && l1 == 64) {
+                drain_vm();   // fill_buffer has just drained it
+                decode_lanes<true>(a, tab, buf, stage, un, j0, lane_start, lb, 0, 64, lane);
+            } else if (full)
+                decode_lanes<false>(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
             else
                 decode_lanes_tail(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
             l0 = l1;
@@ -517,7 +624,9 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     if (blob_bytes < K3HUF_HDR_BYTES + 8 || out_bytes == 0 || (out_bytes & 1)) return K3HUF_E_ARG;
     const uint64_t n_sub = (uint64_t(out_bytes) + K3HUF_SUBBLOCK_BYTES - 1) / K3HUF_SUBBLOCK_BYTES;
     const uint64_t n_stripes = (uint64_t(out_bytes) + K3HUF_STRIPE_BYTES - 1) / K3HUF_STRIPE_BYTES;
-    if (n_sub > 0xFFFFFFFFull || blob_bytes < K3HUF_HDR_BYTES + 8 * n_stripes) return K3HUF_E_ARG;
+    if (n_sub > 0xFFFFFFFFull || blob_bytes < K3HUF_HDR_BYTES + 8 * n_stripes ||
+        uint64_t(blob_bytes) >= (1ull << 36))
+        return K3HUF_E_ARG;
     DevInfo di;
     int rc = device_info(&di);
     if (rc) return rc;
