@@ -138,7 +138,8 @@ int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out);
  *   or a lane whose codes end off its index; the caller clears it beforehand
  *   and reads it after the stream synchronizes. Subblocks with bad records
  *   are left unwritten; no read ever leaves [d_blob, d_blob + blob_bytes).
- * Returns K3HUF_OK once queued, K3HUF_E_ARG for bad sizes or alignment,
+ * Returns K3HUF_OK once queued, K3HUF_E_ARG for bad sizes or alignment (also
+ * for blob_bytes >= 2^36: the kernel keeps stripe offsets in 16-byte units),
  * K3HUF_E_HIP if the launch fails. Decoding follows the K3 page's "decode
  * loop" (MSB-first bit window, one table lookup per symbol) and "key design
  * points" (even plane interleaved back at even offsets).

@@ -69,16 +69,19 @@ constexpr uint32_t kOne = 1u << 31;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // Work distribution. With T waves in the grid and n units, wave w first
-// decodes units w, w + T, ... for R = floor(n / T) rounds. The n - R T
-// leftover units are handed out on demand, so the waves that finished their
-// R units first take them and the grid ends close together: leftover unit
-// R T + x + G i goes to whichever wave of workgroup group x (block mod G,
-// G = min(8, blocks): one group per XCD) takes ticket i from group x's
-// counter. With R = 0 every wave has at most one unit. Launches in
-// flight use different counter slots (the host cycles through kSchedSlots);
-// the last workgroup of a launch clears its slot. The counters live in this
-// array, which exists once per device for the life of the process; at most
-// kSchedSlots decodes may run at the same time on a device.
+// decodes units w, w + T, ... for S = max(floor(n / T) - kDynRounds, 0)
+// static rounds. The n - S T remaining units are handed out on demand:
+// unit S T + x + G i goes to whichever wave of workgroup group x (block mod
+// G, G = min(8, blocks): one group per XCD) takes ticket i from group x's
+// counter. A wave asks for its next unit when it starts the current one and
+// reads the answer halfway through it, so it holds at most one unit ahead;
+// waves that run faster take more units and the grid ends close together.
+// Launches in flight use different counter slots (the host cycles through
+// kSchedSlots); the last workgroup of a launch clears its slot. The
+// counters live in this array, which exists once per device for the life of
+// the process; at most kSchedSlots decodes may run at the same time on a
+// device.
+constexpr uint32_t kDynRounds = 3;
 constexpr uint32_t kSchedSlots = 256;
 constexpr uint32_t kGroupsPerSlot = 8;
 constexpr uint32_t kSlotWords = kGroupsPerSlot + 1;   // tickets per group, workgroups done
@@ -192,81 +195,94 @@ struct Unit {
     uint32_t nsyms;        // symbols in this unit (16384 unless last in stripe)
 };
 
-// Decode lanes [l0, l1) of a full unit (64 chunks of 256 symbols) whose
-// bitstream dwords [j0, ...) the caller has placed in `buf`. kAll: the pass
-// covers all 64 lanes (l0 = 0, l1 = 64), the common case; its loads and
-// stores then carry no per-chunk condition, so no store waits for the ones
-// before it to complete (vmcnt counts stores too, and a store behind a
-// branch makes the compiler wait for everything outstanding).
+// One super-phase (phases sp and sp + 1) of lanes [l0, l1) of a full unit
+// (64 chunks of 256 symbols) whose bitstream dwords [j0, ...) the caller has
+// placed in `buf`. kAll: the pass covers all 64 lanes (l0 = 0, l1 = 64), the
+// common case; its loads and stores then carry no per-chunk condition, so no
+// store waits for the ones before it to complete (vmcnt counts stores too,
+// and a store behind a branch makes the compiler wait for everything
+// outstanding).
 template <bool kAll>
+__device__ __forceinline__ void decode_super(const uint32_t* tab, const uint32_t* buf,
+                                             uint8_t* stage, const Unit& un, int sp, int l0, int l1,
+                                             int lane, uint32_t& pm1, uint32_t& bad) {
+    const bool mine = kAll || (lane >= l0 && lane < l1);
+    const int sub_line = lane >> 3, part = lane & 7;
+    uint2 ev[kRounds][kSuper];
+    // the two phases' even-plane bytes: a whole line per chunk
+#pragma unroll
+    for (int rr = 0; rr < kRounds; ++rr) {
+        const int c = rr * 8 + sub_line;
+#pragma unroll
+        for (int f = 0; f < kSuper; ++f) {
+            const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t((sp + f) * kPhase + part * 8);
+            // in bounds for every chunk of a full unit, so not conditional
+            ev[rr][f] = *reinterpret_cast<const uint2*>(un.even + u);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kSuper; ++q) {
+        const int ph = sp + q;
+        if (mine) {
+            // 16 symbols (one staged 16-byte unit) per iteration
+#pragma unroll 1
+            for (int u4 = 0; u4 < kGroups / 4; ++u4) {
+                uint32_t w[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint64_t acc = window(buf, pm1);
+                    const uint32_t e1 = step2(tab, acc);
+                    const uint32_t e2 = step2(tab, acc);
+                    pm1 += (e1 + e2) & 0xFFu;
+                    bad |= e1 | e2;
+                    w[g] = __builtin_amdgcn_perm(e2, e1, 0x06050201u);
+                }
+                *reinterpret_cast<uint4*>(stage + stage_off(lane, u4)) =
+                    make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int rr = 0; rr < kRounds; ++rr) {
+            const int c = rr * 8 + sub_line;
+            if (!kAll && (c < l0 || c >= l1)) continue;
+            const uint2 sy = *reinterpret_cast<const uint2*>(stage + stage_off(c, part >> 1) +
+                                                             (part & 1) * 8);
+            const uint2 e = ev[rr][q];
+            const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
+            // the output is written once and not read back here: stream it
+            // past the caches (non-temporal store)
+            const v4u o = {__builtin_amdgcn_perm(sy.x, e.x, 0x05010400u),
+                           __builtin_amdgcn_perm(sy.x, e.x, 0x07030602u),
+                           __builtin_amdgcn_perm(sy.y, e.y, 0x05010400u),
+                           __builtin_amdgcn_perm(sy.y, e.y, 0x07030602u)};
+            __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(un.out + 2 * u));
+        }
+        wave_sync();
+    }
+}
+
+// Decode lanes [l0, l1) of a full unit: both super-phases, then the lane
+// checks. The all-lanes pass runs `mid` between its two super-phases (the
+// caller requests the next unit's record there). The super-phase loop stays
+// rolled: unrolled, the compiler hoists the second half's addresses and
+// loads and runs out of registers.
+template <bool kAll, class Mid>
 __device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t* tab,
                                              const uint32_t* buf, uint8_t* stage, const Unit& un,
                                              int j0, uint32_t lane_start, uint32_t lane_bits,
-                                             int l0, int l1, int lane) {
-    const bool mine = kAll || (lane >= l0 && lane < l1);
+                                             int l0, int l1, int lane, Mid&& mid) {
     // buffer bit index of the lane's first code, minus one (>= 0: the buffer
     // starts at least one dword before it)
     uint32_t pm1 = lane_start - 32u * uint32_t(j0) - 1u;
     const uint32_t pm1_0 = pm1;
     uint32_t bad = 0;
-    const int sub_line = lane >> 3, part = lane & 7;
-    uint2 ev[kRounds][kSuper];
-
 #pragma unroll 1
     for (int sp = 0; sp < kPhases; sp += kSuper) {
-        // the next two phases' even-plane bytes: a whole line per chunk
-#pragma unroll
-        for (int rr = 0; rr < kRounds; ++rr) {
-            const int c = rr * 8 + sub_line;
-#pragma unroll
-            for (int f = 0; f < kSuper; ++f) {
-                const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t((sp + f) * kPhase + part * 8);
-                // in bounds for every chunk of a full unit, so not conditional
-                ev[rr][f] = *reinterpret_cast<const uint2*>(un.even + u);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < kSuper; ++q) {
-            const int ph = sp + q;
-            if (mine) {
-                // 16 symbols (one staged 16-byte unit) per iteration
-#pragma unroll 1
-                for (int u4 = 0; u4 < kGroups / 4; ++u4) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        uint64_t acc = window(buf, pm1);
-                        const uint32_t e1 = step2(tab, acc);
-                        const uint32_t e2 = step2(tab, acc);
-                        pm1 += (e1 + e2) & 0xFFu;
-                        bad |= e1 | e2;
-                        w[g] = __builtin_amdgcn_perm(e2, e1, 0x06050201u);
-                    }
-                    *reinterpret_cast<uint4*>(stage + stage_off(lane, u4)) =
-                        make_uint4(w[0], w[1], w[2], w[3]);
-                }
-            }
-            wave_sync();
-#pragma unroll
-            for (int rr = 0; rr < kRounds; ++rr) {
-                const int c = rr * 8 + sub_line;
-                if (!kAll && (c < l0 || c >= l1)) continue;
-                const uint2 sy = *reinterpret_cast<const uint2*>(stage + stage_off(c, part >> 1) +
-                                                                 (part & 1) * 8);
-                const uint2 e = ev[rr][q];
-                const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
-                // the output is written once and not read back here: stream
-                // it past the caches (non-temporal store)
-                const v4u o = {__builtin_amdgcn_perm(sy.x, e.x, 0x05010400u),
-                               __builtin_amdgcn_perm(sy.x, e.x, 0x07030602u),
-                               __builtin_amdgcn_perm(sy.y, e.y, 0x05010400u),
-                               __builtin_amdgcn_perm(sy.y, e.y, 0x07030602u)};
-                __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(un.out + 2 * u));
-            }
-            wave_sync();
-        }
+        if (sp == kSuper) mid();
+        decode_super<kAll>(tab, buf, stage, un, sp, l0, l1, lane, pm1, bad);
     }
-    if (mine) {
+    if (kAll || (lane >= l0 && lane < l1)) {
         if (bad & kBad) flag(a.status, K3HUF_DEV_CODE);
         if (pm1 - pm1_0 != lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
     }
@@ -449,7 +465,18 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const uint32_t n_units = a.n_sub * kUnitsPerSub;
     const uint32_t T = gridDim.x * kWaves;
+    const uint32_t rounds = n_units / T;
+    const uint32_t stat = rounds > kDynRounds ? rounds - kDynRounds : 0u;   // static rounds
+    const uint32_t dyn0 = stat * T;                                          // first handed-out unit
+    const uint32_t groups = min(kGroupsPerSlot, gridDim.x);
+    const uint32_t group = blockIdx.x % groups;
+    uint32_t* slot = &g_sched[kSlotWords * a.slot];
     uint32_t h = blockIdx.x * kWaves + wave;
+    if (stat == 0) {
+        uint32_t t = 0;
+        if (lane == 0) t = atomicAdd(&slot[group], 1u);
+        h = uniform(dyn0 + group + groups * lane_value(t, 0));
+    }
     // stripe values of the block holding this wave's first unit, requested
     // before the table build so that their latency overlaps it
     uint32_t blk = h < n_units ? h / (kUnitsPerSub * kSubPerStripe * 64u) : 0u;
@@ -461,20 +488,36 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     uint8_t* wl = lds + kTabBytes + wave * kWaveLds;
     uint32_t* buf = reinterpret_cast<uint32_t*>(wl);
     uint8_t* stage = wl + kBufBytes;
-    const uint32_t rounds = n_units / T;
-    const uint32_t groups = min(kGroupsPerSlot, gridDim.x);
-    const uint32_t group = blockIdx.x % groups;
-    uint32_t* slot = &g_sched[kSlotWords * a.slot];
     uint32_t round = 0;
     uint32_t pf_h = 0xFFFFFFFFu;   // unit whose record `pf` holds
     RecLanes pf = {0u, 0u, 0u};
+    uint32_t ticket = 0;           // lane 0: the answer to this unit's request
 
     while (h < n_units) {
-        // on the last static round, ask for a leftover unit now; the answer
-        // is needed only when this unit is done
-        const bool ask = rounds > 0 && round + 1 >= rounds;
-        uint32_t ticket = 0;
+        // the next unit: static, or handed out now (the answer is read
+        // halfway through this unit)
+        const bool ask = round + 1 >= stat;
         if (ask && lane == 0) ticket = atomicAdd(&slot[group], 1u);
+        uint32_t h_next = 0xFFFFFFFFu;
+        auto next_unit = [&]() -> uint32_t {
+            return ask ? dyn0 + group + groups * lane_value(ticket, 0) : h + T;
+        };
+        // learn the next unit and request its record (called between the two
+        // super-phases of a full single-pass unit)
+        auto mid = [&]() {
+            h_next = next_unit();
+            pf_h = 0xFFFFFFFFu;
+            if (h_next < n_units) {
+                const uint32_t kn = h_next / kUnitsPerSub;
+                const uint32_t sn = kn / kSubPerStripe, jn = kn % kSubPerStripe;
+                if ((sn >> 6) == blk && lane_value(sl.n_bits, sn & 63u) != kNoStripe) {
+                    const uint8_t* stn = b + (uint64_t(lane_value(sl.off16, sn & 63u)) << 4);
+                    pf = load_rec(stn + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jn,
+                                  jn + 1 < stripe_subblocks(uint32_t(stripe_raw(a, sn) / 2)), lane);
+                    pf_h = h_next;
+                }
+            }
+        };
         const uint32_t k = h / kUnitsPerSub, half = h % kUnitsPerSub;
         const uint32_t s = k / kSubPerStripe, jsb = k % kSubPerStripe;
         if ((s >> 6) != blk) {
@@ -502,18 +545,6 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         const uint32_t incl = wave_incl_scan(lb);   // prefix within this unit
         const uint32_t unit_bits = lane_value(incl, 63);
         const uint32_t other_bits = lane_value(wave_incl_scan(half ? pf.lo : pf.hi), 63);
-        // request the record of this wave's next static unit
-        pf_h = 0xFFFFFFFFu;
-        if (round + 1 < rounds) {
-            const uint32_t hn = h + T, kn = hn / kUnitsPerSub;
-            const uint32_t sn = kn / kSubPerStripe, jn = kn % kSubPerStripe;
-            if ((sn >> 6) == blk && lane_value(sl.n_bits, sn & 63u) != kNoStripe) {
-                const uint8_t* stn = b + (uint64_t(lane_value(sl.off16, sn & 63u)) << 4);
-                pf = load_rec(stn + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jn,
-                              jn + 1 < stripe_subblocks(uint32_t(stripe_raw(a, sn) / 2)), lane);
-                pf_h = hn;
-            }
-        }
         do {
         if (n_bits == kNoStripe) {
             if (lane == 0 && half == 0) flag(a.status, K3HUF_DEV_STRIPE);
@@ -545,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         const uint32_t lane_end = unit_start + incl;
         const bool full = un.nsyms == uint32_t(kUnitSyms);
 
-    // passes over consecutive lane ranges whose codes fit the buffer
+        // passes over consecutive lane ranges whose codes fit the buffer
         // (one pass unless the unit's codes exceed kBufBytes)
         for (int l0 = 0; l0 < 64;) {
             const int j0 = first_dword(lane_value(lane_start, l0));
@@ -556,21 +587,17 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
             fill_buffer(buf, un, j0, units, lane);
             if (full && l0 == 0 && l1 == 64) {
                 drain_vm();   // fill_buffer has just drained it
-                decode_lanes<true>(a, tab, buf, stage, un, j0, lane_start, lb, 0, 64, lane);
+                decode_lanes<true>(a, tab, buf, stage, un, j0, lane_start, lb, 0, 64, lane, mid);
             } else if (full)
-                decode_lanes<false>(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
+                decode_lanes<false>(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane, [] {});
             else
                 decode_lanes_tail(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
             l0 = l1;
         }
         } while (false);   // the checks above leave a bad unit with `continue`
+        if (h_next == 0xFFFFFFFFu) h_next = next_unit();   // no mid-unit step ran
+        h = uniform(h_next);
         ++round;
-        if (round < rounds)
-            h += T;
-        else if (ask)
-            h = rounds * T + group + groups * __builtin_amdgcn_readlane(ticket, 0);
-        else
-            h = n_units;
     }
 
     // the last workgroup to finish clears this launch's counter slot

@@ -109,3 +109,26 @@ def test_packer_bad_args():
     assert k3huf.lib().k3huf_encode_bound(3) == k3huf.E_ARG
     assert k3huf.lib().k3huf_encode_bound(0) == k3huf.E_ARG
     assert k3huf.encode_bound(2) == O.encode_bound(2)
+
+
+def test_decode_layer_rejects_bad_arguments_before_any_device_call():
+    """The launcher validates sizes and alignment on the host and returns
+    K3HUF_E_ARG without touching the device (so this runs without a GPU).
+    The pointers are never dereferenced on these paths."""
+    raw = k3huf.decode_layer_raw
+    blob, lut, out = 1 << 20, 1 << 21, 1 << 22          # 16-byte aligned fake addresses
+    good = 304 + 8
+    assert raw(0, good, lut, out, 2, 0, None) == k3huf.E_ARG              # null blob
+    assert raw(blob, good, 0, out, 2, 0, None) == k3huf.E_ARG             # null table
+    assert raw(blob, good, lut, 0, 2, 0, None) == k3huf.E_ARG             # null output
+    assert raw(blob + 8, good, lut, out, 2, 0, None) == k3huf.E_ARG       # blob not 16-aligned
+    assert raw(blob, good, lut, out + 4, 2, 0, None) == k3huf.E_ARG       # output not 16-aligned
+    assert raw(blob, good, lut + 1, out, 2, 0, None) == k3huf.E_ARG       # table not 2-aligned
+    assert raw(blob, good, lut, out, 3, 0, None) == k3huf.E_ARG           # odd raw size
+    assert raw(blob, good, lut, out, 0, 0, None) == k3huf.E_ARG           # empty layer
+    assert raw(blob, 303, lut, out, 2, 0, None) == k3huf.E_ARG            # shorter than a header
+    # 3 stripes need 3 stripe offsets after the 304-byte header
+    three = 2 * (1 << 26) + 2
+    assert raw(blob, 304 + 16, lut, out, three, 0, None) == k3huf.E_ARG
+    # offsets are kept in 16-byte units by the kernel: blobs stop below 64 GiB
+    assert raw(blob, 1 << 36, lut, out, 2, 0, None) == k3huf.E_ARG
