@@ -9,11 +9,11 @@
 //   - "key design points": each decoded symbol is the high byte at an odd
 //     offset; the raw even-plane byte goes back at the even offset before it.
 // How it is laid out on the GPU (not from the pages): one wave decodes one
-// 64 KiB-output subblock; lane t decodes lane chunk t (512 symbols) starting
-// at the bit offset the subblock index gives it (the ECF8 page, section 2.1,
-// keeps such per-thread bit offsets beside its code); the table lives in LDS;
-// decoded bytes are staged in LDS so that the even-plane loads and the output
-// stores of a wave cover whole 128-byte lines.
+// half subblock (32 KiB of output); lane t decodes its lane chunk t (256
+// symbols) starting at the bit offset the subblock index gives it (the ECF8
+// page, section 2.1, keeps such per-thread bit offsets beside its code); the
+// table lives in LDS; decoded bytes are staged in LDS so that the even-plane
+// loads and the output stores of a wave cover whole 128-byte lines.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -42,12 +42,19 @@ constexpr int kUnitsPerSub = K3HUF_LANES / kUnitLanes;   // 2
 constexpr int kPhase = 64;                            // symbols per lane per phase
 constexpr int kPhases = K3HUF_LANE_SYMS / kPhase;    // 4
 constexpr int kSuper = 2;                             // phases per even-plane prefetch
-constexpr int kGroups = kPhase / 4;                   // 4-symbol groups per phase
+constexpr int kGroups = kPhase / 4;                   // 4-symbol groups per phase (tail path)
 constexpr int kRounds = 64 / 8;                       // write-out rounds (8 chunks each)
-constexpr int kBufBytes = 8192;                       // per-wave bitstream buffer
+constexpr int kBufBytes = 7680;                       // per-wave bitstream buffer
 constexpr int kBufUnits = kBufBytes / 16;
-constexpr int kStageStride = kPhase;                  // LDS bytes per chunk per phase
+// LDS bytes per chunk per phase: the phase's 64 symbols, then room for the
+// bytes a lane writes past them (one symbol of the next phase, one unused)
+constexpr int kStageStride = kPhase + 4;
 constexpr int kWaveLds = kBufBytes + 64 * kStageStride;
+// table lookups per bit window: each consumes at most 12 bits, five fit in 64
+constexpr int kLookups = 5;
+// bit windows per phase: every lookup yields a symbol, so 64 lookups always
+// finish a phase
+constexpr int kMaxWindows = (kPhase + kLookups - 1) / kLookups;
 constexpr int kTabBytes = K3HUF_LUT_ENTRIES * 4;
 constexpr int kLdsBytes = kTabBytes + kWaves * kWaveLds;
 constexpr uint32_t kSubPerStripe = K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES;
@@ -57,14 +64,18 @@ static_assert(kLdsBytes <= 163840, "LDS budget");
 // (symbol << 4 | length) table: one lookup of the top 12 window bits yields
 // the first code and, when the next code also lies inside those 12 bits, the
 // second one too (the "double-symbol table" the K3 page names under "if
-// revisited"; the container format is unchanged).
-//   [4:0]   bits consumed by the entry's symbols (T); [7:5] zero
-//   [15:8]  first symbol      [23:16] second symbol
+// revisited"; the container format is unchanged). A lookup thus yields one
+// or two symbols; no entry is zero.
+//   [7:0]   first symbol
+//   [11:8]  bits consumed by the entry's symbols (T, 1..12)
+//   [13:12] symbols in the entry (1 or 2)
+//   [14]    index no code covers (decoded as one 12-bit code)
+//   [23:16] second symbol (zero if the entry holds one)
 //   [27:24] length of the first code
-//   [29]    index no code covers (decoded as a 12-bit code)
-//   [31]    entry holds only the first symbol
-constexpr uint32_t kBad = 1u << 29;
-constexpr uint32_t kOne = 1u << 31;
+constexpr uint32_t kBad = 1u << 14;
+__device__ __forceinline__ uint32_t ent_bits(uint32_t e) { return (e >> 8) & 15u; }
+__device__ __forceinline__ uint32_t ent_syms(uint32_t e) { return (e >> 12) & 3u; }
+__device__ __forceinline__ uint32_t ent_len1(uint32_t e) { return (e >> 24) & 15u; }
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -144,31 +155,18 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) {
 __device__ uint32_t make_entry(const uint16_t* lut, uint32_t i) {
     const uint32_t a = lut[i];
     const uint32_t l1 = a & 15u;
-    if (l1 == 0 || l1 > K3HUF_MAXLEN) return kBad | (12u << 24) | 12u;
-    const uint32_t e = (l1 << 24) | (((a >> 4) & 0xFFu) << 8) | l1;
+    if (l1 == 0 || l1 > K3HUF_MAXLEN) return kBad | (12u << 24) | (1u << 12) | (12u << 8);
+    const uint32_t e = (l1 << 24) | (1u << 12) | (l1 << 8) | ((a >> 4) & 0xFFu);
     if (l1 < K3HUF_MAXLEN) {
         const uint32_t b = lut[(i << l1) & 0xFFFu];
         const uint32_t l2 = b & 15u;
-        if (l2 && l1 + l2 <= K3HUF_MAXLEN) return e + (((b >> 4) & 0xFFu) << 16) + l2;
+        if (l2 && l1 + l2 <= K3HUF_MAXLEN) return e + (((b >> 4) & 0xFFu) << 16) + (1u << 12) + (l2 << 8);
     }
-    return e | kOne;
+    return e;
 }
 
 __device__ __forceinline__ uint32_t peek(const uint32_t* tab, uint64_t acc) {
     return tab[uint32_t(acc >> 52)];
-}
-
-// Two symbols from the top of the window, then shift them out. An entry
-// holding one symbol is completed with a second lookup after its first code.
-__device__ __forceinline__ uint32_t step2(const uint32_t* tab, uint64_t& acc) {
-    uint32_t e = peek(tab, acc);
-    if (int32_t(e) < 0) {
-        const uint32_t e2 = peek(tab, acc << (e & 63u));
-        e = e + (((e2 >> 8) & 0xFFu) << 16) + ((e2 >> 24) & 15u) + kOne;
-        e |= e2 & kBad;
-    }
-    acc <<= (e & 63u);
-    return e;
 }
 
 // 64-bit window whose top bit is the bit after buffer bit pm1: buffer dwords
@@ -181,10 +179,10 @@ __device__ __forceinline__ uint64_t window(const uint32_t* buf, uint32_t pm1) {
            __builtin_amdgcn_alignbit(d1, d2, r);
 }
 
-// staged 16-byte unit q of chunk c's phase symbols, swizzled so that 8
-// consecutive lanes writing or 32 lanes reading hit distinct LDS banks
-__device__ __forceinline__ int stage_off(int c, int q) {
-    return c * kStageStride + ((q ^ ((c >> 2) & 3)) << 4);
+// the 8 staged symbols (2 dwords) of chunk c at phase offset 8 part
+__device__ __forceinline__ uint2 staged8(const uint8_t* stage, int c, int part) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(stage + c * kStageStride + part * 8);
+    return make_uint2(p[0], p[1]);
 }
 
 struct Unit {
@@ -194,6 +192,47 @@ struct Unit {
     int dmax;              // last readable 16-byte unit (dwords from `bits`)
     uint32_t nsyms;        // symbols in this unit (16384 unless last in stripe)
 };
+
+// Per-lane decode state across the phases of a unit.
+struct LaneState {
+    uint32_t pm1;    // buffer bit index of the next code, minus one
+    uint32_t cnt;    // symbols decoded in this unit (may pass the end by one)
+    uint32_t last;   // the last table entry taken
+    uint32_t bad;    // OR of all entries taken
+};
+
+// Decode one phase of a lane: symbols [64 ph, 64 ph + 64) of its chunk into
+// its stage row. Each 64-bit window feeds kLookups table lookups; each
+// lookup yields one or two symbols, written as two bytes at the lane's count
+// (a second byte past the entry's symbols is overwritten by the next lookup
+// or lands past the phase). A lane that has its 64 symbols takes zero entries
+// (no bits, no symbols) until the wave's slowest lane is done. A lookup that
+// ends one symbol past the phase leaves that symbol at row offset 64; it is
+// moved to offset 0 when the next phase starts.
+__device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint32_t* buf, uint8_t* row,
+                                             int ph, LaneState& ls) {
+    const uint32_t base = uint32_t(ph * kPhase), target = base + kPhase;
+    if (ls.cnt > base) row[0] = uint8_t(ls.last >> 16);   // carried symbol
+#pragma unroll 1
+    for (int w = 0; w < kMaxWindows; ++w) {
+        if (!__any(ls.cnt < target)) break;
+        uint64_t acc = window(buf, ls.pm1);
+#pragma unroll
+        for (int i = 0; i < kLookups; ++i) {
+            uint32_t e = peek(tab, acc);
+            e = ls.cnt < target ? e : 0u;
+            const uint32_t t = ent_bits(e);
+            uint8_t* p = row + (ls.cnt - base);
+            p[0] = uint8_t(e);
+            p[1] = uint8_t(e >> 16);
+            ls.last = e ? e : ls.last;
+            ls.bad |= e;
+            ls.cnt += ent_syms(e);
+            ls.pm1 += t;
+            acc <<= t;
+        }
+    }
+}
 
 // One super-phase (phases sp and sp + 1) of lanes [l0, l1) of a full unit
 // (64 chunks of 256 symbols) whose bitstream dwords [j0, ...) the caller has
@@ -205,7 +244,7 @@ struct Unit {
 template <bool kAll>
 __device__ __forceinline__ void decode_super(const uint32_t* tab, const uint32_t* buf,
                                              uint8_t* stage, const Unit& un, int sp, int l0, int l1,
-                                             int lane, uint32_t& pm1, uint32_t& bad) {
+                                             int lane, LaneState& ls) {
     const bool mine = kAll || (lane >= l0 && lane < l1);
     const int sub_line = lane >> 3, part = lane & 7;
     uint2 ev[kRounds][kSuper];
@@ -223,31 +262,13 @@ __device__ __forceinline__ void decode_super(const uint32_t* tab, const uint32_t
 #pragma unroll
     for (int q = 0; q < kSuper; ++q) {
         const int ph = sp + q;
-        if (mine) {
-            // 16 symbols (one staged 16-byte unit) per iteration
-#pragma unroll 1
-            for (int u4 = 0; u4 < kGroups / 4; ++u4) {
-                uint32_t w[4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    uint64_t acc = window(buf, pm1);
-                    const uint32_t e1 = step2(tab, acc);
-                    const uint32_t e2 = step2(tab, acc);
-                    pm1 += (e1 + e2) & 0xFFu;
-                    bad |= e1 | e2;
-                    w[g] = __builtin_amdgcn_perm(e2, e1, 0x06050201u);
-                }
-                *reinterpret_cast<uint4*>(stage + stage_off(lane, u4)) =
-                    make_uint4(w[0], w[1], w[2], w[3]);
-            }
-        }
+        if (mine) decode_phase(tab, buf, stage + lane * kStageStride, ph, ls);
         wave_sync();
 #pragma unroll
         for (int rr = 0; rr < kRounds; ++rr) {
             const int c = rr * 8 + sub_line;
             if (!kAll && (c < l0 || c >= l1)) continue;
-            const uint2 sy = *reinterpret_cast<const uint2*>(stage + stage_off(c, part >> 1) +
-                                                             (part & 1) * 8);
+            const uint2 sy = staged8(stage, c, part);
             const uint2 e = ev[rr][q];
             const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
             // the output is written once and not read back here: stream it
@@ -272,25 +293,28 @@ __device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t
                                              const uint32_t* buf, uint8_t* stage, const Unit& un,
                                              int j0, uint32_t lane_start, uint32_t lane_bits,
                                              int l0, int l1, int lane, Mid&& mid) {
-    // buffer bit index of the lane's first code, minus one (>= 0: the buffer
-    // starts at least one dword before it)
-    uint32_t pm1 = lane_start - 32u * uint32_t(j0) - 1u;
-    const uint32_t pm1_0 = pm1;
-    uint32_t bad = 0;
+    // the buffer starts at least one dword before the lane's first code, so
+    // pm1 >= 0
+    LaneState ls = {lane_start - 32u * uint32_t(j0) - 1u, 0u, 0u, 0u};
+    const uint32_t pm1_0 = ls.pm1;
 #pragma unroll 1
     for (int sp = 0; sp < kPhases; sp += kSuper) {
         if (sp == kSuper) mid();
-        decode_super<kAll>(tab, buf, stage, un, sp, l0, l1, lane, pm1, bad);
+        decode_super<kAll>(tab, buf, stage, un, sp, l0, l1, lane, ls);
     }
     if (kAll || (lane >= l0 && lane < l1)) {
-        if (bad & kBad) flag(a.status, K3HUF_DEV_CODE);
-        if (pm1 - pm1_0 != lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
+        // a last lookup that ran one symbol past the chunk took that
+        // symbol's bits too
+        uint32_t used = ls.pm1 - pm1_0;
+        if (ls.cnt > K3HUF_LANE_SYMS) used -= ent_bits(ls.last) - ent_len1(ls.last);
+        if (ls.bad & kBad) flag(a.status, K3HUF_DEV_CODE);
+        if (used != lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
     }
 }
 
 // The same for the layer's last unit when it holds fewer than 16384 symbols:
-// lane t decodes clamp(nsyms - 256 t, 0, 256) symbols one table step per
-// symbol; kept plain (it runs at most once per layer).
+// lane t decodes clamp(nsyms - 256 t, 0, 256) symbols one code per table
+// step; kept plain (it runs at most once per layer).
 __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uint32_t* tab,
                                                             const uint32_t* buf, uint8_t* stage,
                                                             const Unit& un, int j0,
@@ -302,30 +326,27 @@ __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uin
     const uint32_t pm1_0 = pm1;
     uint32_t bad = 0;
     const int sub_line = lane >> 3, part = lane & 7;
+    uint32_t* row = reinterpret_cast<uint32_t*>(stage + lane * kStageStride);
 #pragma unroll 1
     for (int ph = 0; ph < kPhases; ++ph) {
         if (mine) {
 #pragma unroll 1
-            for (int u4 = 0; u4 < kGroups / 4; ++u4) {
-                uint32_t w[4];
+            for (int g = 0; g < kGroups; ++g) {
+                uint64_t acc = window(buf, pm1);
+                uint32_t ww = 0;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    uint64_t acc = window(buf, pm1);
-                    uint32_t ww = 0;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const uint32_t e = peek(tab, acc);
-                        const bool live = ph * kPhase + (u4 * 4 + g) * 4 + t < lane_cnt;
-                        const uint32_t l = live ? (e >> 24) & 15u : 0u;
-                        if (live) bad |= e;
-                        acc <<= l;
-                        pm1 += l;
-                        constexpr uint32_t sel[4] = {0x03020105u, 0x03020500u, 0x03050100u, 0x05020100u};
-                        ww = __builtin_amdgcn_perm(e, ww, sel[t]);
-                    }
-                    w[g] = ww;
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t e = peek(tab, acc);
+                    const bool live = ph * kPhase + g * 4 + t < lane_cnt;
+                    const uint32_t l = live ? ent_len1(e) : 0u;
+                    if (live) bad |= e;
+                    acc <<= l;
+                    pm1 += l;
+                    // the entry's first symbol into byte t of ww
+                    constexpr uint32_t sel[4] = {0x03020104u, 0x03020400u, 0x03040100u, 0x04020100u};
+                    ww = __builtin_amdgcn_perm(e, ww, sel[t]);
                 }
-                *reinterpret_cast<uint4*>(stage + stage_off(lane, u4)) = make_uint4(w[0], w[1], w[2], w[3]);
+                row[g] = ww;
             }
         }
         wave_sync();
@@ -334,7 +355,7 @@ __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uin
             const int c = rr * 8 + sub_line;
             const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
             if (c < l0 || c >= l1 || u >= un.nsyms) continue;
-            const uint2 sy = *reinterpret_cast<const uint2*>(stage + stage_off(c, part >> 1) + (part & 1) * 8);
+            const uint2 sy = staged8(stage, c, part);
             const uint2 e = *reinterpret_cast<const uint2*>(un.even + u);
             const uint32_t m = min(un.nsyms - u, 8u);
             for (uint32_t i = 0; i < m; ++i) {
@@ -358,7 +379,7 @@ __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uin
 // unconditional lets the compiler count outstanding loads exactly instead of
 // waiting for all memory operations at later register reuse.
 __device__ __forceinline__ void fill_buffer(uint32_t* buf, const Unit& un, int j0, int units, int lane) {
-    constexpr int kPer = kBufUnits / 64;
+    constexpr int kPer = (kBufUnits + 63) / 64;
     uint4 v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -367,8 +388,9 @@ __device__ __forceinline__ void fill_buffer(uint32_t* buf, const Unit& un, int j
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-        *reinterpret_cast<uint4*>(buf + 4 * (lane + 64 * i)) =
-            make_uint4(bswap32(v[i].x), bswap32(v[i].y), bswap32(v[i].z), bswap32(v[i].w));
+        if (kBufUnits % 64 == 0 || i < kPer - 1 || lane + 64 * i < kBufUnits)
+            *reinterpret_cast<uint4*>(buf + 4 * (lane + 64 * i)) =
+                make_uint4(bswap32(v[i].x), bswap32(v[i].y), bswap32(v[i].z), bswap32(v[i].w));
     wave_sync();
 }
 
