@@ -175,6 +175,47 @@ int k3huf_decode_ring(const k3huf_ring_layer* layers, int n_layers, void* const*
                       k3huf_ring_cb cb, void* user, uint32_t* d_status);
 
 /*
+ * k3huf_decode_ring_host -- the layer ring fed from host memory: each layer's
+ * container is copied over PCIe into a device stage buffer on copy_stream,
+ * then decoded from there into the slot ring as k3huf_decode_ring does.
+ * K3 page, "background" and "the measurement that shelved it": every token
+ * streams the trunk from storage in the fixed layer order, and the decoder
+ * must keep up with the feed; K3 TUNING page, section 5 ("--trunk-ring N"):
+ * of the ring's slots one holds the layer in use and the others are reads in
+ * flight, so extra stage buffers let copies run ahead of decoding.
+ * Layer k is copied into stage k % n_stage once the decode that last read
+ * that stage is done (event wait on copy_stream), and decoded on stream
+ * k % n_streams into slot k % n_slots once the copy is done and the slot's
+ * previous consumer released it; cb (nullable) then queues the consumer, and
+ * the slot is released behind it. Everything is queued asynchronously; the
+ * call returns without synchronizing.
+ * layers[k]: h_blob, the container in host memory (pinned memory, e.g. from
+ *   hipHostMalloc, for copies that overlap decoding; pageable memory works
+ *   but its copies do not overlap), its size (<= stage_bytes), its device LUT
+ *   (from k3huf_build_table), its raw size (<= slot_bytes). The host blob
+ *   must stay unchanged until its copy has run.
+ * d_stage[n_stage]: device buffers, 16-byte aligned, stage_bytes each.
+ * d_slots[n_slots], streams[n_streams], copy_stream (hipStream_t as void*):
+ *   caller-owned; copy_stream should differ from the decode streams so
+ *   copies overlap decoding.
+ * d_status: as for k3huf_decode_layer (shared by all layers).
+ * Errors: K3HUF_E_ARG (nulls, counts < 1, a layer larger than a stage or
+ * slot, a misaligned stage), K3HUF_E_HIP (work queued before the failing call
+ * still runs).
+ */
+typedef struct k3huf_host_layer {
+    const void* h_blob;
+    size_t blob_bytes;
+    const uint16_t* d_lut;
+    size_t raw_bytes;
+} k3huf_host_layer;
+
+int k3huf_decode_ring_host(const k3huf_host_layer* layers, int n_layers, void* const* d_stage,
+                           int n_stage, size_t stage_bytes, void* const* d_slots, int n_slots,
+                           size_t slot_bytes, void* copy_stream, void* const* streams,
+                           int n_streams, k3huf_ring_cb cb, void* user, uint32_t* d_status);
+
+/*
  * k3huf_encode_bound -- container size upper bound for raw_bytes of layer data.
  * k3huf_encode_layer -- host packer: one histogram and codelen[256] over the
  * whole layer's odd bytes (K3 page, "what was implemented"), Huffman depths

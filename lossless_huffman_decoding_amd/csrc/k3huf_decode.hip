@@ -730,4 +730,58 @@ int k3huf_decode_ring(const k3huf_ring_layer* layers, int n_layers, void* const*
     return rc;
 }
 
+int k3huf_decode_ring_host(const k3huf_host_layer* layers, int n_layers, void* const* d_stage,
+                           int n_stage, size_t stage_bytes, void* const* d_slots, int n_slots,
+                           size_t slot_bytes, void* copy_stream, void* const* streams,
+                           int n_streams, k3huf_ring_cb cb, void* user, uint32_t* d_status) {
+    if (!layers || n_layers < 0 || !d_stage || n_stage < 1 || !d_slots || n_slots < 1 || !streams ||
+        n_streams < 1)
+        return K3HUF_E_ARG;
+    for (int k = 0; k < n_layers; ++k)
+        if (!layers[k].h_blob || !layers[k].d_lut || layers[k].blob_bytes > stage_bytes ||
+            layers[k].raw_bytes > slot_bytes)
+            return K3HUF_E_ARG;
+    for (int s = 0; s < n_stage; ++s)
+        if (!d_stage[s] || (reinterpret_cast<uintptr_t>(d_stage[s]) & 15)) return K3HUF_E_ARG;
+    for (int s = 0; s < n_slots; ++s)
+        if (!d_slots[s]) return K3HUF_E_ARG;
+    hipStream_t cs = static_cast<hipStream_t>(copy_stream);
+    // copied[s]: stage buffer s holds its layer; stage_free[s]: the decode
+    // that read it is done; slot_free[o]: slot o's consumer is done
+    std::vector<hipEvent_t> ev(2 * size_t(n_stage) + size_t(n_slots), nullptr);
+    hipEvent_t* copied = ev.data();
+    hipEvent_t* stage_free = copied + n_stage;
+    hipEvent_t* slot_free = stage_free + n_stage;
+    std::vector<char> stage_used(n_stage, 0), slot_used(n_slots, 0);
+    int rc = K3HUF_OK;
+    for (auto& e : ev)
+        if (rc == K3HUF_OK && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+            rc = K3HUF_E_HIP;
+    for (int k = 0; k < n_layers && rc == K3HUF_OK; ++k) {
+        const int s = k % n_stage, o = k % n_slots;
+        hipStream_t st = static_cast<hipStream_t>(streams[k % n_streams]);
+        // the copy into stage s waits for the decode that last read it
+        if (stage_used[s] && hipStreamWaitEvent(cs, stage_free[s], 0) != hipSuccess) rc = K3HUF_E_HIP;
+        if (rc == K3HUF_OK &&
+            (hipMemcpyAsync(d_stage[s], layers[k].h_blob, layers[k].blob_bytes, hipMemcpyHostToDevice,
+                            cs) != hipSuccess ||
+             hipEventRecord(copied[s], cs) != hipSuccess || hipStreamWaitEvent(st, copied[s], 0) != hipSuccess))
+            rc = K3HUF_E_HIP;
+        if (rc == K3HUF_OK && slot_used[o] && hipStreamWaitEvent(st, slot_free[o], 0) != hipSuccess)
+            rc = K3HUF_E_HIP;
+        if (rc) break;
+        rc = k3huf_decode_layer(d_stage[s], layers[k].blob_bytes, layers[k].d_lut, d_slots[o],
+                                layers[k].raw_bytes, st, d_status);
+        if (rc) break;
+        if (hipEventRecord(stage_free[s], st) != hipSuccess) rc = K3HUF_E_HIP;
+        stage_used[s] = 1;
+        if (cb) cb(k, d_slots[o], layers[k].raw_bytes, st, user);
+        if (rc == K3HUF_OK && hipEventRecord(slot_free[o], st) != hipSuccess) rc = K3HUF_E_HIP;
+        slot_used[o] = 1;
+    }
+    for (auto& e : ev)
+        if (e) (void)hipEventDestroy(e);
+    return rc;
+}
+
 }  // extern "C"

@@ -22,7 +22,7 @@ DEV_HEADER, DEV_STRIPE, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 2, 4, 8, 16
 
 # names the C header declares, checked by the ABI test
 EXPORTS = ("k3huf_build_table", "k3huf_layer_info", "k3huf_decode_layer", "k3huf_decode_ring",
-           "k3huf_encode_bound", "k3huf_encode_layer", "k3huf_strerror")
+           "k3huf_decode_ring_host", "k3huf_encode_bound", "k3huf_encode_layer", "k3huf_strerror")
 
 
 class K3HufError(RuntimeError):
@@ -39,6 +39,11 @@ class Info(ctypes.Structure):
 
 class RingLayer(ctypes.Structure):
     _fields_ = [("d_blob", ctypes.c_void_p), ("blob_bytes", ctypes.c_size_t),
+                ("d_lut", ctypes.c_void_p), ("raw_bytes", ctypes.c_size_t)]
+
+
+class HostLayer(ctypes.Structure):
+    _fields_ = [("h_blob", ctypes.c_void_p), ("blob_bytes", ctypes.c_size_t),
                 ("d_lut", ctypes.c_void_p), ("raw_bytes", ctypes.c_size_t)]
 
 
@@ -66,6 +71,11 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(vp), ctypes.c_int, sz,
                                         ctypes.POINTER(vp), ctypes.c_int, RING_CB, vp, vp]
         L.k3huf_decode_ring.restype = ctypes.c_int
+        L.k3huf_decode_ring_host.argtypes = [ctypes.POINTER(HostLayer), ctypes.c_int,
+                                             ctypes.POINTER(vp), ctypes.c_int, sz,
+                                             ctypes.POINTER(vp), ctypes.c_int, sz, vp,
+                                             ctypes.POINTER(vp), ctypes.c_int, RING_CB, vp, vp]
+        L.k3huf_decode_ring_host.restype = ctypes.c_int
         L.k3huf_encode_bound.argtypes = [ctypes.c_uint64]
         L.k3huf_encode_bound.restype = ctypes.c_int64
         L.k3huf_encode_layer.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, ctypes.c_int]
@@ -172,14 +182,39 @@ def decode_ring(layers, slots, streams, cb=None, d_status=None) -> None:
     slot_ptrs = (ctypes.c_void_p * len(slots))(*[s.data_ptr() for s in slots])
     stream_ptrs = (ctypes.c_void_p * len(streams))(*[_stream_handle(s) for s in streams])
     slot_bytes = min(s.numel() for s in slots)
-    index = {s.data_ptr(): i for i, s in enumerate(slots)}
-    if cb is not None:
-        def _tramp(k, slot, raw, stream, user):
-            cb(k, index[slot], stream)
-        c_cb = RING_CB(_tramp)
-    else:
-        c_cb = RING_CB()
+    c_cb = _ring_cb(cb, slots)
     rc = lib().k3huf_decode_ring(arr, n, slot_ptrs, len(slots), slot_bytes, stream_ptrs,
                                  len(streams), c_cb, None,
                                  d_status.data_ptr() if d_status is not None else None)
     _check(rc, "k3huf_decode_ring")
+
+
+def _ring_cb(cb, slots):
+    if cb is None:
+        return RING_CB()
+    index = {s.data_ptr(): i for i, s in enumerate(slots)}
+
+    def _tramp(k, slot, raw, stream, user):
+        cb(k, index[slot], stream)
+    return RING_CB(_tramp)
+
+
+def decode_ring_host(layers, stages, slots, copy_stream, streams, cb=None, d_status=None) -> None:
+    """The host-fed ring: ``layers`` is a list of (h_blob, d_lut, raw_bytes)
+    with h_blob a host uint8 tensor (pinned for overlapped copies); each
+    container is copied into stage buffer k % len(stages) (device uint8
+    tensors) on ``copy_stream``, then decoded into slot k % len(slots) on
+    streams[k % len(streams)]. ``cb`` as for decode_ring."""
+    n = len(layers)
+    arr = (HostLayer * max(n, 1))()
+    for k, (blob, lut, raw) in enumerate(layers):
+        arr[k] = HostLayer(blob.data_ptr(), blob.numel(), lut.data_ptr(), raw)
+    stage_ptrs = (ctypes.c_void_p * len(stages))(*[s.data_ptr() for s in stages])
+    slot_ptrs = (ctypes.c_void_p * len(slots))(*[s.data_ptr() for s in slots])
+    stream_ptrs = (ctypes.c_void_p * len(streams))(*[_stream_handle(s) for s in streams])
+    c_cb = _ring_cb(cb, slots)
+    rc = lib().k3huf_decode_ring_host(arr, n, stage_ptrs, len(stages), min(s.numel() for s in stages),
+                                      slot_ptrs, len(slots), min(s.numel() for s in slots),
+                                      _stream_handle(copy_stream), stream_ptrs, len(streams), c_cb,
+                                      None, d_status.data_ptr() if d_status is not None else None)
+    _check(rc, "k3huf_decode_ring_host")

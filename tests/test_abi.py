@@ -132,3 +132,34 @@ def test_decode_layer_rejects_bad_arguments_before_any_device_call():
     assert raw(blob, 304 + 16, lut, out, three, 0, None) == k3huf.E_ARG
     # offsets are kept in 16-byte units by the kernel: blobs stop below 64 GiB
     assert raw(blob, 1 << 36, lut, out, 2, 0, None) == k3huf.E_ARG
+
+
+def test_host_ring_rejects_bad_arguments_before_any_device_call():
+    """k3huf_decode_ring_host checks counts, sizes and alignment on the host
+    and returns K3HUF_E_ARG before creating events or queuing work (so this
+    runs without a GPU; no pointer is dereferenced on these paths)."""
+    import ctypes
+    L = k3huf.lib()
+    vp = ctypes.c_void_p
+    lay = (k3huf.HostLayer * 1)(k3huf.HostLayer(1 << 20, 4096, 1 << 21, 8192))
+    stage = (vp * 2)(1 << 24, 1 << 25)
+    slots = (vp * 2)(1 << 26, 1 << 27)
+    streams = (vp * 1)(None)
+    cb = k3huf.RING_CB()
+
+    def call(layers=lay, n=1, st=stage, n_st=2, st_bytes=4096, sl=slots, n_sl=2, sl_bytes=8192,
+             strm=streams, n_strm=1):
+        return L.k3huf_decode_ring_host(layers, n, st, n_st, st_bytes, sl, n_sl, sl_bytes, None,
+                                        strm, n_strm, cb, None, None)
+    assert call(layers=None) == k3huf.E_ARG
+    assert call(n=-1) == k3huf.E_ARG
+    assert call(n_st=0) == k3huf.E_ARG
+    assert call(n_sl=0) == k3huf.E_ARG
+    assert call(n_strm=0) == k3huf.E_ARG
+    assert call(st_bytes=4095) == k3huf.E_ARG               # container larger than a stage
+    assert call(sl_bytes=8190) == k3huf.E_ARG               # layer larger than a slot
+    assert call(st=(vp * 2)(1 << 24, (1 << 25) + 8)) == k3huf.E_ARG   # stage not 16-aligned
+    assert call(st=(vp * 2)(1 << 24, None)) == k3huf.E_ARG
+    assert call(sl=(vp * 2)(None, 1 << 27)) == k3huf.E_ARG
+    assert call(layers=(k3huf.HostLayer * 1)(k3huf.HostLayer(None, 4096, 1 << 21, 8192))) == k3huf.E_ARG
+    assert call(layers=(k3huf.HostLayer * 1)(k3huf.HostLayer(1 << 20, 4096, None, 8192))) == k3huf.E_ARG

@@ -241,3 +241,74 @@ def test_ring_decodes_layers_in_order(n_slots, n_streams):
     assert int(status.item()) == 0
     for k in range(len(xs)):
         assert (results[k].cpu().numpy() == xs[k]).all(), k
+
+
+# ---------------------------------------------------------------------------
+# host-fed ring (K3 page, "background": the trunk streams from storage in the
+# fixed layer order; K3 TUNING page, section 5: extra ring slots hold reads in
+# flight)
+
+def _pinned(a):
+    t = torch.empty(a.size, dtype=torch.uint8, pin_memory=True)
+    t.numpy()[:] = a
+    return t
+
+
+@pytest.mark.parametrize("n_stage,n_slots,n_streams", [(2, 2, 2), (1, 1, 1), (3, 2, 2), (2, 3, 1)])
+def test_host_ring_decodes_layers_in_order(n_stage, n_slots, n_streams):
+    sizes = [3 * 65536 + 514, 65536, 2 * 65536 + 2, 5 * 65536, 1026, 4 * 65536 + 100, 70000]
+    xs = [synth.small_random(300 + k, n) for k, n in enumerate(sizes)]
+    blobs = [O.encode_layer(x) for x in xs]
+    luts = [k3huf.build_table(k3huf.layer_info(b)["codelen"]) for b in blobs]
+    h_blobs = [_pinned(b) for b in blobs]
+    d_luts = [torch.from_numpy(l.view(np.int16)).to(DEV) for l in luts]
+    layers = [(hb, dl, x.size) for hb, dl, x in zip(h_blobs, d_luts, xs)]
+    stages = [torch.empty(max(b.size for b in blobs), dtype=torch.uint8, device=DEV)
+              for _ in range(n_stage)]
+    slots = [torch.empty(max(sizes), dtype=torch.uint8, device=DEV) for _ in range(n_slots)]
+    copy_stream = torch.cuda.Stream()
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]
+    by_handle = {s.cuda_stream: s for s in streams}
+    results = [torch.empty(n, dtype=torch.uint8, device=DEV) for n in sizes]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+
+    def consume(k, slot, handle):
+        with torch.cuda.stream(by_handle[handle]):
+            results[k].copy_(slots[slot][: sizes[k]])
+
+    say("host ring", n_stage, n_slots, n_streams)
+    k3huf.decode_ring_host(layers, stages, slots, copy_stream, streams, consume, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for k in range(len(xs)):
+        assert (results[k].cpu().numpy() == xs[k]).all(), k
+
+
+def test_host_ring_repeated_containers_and_pageable_memory():
+    """The same host container fed several times (stage reuse), and a
+    pageable (not pinned) host container: both decode exactly."""
+    x = synth.small_random(77, 6 * 65536 + 6)
+    blob = O.encode_layer(x)
+    lut = torch.from_numpy(k3huf.build_table(k3huf.layer_info(blob)["codelen"]).view(np.int16)).to(DEV)
+    pinned = _pinned(blob)
+    pageable = torch.from_numpy(blob.copy())
+    layers = [(pinned, lut, x.size), (pageable, lut, x.size), (pinned, lut, x.size),
+              (pinned, lut, x.size)]
+    stages = [torch.empty(blob.size, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    slots = [torch.empty(x.size, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    copy_stream = torch.cuda.Stream()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    by_handle = {s.cuda_stream: s for s in streams}
+    results = [torch.empty(x.size, dtype=torch.uint8, device=DEV) for _ in layers]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+
+    def consume(k, slot, handle):
+        with torch.cuda.stream(by_handle[handle]):
+            results[k].copy_(slots[slot])
+
+    say("host ring repeat/pageable")
+    k3huf.decode_ring_host(layers, stages, slots, copy_stream, streams, consume, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for k, r in enumerate(results):
+        assert (r.cpu().numpy() == x).all(), k
