@@ -229,6 +229,34 @@ int64_t k3huf_encode_bound(uint64_t raw_bytes);
 int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, uint64_t cap,
                            int n_threads);
 
+/*
+ * k3huf_encode_work_bytes -- device work-buffer size k3huf_encode_layer_dev
+ *   needs for raw_bytes of layer data (or K3HUF_E_ARG for an odd or zero size).
+ * k3huf_encode_layer_dev -- the packer on the GPU: the bf16 layer in device
+ * memory becomes, in device memory, the container k3huf_encode_layer writes
+ * for the same bytes (byte for byte). K3 page, "what was implemented": one
+ * histogram and codelen[256] for the whole layer's odd bytes, MSB-first
+ * Huffman bitstream per stripe, even plane raw; "canonical code assignment
+ * and Kraft check": depths limited to 12 bits, longest-first canonical codes.
+ * The histogram, the lane-chunk bit counts, their per-stripe prefix sums (the
+ * subblock index), the bit packing and the even-plane copy run on the GPU;
+ * the code lengths and the layout are computed on the host from the GPU's
+ * 256-bin histograms.
+ * d_raw: device, 16-byte aligned, raw_bytes (even, > 0). d_out: device,
+ *   16-byte aligned, cap >= k3huf_encode_bound(raw_bytes). d_work: device,
+ *   16-byte aligned, work_bytes >= k3huf_encode_work_bytes(raw_bytes); its
+ *   contents are scratch. All buffers are caller-owned.
+ * stream: hipStream_t as void*. The call is synchronous: it waits for the
+ *   histograms, then queues the rest and waits for it, so the container is
+ *   complete on return. It allocates no device memory.
+ * Returns the container size, K3HUF_E_ARG (bad sizes, alignment or
+ * capacity), K3HUF_E_HIP, or K3HUF_E_CORRUPT if d_raw changed during the
+ * call (the GPU's bit counts disagree with its histograms).
+ */
+int64_t k3huf_encode_work_bytes(uint64_t raw_bytes);
+int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
+                               void* d_work, uint64_t work_bytes, void* stream);
+
 /* Static text for a return code. */
 const char* k3huf_strerror(int code);
 

@@ -1,6 +1,8 @@
 """Compile the k3huf HIP library for gfx950, in-tree.
 
-Produces lossless_huffman_decoding_amd/_lib/libk3huf.so from csrc/ with hipcc.
+Produces lossless_huffman_decoding_amd/_lib/libk3huf.so from csrc/ with hipcc
+(decode kernels and ring drivers, GPU encoder) and g++ (host table build,
+header parsing, packer).
 Always recompiles when called (the build check wants a real compile).
 """
 
@@ -38,9 +40,10 @@ def build(verbose: bool = False) -> str:
     bdir = os.path.join(OUT_DIR, "_obj")
     os.makedirs(bdir, exist_ok=True)
     objs = []
-    o = os.path.join(bdir, "k3huf_decode.o")
-    _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "k3huf_decode.hip"), "-o", o])
-    objs.append(o)
+    for name in ("k3huf_decode", "k3huf_encode"):
+        o = os.path.join(bdir, name + ".o")
+        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
+        objs.append(o)
     o = os.path.join(bdir, "k3huf_host.o")
     _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "k3huf_host.cpp"), "-o", o])
     objs.append(o)

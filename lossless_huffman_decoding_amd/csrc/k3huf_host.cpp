@@ -1,6 +1,7 @@
 // Host side of the k3huf library: decode-table build, header parsing and the
 // native packer. Container layout and sources: include/k3huf.h.
 #include "k3huf.h"
+#include "k3huf_internal.h"
 
 #include <algorithm>
 #include <cstring>
@@ -18,13 +19,10 @@ inline uint64_t rd(const uint8_t* p, int n) {
 inline void wr(uint8_t* p, uint64_t v, int n) {
     for (int i = 0; i < n; ++i, v >>= 8) p[i] = uint8_t(v);
 }
-inline uint64_t pad16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
-// planes and stripe records start on 256-byte boundaries (whole cache lines)
-inline uint64_t pad256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
-
-inline uint32_t stripes_for(uint64_t raw) {
-    return uint32_t((raw + K3HUF_STRIPE_BYTES - 1) / K3HUF_STRIPE_BYTES);
-}
+using k3huf_detail::pad16;
+using k3huf_detail::pad256;
+using k3huf_detail::stripes_for;
+using k3huf_detail::StripeGeom;
 
 int kraft_units(const uint8_t* len) {
     int k = 0;
@@ -67,6 +65,27 @@ void huffman_depths(const uint64_t* count, uint8_t* depth) {
         depth[s] = uint8_t(std::min(d, 255));
     }
 }
+
+int pick_threads(int n) {
+    if (n > 0) return n;
+    unsigned h = std::thread::hardware_concurrency();
+    return int(std::max(1u, std::min(h, 64u)));
+}
+
+template <class F>
+void parallel_for(int n, int threads, F f) {
+    threads = std::max(1, std::min(threads, n));
+    std::vector<std::thread> pool;
+    for (int t = 0; t < threads; ++t)
+        pool.emplace_back([=] {
+            for (int i = t; i < n; i += threads) f(i);
+        });
+    for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+namespace k3huf_detail {
 
 // Code lengths for the layer: Huffman depths, then the 12-bit limit (K3
 // page, "canonical code assignment and Kraft check": while the Kraft sum is
@@ -119,29 +138,55 @@ void canonical_codes(const uint8_t* len, uint32_t* code) {
     for (int s = 0; s < 256; ++s) code[s] = len[s] ? next[len[s]]++ : 0;
 }
 
-int pick_threads(int n) {
-    if (n > 0) return n;
-    unsigned h = std::thread::hardware_concurrency();
-    return int(std::max(1u, std::min(h, 64u)));
+uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len,
+                std::vector<StripeGeom>& g, uint32_t* nsb_total) {
+    const uint32_t ns = stripes_for(raw_bytes);
+    g.assign(ns, StripeGeom{});
+    uint64_t o = pad256(K3HUF_HDR_BYTES + 8ull * ns);
+    uint32_t nsb = 0;
+    for (uint32_t s = 0; s < ns; ++s) {
+        StripeGeom& G = g[s];
+        G.raw0 = uint64_t(s) * K3HUF_STRIPE_BYTES;
+        G.raw = uint32_t(std::min<uint64_t>(K3HUF_STRIPE_BYTES, raw_bytes - G.raw0));
+        G.n = G.raw / 2;
+        G.nsb = (G.n + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
+        uint64_t nbits = 0;
+        for (int v = 0; v < 256; ++v) nbits += hist[size_t(s) * 256 + v] * len[v];
+        G.nbits = uint32_t(nbits);
+        G.bit_bytes = uint32_t(pad16((nbits + 7) / 8));
+        G.bits_off = uint32_t(pad256(K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * G.nsb));
+        G.even_off = uint32_t(pad256(uint64_t(G.bits_off) + G.bit_bytes));
+        G.off = o;
+        o += pad256(uint64_t(G.even_off) + G.n);
+        nsb += G.nsb;
+    }
+    *nsb_total = nsb;
+    return o;
 }
 
-template <class F>
-void parallel_for(int n, int threads, F f) {
-    threads = std::max(1, std::min(threads, n));
-    std::vector<std::thread> pool;
-    for (int t = 0; t < threads; ++t)
-        pool.emplace_back([=] {
-            for (int i = t; i < n; i += threads) f(i);
-        });
-    for (auto& th : pool) th.join();
+void write_layer_header(uint8_t* out, uint64_t raw_bytes, const uint8_t* len,
+                        const std::vector<StripeGeom>& g, uint32_t nsb_total, uint64_t total) {
+    const uint32_t ns = uint32_t(g.size());
+    std::memset(out, 0, pad256(K3HUF_HDR_BYTES + 8ull * ns));
+    std::memcpy(out, "K3HF", 4);
+    wr(out + 4, 1, 2);
+    wr(out + 6, K3HUF_MAXLEN, 2);
+    wr(out + 8, K3HUF_STRIPE_BYTES, 4);
+    wr(out + 12, K3HUF_SUBBLOCK_BYTES, 4);
+    wr(out + 16, K3HUF_LANE_SYMS, 4);
+    wr(out + 20, ns, 4);
+    wr(out + 24, raw_bytes, 8);
+    wr(out + 32, nsb_total, 4);
+    wr(out + 36, 0, 4);
+    wr(out + 40, total, 8);
+    std::memcpy(out + 48, len, 256);
+    for (uint32_t s = 0; s < ns; ++s) wr(out + K3HUF_HDR_BYTES + 8ull * s, g[s].off, 8);
 }
 
-struct StripeGeom {
-    uint64_t raw0, off;       // first raw byte, record offset in the blob
-    uint32_t raw, n, nsb, nbits, bit_bytes, bits_off, even_off;
-};
+}  // namespace k3huf_detail
 
-}  // namespace
+using k3huf_detail::canonical_codes;
+using k3huf_detail::limited_lengths;
 
 extern "C" {
 
@@ -242,7 +287,6 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
         g[s].raw0 = uint64_t(s) * K3HUF_STRIPE_BYTES;
         g[s].raw = uint32_t(std::min<uint64_t>(K3HUF_STRIPE_BYTES, raw_bytes - g[s].raw0));
         g[s].n = g[s].raw / 2;
-        g[s].nsb = (g[s].n + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
     }
     parallel_for(int(ns), threads, [&](int s) {
         uint64_t h[4][256] = {};
@@ -264,35 +308,9 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
     canonical_codes(len, code);
 
     // layout: every stripe's size is known from its histogram
-    uint64_t o = pad256(K3HUF_HDR_BYTES + 8ull * ns);
     uint32_t nsb_total = 0;
-    for (uint32_t s = 0; s < ns; ++s) {
-        uint64_t nbits = 0;
-        for (int v = 0; v < 256; ++v) nbits += hist[size_t(s) * 256 + v] * len[v];
-        g[s].nbits = uint32_t(nbits);
-        g[s].bit_bytes = uint32_t(pad16((nbits + 7) / 8));
-        g[s].bits_off = uint32_t(pad256(K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * g[s].nsb));
-        g[s].even_off = uint32_t(pad256(uint64_t(g[s].bits_off) + g[s].bit_bytes));
-        g[s].off = o;
-        o += pad256(uint64_t(g[s].even_off) + g[s].n);
-        nsb_total += g[s].nsb;
-    }
-    const uint64_t total = o;
-
-    std::memset(out, 0, pad256(K3HUF_HDR_BYTES + 8ull * ns));
-    std::memcpy(out, "K3HF", 4);
-    wr(out + 4, 1, 2);
-    wr(out + 6, K3HUF_MAXLEN, 2);
-    wr(out + 8, K3HUF_STRIPE_BYTES, 4);
-    wr(out + 12, K3HUF_SUBBLOCK_BYTES, 4);
-    wr(out + 16, K3HUF_LANE_SYMS, 4);
-    wr(out + 20, ns, 4);
-    wr(out + 24, raw_bytes, 8);
-    wr(out + 32, nsb_total, 4);
-    wr(out + 36, 0, 4);
-    wr(out + 40, total, 8);
-    std::memcpy(out + 48, len, 256);
-    for (uint32_t s = 0; s < ns; ++s) wr(out + K3HUF_HDR_BYTES + 8ull * s, g[s].off, 8);
+    const uint64_t total = k3huf_detail::layout(raw_bytes, hist.data(), len, g, &nsb_total);
+    k3huf_detail::write_layer_header(out, raw_bytes, len, g, nsb_total, total);
 
     // stripes are independent (K3 page, "key design points"): pack in parallel
     parallel_for(int(ns), threads, [&](int s) {

@@ -22,7 +22,8 @@ DEV_HEADER, DEV_STRIPE, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 2, 4, 8, 16
 
 # names the C header declares, checked by the ABI test
 EXPORTS = ("k3huf_build_table", "k3huf_layer_info", "k3huf_decode_layer", "k3huf_decode_ring",
-           "k3huf_decode_ring_host", "k3huf_encode_bound", "k3huf_encode_layer", "k3huf_strerror")
+           "k3huf_decode_ring_host", "k3huf_encode_bound", "k3huf_encode_layer",
+           "k3huf_encode_work_bytes", "k3huf_encode_layer_dev", "k3huf_strerror")
 
 
 class K3HufError(RuntimeError):
@@ -80,6 +81,11 @@ def lib() -> ctypes.CDLL:
         L.k3huf_encode_bound.restype = ctypes.c_int64
         L.k3huf_encode_layer.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, ctypes.c_int]
         L.k3huf_encode_layer.restype = ctypes.c_int64
+        L.k3huf_encode_work_bytes.argtypes = [ctypes.c_uint64]
+        L.k3huf_encode_work_bytes.restype = ctypes.c_int64
+        L.k3huf_encode_layer_dev.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp,
+                                             ctypes.c_uint64, vp]
+        L.k3huf_encode_layer_dev.restype = ctypes.c_int64
         L.k3huf_strerror.argtypes = [ctypes.c_int]
         L.k3huf_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -142,6 +148,27 @@ def encode_layer(raw, n_threads: int = 0) -> np.ndarray:
     n = _check(lib().k3huf_encode_layer(r.ctypes.data, r.size, out.ctypes.data, cap, n_threads),
                "k3huf_encode_layer")
     return out[:n]
+
+
+def encode_work_bytes(raw_bytes: int) -> int:
+    return _check(lib().k3huf_encode_work_bytes(raw_bytes), "k3huf_encode_work_bytes")
+
+
+def encode_layer_dev(d_raw, d_out=None, d_work=None, stream=None):
+    """Pack the bf16 layer in device uint8 tensor ``d_raw`` on the GPU.
+    ``d_out`` (device uint8, at least encode_bound bytes) and ``d_work``
+    (device uint8, at least encode_work_bytes) are allocated when None.
+    Returns the container as a view of d_out (synchronous call)."""
+    import torch
+    n = d_raw.numel() * d_raw.element_size()
+    if d_out is None:
+        d_out = torch.empty(encode_bound(n), dtype=torch.uint8, device=d_raw.device)
+    if d_work is None:
+        d_work = torch.empty(encode_work_bytes(n), dtype=torch.uint8, device=d_raw.device)
+    size = _check(lib().k3huf_encode_layer_dev(d_raw.data_ptr(), n, d_out.data_ptr(), d_out.numel(),
+                                               d_work.data_ptr(), d_work.numel(),
+                                               _stream_handle(stream)), "k3huf_encode_layer_dev")
+    return d_out[:size]
 
 
 def _stream_handle(stream) -> int:

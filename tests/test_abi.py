@@ -163,3 +163,24 @@ def test_host_ring_rejects_bad_arguments_before_any_device_call():
     assert call(sl=(vp * 2)(None, 1 << 27)) == k3huf.E_ARG
     assert call(layers=(k3huf.HostLayer * 1)(k3huf.HostLayer(None, 4096, 1 << 21, 8192))) == k3huf.E_ARG
     assert call(layers=(k3huf.HostLayer * 1)(k3huf.HostLayer(1 << 20, 4096, None, 8192))) == k3huf.E_ARG
+
+
+def test_gpu_encoder_rejects_bad_arguments_before_any_device_call():
+    """k3huf_encode_layer_dev validates sizes, alignment and capacities on the
+    host before any HIP call (so this runs without a GPU)."""
+    L = k3huf.lib()
+    raw, out, work = 1 << 20, 1 << 24, 1 << 28     # 16-byte aligned fake addresses
+    n = 3 * 65536 + 514
+    cap, wb = k3huf.encode_bound(n), k3huf.encode_work_bytes(n)
+    assert L.k3huf_encode_work_bytes(3) == k3huf.E_ARG
+    assert L.k3huf_encode_work_bytes(0) == k3huf.E_ARG
+    f = L.k3huf_encode_layer_dev
+    assert f(None, n, out, cap, work, wb, None) == k3huf.E_ARG
+    assert f(raw, n, None, cap, work, wb, None) == k3huf.E_ARG
+    assert f(raw, n, out, cap, None, wb, None) == k3huf.E_ARG
+    assert f(raw, n + 1, out, cap, work, wb, None) == k3huf.E_ARG       # odd size
+    assert f(raw, 0, out, cap, work, wb, None) == k3huf.E_ARG
+    assert f(raw + 8, n, out, cap, work, wb, None) == k3huf.E_ARG       # misaligned input
+    assert f(raw, n, out + 4, cap, work, wb, None) == k3huf.E_ARG       # misaligned output
+    assert f(raw, n, out, cap - 1, work, wb, None) == k3huf.E_ARG       # output too small
+    assert f(raw, n, out, cap, work, wb - 1, None) == k3huf.E_ARG       # work too small

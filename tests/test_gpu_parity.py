@@ -14,19 +14,13 @@ import oracle as O
 from lossless_huffman_decoding_amd import k3huf, synth
 
 pytestmark = pytest.mark.gpu
+from oracle_cache import oracle_container
+
 DEV = "cuda:0"
-_cache = {}
 
 
 def say(*a):
     print("[gpu-case]", *a, flush=True)
-
-
-def oracle_container(name, gen):
-    if name not in _cache:
-        x = gen()
-        _cache[name] = (x, O.encode_layer(x))
-    return _cache[name]
 
 
 def to_dev(blob, lut):
