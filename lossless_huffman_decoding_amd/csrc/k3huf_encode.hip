@@ -12,12 +12,16 @@
 // host from the GPU's histograms (they are 256-entry problems); the byte work
 // runs in four kernels:
 //   enc_hist   per-stripe histograms of the odd bytes;
-//   enc_count  code bits of every 256-symbol lane chunk;
-//   enc_scan   per stripe: chunk start bits, the subblock records and the
-//              stripe record;
-//   enc_pack   one thread per lane chunk: its codes from its start bit (words
-//              it shares with a neighbour are OR-ed in atomically), and its
-//              even bytes.
+//   enc_count  code bits of every 256-symbol lane chunk, and of every
+//              subblock (128 chunks);
+//   enc_scan   per stripe: subblock start bits (the subblock records) and
+//              the stripe record;
+//   enc_pack   one wave per half subblock (64 lane chunks, one per lane): the
+//              lanes' start bits (a wave prefix sum), their lane bit counts,
+//              their codes packed into a per-wave LDS buffer (words two lanes
+//              share are OR-ed), then copied out with whole-wave stores (the
+//              unit's first and last words, which a neighbouring unit may
+//              share, are OR-ed into memory), and the even bytes.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -35,8 +39,13 @@ constexpr uint32_t kChunksPerStripe = (K3HUF_STRIPE_BYTES / 2) / K3HUF_LANE_SYMS
 constexpr int kHistThreads = 1024;
 constexpr int kHistCopies = 32;        // sub-histograms per block (lane mod 32)
 constexpr int kHistBlocksPerStripe = 64;
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 1024;     // = subblocks per stripe
 constexpr int kChunkThreads = 256;
+constexpr int kPackWaves = 4;       // waves (units) per packing block
+constexpr int kPackWords = 2048;       // per-wave LDS bit buffer (8 KiB)
+constexpr uint32_t kUnitChunks = 64;   // lane chunks per packing unit
+constexpr uint32_t kUnitsPerStripe = kChunksPerStripe / kUnitChunks;
+static_assert(kScanThreads == K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES, "one scan thread per subblock");
 
 // stripe geometry as the kernels read it
 struct StripeDev {
@@ -51,19 +60,42 @@ struct CodeTable {
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct WorkLayout {
-    uint64_t hist, geom, chunks, status, total;
+    uint64_t hist, geom, chunks, subblocks, status, total;
 };
 
+// work buffer: per-stripe histograms (u64), stripe geometry, lane-chunk bit
+// counts (u32), subblock bit counts then start bits (u32), a status word
 WorkLayout work_layout(uint64_t raw_bytes) {
     const uint64_t ns = k3huf_detail::stripes_for(raw_bytes);
     const uint64_t n_chunks = (raw_bytes / 2 + K3HUF_LANE_SYMS - 1) / K3HUF_LANE_SYMS;
+    const uint64_t n_sub = (raw_bytes + K3HUF_SUBBLOCK_BYTES - 1) / K3HUF_SUBBLOCK_BYTES;
     WorkLayout w;
     w.hist = 0;
     w.geom = align256(w.hist + 256 * 8 * ns);
     w.chunks = align256(w.geom + sizeof(StripeDev) * ns);
-    w.status = align256(w.chunks + 4 * n_chunks);
+    w.subblocks = align256(w.chunks + 4 * n_chunks);
+    w.status = align256(w.subblocks + 4 * n_sub);
     w.total = w.status + 256;
     return w;
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
 }
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) {
@@ -133,74 +165,72 @@ __global__ __launch_bounds__(kHistThreads) void enc_hist(const uint8_t* raw, uin
 }
 
 // Code bits of lane chunk c (symbols [256 c, min(256 c + 256, n))): one
-// thread per chunk.
+// thread per chunk. A block's 256 chunks are two whole subblocks (stripes
+// hold whole blocks); their sums go to sb_bits.
 __global__ __launch_bounds__(kChunkThreads) void enc_count(const uint8_t* raw, uint64_t raw_bytes,
                                                            uint64_t n_chunks, CodeTable ct,
-                                                           uint32_t* chunk) {
+                                                           uint32_t* chunk, uint32_t* sb_bits) {
     __shared__ uint8_t len[256];
+    __shared__ uint32_t wsum[kChunkThreads / 64];
     if (threadIdx.x < 256) len[threadIdx.x] = uint8_t(ct.e[threadIdx.x] >> 16);
     __syncthreads();
     const uint64_t c = uint64_t(blockIdx.x) * kChunkThreads + threadIdx.x;
-    if (c >= n_chunks) return;
-    const uint64_t b0 = c * 2 * K3HUF_LANE_SYMS;
-    const uint64_t b1 = min(b0 + 2 * K3HUF_LANE_SYMS, raw_bytes);
     uint32_t bits = 0;
-    if (b1 - b0 == 2 * K3HUF_LANE_SYMS) {
-        const uint4* p = reinterpret_cast<const uint4*>(raw + b0);
+    if (c < n_chunks) {
+        const uint64_t b0 = c * 2 * K3HUF_LANE_SYMS;
+        const uint64_t b1 = min(b0 + 2 * K3HUF_LANE_SYMS, raw_bytes);
+        if (b1 - b0 == 2 * K3HUF_LANE_SYMS) {
+            const uint4* p = reinterpret_cast<const uint4*>(raw + b0);
 #pragma unroll 4
-        for (int i = 0; i < 32; ++i) {
-            const uint4 v = p[i];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int i = 0; i < 32; ++i) {
+                const uint4 v = p[i];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) bits += len[(w[k] >> 8) & 0xFFu] + len[w[k] >> 24];
+                for (int k = 0; k < 4; ++k) bits += len[(w[k] >> 8) & 0xFFu] + len[w[k] >> 24];
+            }
+        } else {
+            for (uint64_t i = b0; i < b1; i += 2) bits += len[raw[i + 1]];
         }
-    } else {
-        for (uint64_t i = b0; i < b1; i += 2) bits += len[raw[i + 1]];
+        chunk[c] = bits;
     }
-    chunk[c] = bits;
+    const uint32_t ws = wave_sum(bits);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ws;
+    __syncthreads();
+    if (threadIdx.x < 2) {
+        const uint64_t sb = uint64_t(blockIdx.x) * 2 + threadIdx.x;
+        if (sb * K3HUF_LANES < n_chunks) sb_bits[sb] = wsum[2 * threadIdx.x] + wsum[2 * threadIdx.x + 1];
+    }
 }
 
-// Per stripe (one block each): exclusive prefix of the chunk bit counts.
-// Writes the stripe record, the subblock records (start bit, symbol count,
-// lane bit counts) and replaces chunk[] with stripe-relative start bits. A
+// Per stripe (one block, thread j = subblock j): exclusive prefix of the
+// subblock bit counts. Writes each subblock record's start bit and symbol
+// count, the stripe record, and replaces sb_bits[] with the start bits. A
 // total that differs from the host's count (the input changed during the
 // call) sets *status.
 __global__ __launch_bounds__(kScanThreads) void enc_scan(uint8_t* out, const StripeDev* g,
-                                                         uint32_t* chunk, uint32_t* status) {
+                                                         uint32_t* sb_bits, uint32_t* status) {
     __shared__ uint32_t part[kScanThreads];
-    const uint32_t s = blockIdx.x;
+    const uint32_t s = blockIdx.x, j = threadIdx.x;
     const StripeDev G = g[s];
-    const uint32_t nc = (G.n + K3HUF_LANE_SYMS - 1) / K3HUF_LANE_SYMS;
-    uint32_t* cb = chunk + uint64_t(s) * kChunksPerStripe;
-    const uint32_t per = (nc + kScanThreads - 1) / kScanThreads;
-    const uint32_t j0 = min(threadIdx.x * per, nc), j1 = min(j0 + per, nc);
-    uint32_t sum = 0;
-    for (uint32_t j = j0; j < j1; ++j) sum += cb[j];
-    part[threadIdx.x] = sum;
+    uint32_t* sb = sb_bits + uint64_t(s) * kScanThreads;
+    const uint32_t v = j < G.nsb ? sb[j] : 0u;
+    part[j] = v;
     __syncthreads();
-    // inclusive scan of the per-thread sums (Hillis-Steele in LDS)
     for (int d = 1; d < kScanThreads; d <<= 1) {
-        const uint32_t v = threadIdx.x >= uint32_t(d) ? part[threadIdx.x - d] : 0u;
+        const uint32_t t = j >= uint32_t(d) ? part[j - d] : 0u;
         __syncthreads();
-        part[threadIdx.x] += v;
+        part[j] += t;
         __syncthreads();
     }
-    uint32_t pos = part[threadIdx.x] - sum;
-    uint8_t* recs = out + G.off + K3HUF_STRIPE_HDR_BYTES;
-    for (uint32_t j = j0; j < j1; ++j) {
-        const uint32_t bits = cb[j];
-        const uint32_t b = j / K3HUF_LANES, t = j % K3HUF_LANES;
-        uint8_t* rec = recs + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * b;
-        *reinterpret_cast<uint16_t*>(rec + 8 + 2 * t) = uint16_t(bits);
-        if (t == 0) {
-            *reinterpret_cast<uint32_t*>(rec) = pos;
-            *reinterpret_cast<uint32_t*>(rec + 4) = min(uint32_t(K3HUF_SUBBLOCK_SYMS), G.n - b * K3HUF_SUBBLOCK_SYMS);
-        }
-        cb[j] = pos;
-        pos += bits;
+    const uint32_t start = part[j] - v;
+    if (j < G.nsb) {
+        uint8_t* rec = out + G.off + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * j;
+        reinterpret_cast<uint32_t*>(rec)[0] = start;
+        reinterpret_cast<uint32_t*>(rec)[1] = min(uint32_t(K3HUF_SUBBLOCK_SYMS), G.n - j * K3HUF_SUBBLOCK_SYMS);
+        sb[j] = start;
     }
-    if (threadIdx.x == kScanThreads - 1) {
-        if (part[kScanThreads - 1] != G.nbits) atomicOr(status, 1u);
+    if (j == kScanThreads - 1) {
+        if (part[j] != G.nbits) atomicOr(status, 1u);
         uint32_t* hd = reinterpret_cast<uint32_t*>(out + G.off);
         hd[0] = G.raw;
         hd[1] = G.n;
@@ -213,70 +243,183 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan(uint8_t* out, const Str
     }
 }
 
-// One thread per lane chunk: its codes, MSB first, from its start bit, and
-// its even bytes. Words wholly inside the chunk's bit range are stored;
-// its first and last words may hold a neighbour's bits and are OR-ed in
-// (enc_zero_stripes cleared them).
-__global__ __launch_bounds__(kChunkThreads) void enc_pack(const uint8_t* raw, uint64_t raw_bytes,
-                                                          uint64_t n_chunks, CodeTable ct,
-                                                          const StripeDev* g, const uint32_t* chunk,
-                                                          uint8_t* out) {
+// One wave per unit of 64 lane chunks (half a subblock), lane t packing
+// chunk t, in two phases of 128 symbols per chunk:
+//   A. whole-wave loads of the phase's raw bytes (16 lanes cover the 256
+//      bytes of one chunk's half); the odd bytes go to the chunk's LDS row,
+//      the even bytes straight to the even plane (16 lanes write one line);
+//   B. each lane appends its row's codes, MSB first, to the unit's words in
+//      the wave's LDS bit buffer (a lane's first and last words may be
+//      shared with its neighbours and are OR-ed in; the words between are its
+//      own).
+// Then the buffer is written out with whole-wave stores; the unit's first and
+// last words may hold a neighbouring unit's bits and are OR-ed into memory
+// (enc_zero_stripes cleared them). A unit whose codes exceed the buffer packs
+// straight into memory with the same rule per lane. The layer's last unit,
+// which may end inside a chunk, stages its rows symbol by symbol.
+constexpr int kRowBytes = 132;          // 128 odd bytes + 4: rows start in distinct LDS banks
+constexpr int kHalfSyms = K3HUF_LANE_SYMS / 2;
+
+__global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, uint64_t raw_bytes,
+                                                            uint64_t n_chunks, CodeTable ct,
+                                                            const StripeDev* g, const uint32_t* chunk,
+                                                            const uint32_t* sb_start, uint8_t* out) {
     __shared__ uint32_t tab[256];
+    __shared__ uint32_t stage[kPackWaves][kPackWords];
+    __shared__ __attribute__((aligned(16))) uint8_t rows[kPackWaves][64 * kRowBytes];
     if (threadIdx.x < 256) tab[threadIdx.x] = ct.e[threadIdx.x];
     __syncthreads();
-    const uint64_t c = uint64_t(blockIdx.x) * kChunkThreads + threadIdx.x;
-    if (c >= n_chunks) return;
-    const uint32_t s = uint32_t(c / kChunksPerStripe);
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t u = uint64_t(blockIdx.x) * kPackWaves + wave;   // unit
+    const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
+    if (u >= n_units) return;
+    const uint32_t s = uint32_t(u / kUnitsPerStripe);
     const StripeDev G = g[s];
+    const uint64_t sbg = u / 2;                         // global subblock
+    const uint32_t half = uint32_t(u & 1);
+    const uint32_t sbl = uint32_t(sbg % kScanThreads);  // subblock within the stripe
+    // bit counts of both halves of the subblock: this unit starts after the
+    // first half when it is the second
+    const uint64_t ca = sbg * K3HUF_LANES + lane, cb = ca + kUnitChunks;
+    const uint32_t ba = ca < n_chunks ? chunk[ca] : 0u, bb = cb < n_chunks ? chunk[cb] : 0u;
+    const uint32_t ia = wave_incl_scan(ba, lane), ib = wave_incl_scan(bb, lane);
+    const uint32_t bits = half ? bb : ba, incl = half ? ib : ia;
+    const uint32_t u0 = sb_start[sbg] + (half ? __shfl(ia, 63) : 0u);
+    const uint32_t u1 = u0 + __shfl(incl, 63);
+    const uint64_t c0 = u * kUnitChunks;                // first chunk of the unit
+    const uint64_t c = c0 + lane;
+    const bool has = c < n_chunks;
+    uint8_t* rec = out + G.off + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * sbl;
+    if (has) reinterpret_cast<uint16_t*>(rec + 8)[half * kUnitChunks + lane] = uint16_t(bits);
+
     uint32_t* words = reinterpret_cast<uint32_t*>(out + G.off + G.bits_off);
-    const uint32_t local = uint32_t(c % kChunksPerStripe) * K3HUF_LANE_SYMS;   // stripe symbol index
-    uint8_t* even = out + G.off + G.even_off + local;
-    const uint32_t b0 = chunk[c];
+    uint32_t* buf = stage[wave];
+    uint8_t* row = rows[wave];
+    const uint32_t w0 = u0 >> 5, nw = ((u1 + 31) >> 5) - w0;
+    const bool staged = __builtin_amdgcn_readfirstlane(nw) <= uint32_t(kPackWords);   // uniform
+    if (staged)
+        for (uint32_t i = lane; i < nw; i += 64) buf[i] = 0u;
+    // the unit's raw bytes, symbols and even plane (stripe symbol index)
+    const uint8_t* uraw = raw + c0 * 2 * K3HUF_LANE_SYMS;
+    const uint64_t n_syms = raw_bytes / 2;
+    const bool tail = (c0 + kUnitChunks) * K3HUF_LANE_SYMS > n_syms;   // layer's last unit, partial
+    uint8_t* ueven = out + G.off + G.even_off + uint32_t(c0 % kChunksPerStripe) * K3HUF_LANE_SYMS;
+    const int cnt = has ? int(min(uint64_t(K3HUF_LANE_SYMS), n_syms - c * K3HUF_LANE_SYMS)) : 0;
+
+    const uint32_t b0 = u0 + incl - bits;
     uint32_t w = b0 >> 5;
     uint64_t acc = 0;            // pending bits, the earliest at bit 63
-    uint32_t nacc = b0 & 31u;    // bits of word w before acc's top are a neighbour's (zero here)
+    uint32_t nacc = b0 & 31u;    // word w's bits before acc's top belong to the previous lane
     bool first = true;
+    // word w of the stripe's bitstream (bit 31 = earliest); shared words are OR-ed
+    auto emit = [&](uint32_t v, bool shared) {
+        if (staged) {
+            if (shared)
+                atomicOr(&buf[w - w0], v);
+            else
+                buf[w - w0] = v;
+        } else {
+            if (shared)
+                atomicOr(&words[w], bswap32(v));
+            else
+                words[w] = bswap32(v);
+        }
+    };
+    // two symbols into the staged buffer without branches: their codes (at
+    // most 24 bits) complete at most one word, which is OR-ed in; when none
+    // completes, zero is OR-ed into the word being filled (a no-op)
+    auto put2 = [&](uint32_t s0, uint32_t s1) {
+        const uint32_t e0 = tab[s0], e1 = tab[s1];
+        const uint32_t l1 = e1 >> 16, l = (e0 >> 16) + l1;
+        const uint32_t code = ((e0 & 0xFFFFu) << l1) | (e1 & 0xFFFFu);
+        acc |= uint64_t(code) << (64u - nacc - l);
+        nacc += l;
+        const bool full = nacc >= 32;
+        atomicOr(&buf[w - w0], full ? uint32_t(acc >> 32) : 0u);
+        w += full ? 1u : 0u;
+        acc = full ? acc << 32 : acc;
+        nacc -= full ? 32u : 0u;
+    };
     auto put = [&](uint32_t sym) {
         const uint32_t e = tab[sym];
         const uint32_t l = e >> 16;
         acc |= uint64_t(e & 0xFFFFu) << (64u - nacc - l);
         nacc += l;
         if (nacc >= 32) {
-            const uint32_t v = bswap32(uint32_t(acc >> 32));
-            if (first)
-                atomicOr(&words[w], v);
-            else
-                words[w] = v;
+            emit(uint32_t(acc >> 32), first);
             first = false;
             ++w;
             acc <<= 32;
             nacc -= 32;
         }
     };
-    const uint64_t r0 = c * 2 * K3HUF_LANE_SYMS;
-    const uint64_t r1 = min(r0 + 2 * K3HUF_LANE_SYMS, raw_bytes);
-    if (r1 - r0 == 2 * K3HUF_LANE_SYMS) {
-        const uint4* p = reinterpret_cast<const uint4*>(raw + r0);
-        for (int i = 0; i < 32; ++i) {
-            const uint4 v = p[i];
-            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                put((q[k] >> 8) & 0xFFu);
-                put(q[k] >> 24);
+
+#pragma unroll 1
+    for (int ph = 0; ph < 2; ++ph) {
+        // A. stage this phase's odd bytes, write its even bytes
+        if (!tail) {
+            const int q = lane & 15, sub = lane >> 4;   // 16 lanes per chunk half
+#pragma unroll 4
+            for (int i = 0; i < 16; ++i) {
+                const int ch = i * 4 + sub;
+                const uint4 v = *reinterpret_cast<const uint4*>(uraw + uint64_t(ch) * 512 + ph * 256 + q * 16);
+                const uint32_t o0 = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
+                const uint32_t o1 = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
+                uint32_t* r = reinterpret_cast<uint32_t*>(row + ch * kRowBytes + q * 8);
+                r[0] = o0;
+                r[1] = o1;
+                *reinterpret_cast<uint2*>(ueven + ch * K3HUF_LANE_SYMS + ph * kHalfSyms + q * 8) =
+                    make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
+                               __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
             }
-            // even bytes: bytes 0, 2 of each dword
-            const uint2 ev = make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
-                                        __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
-            *reinterpret_cast<uint2*>(even + 8 * i) = ev;
+        } else {
+            for (int j = ph * kHalfSyms; j < min(cnt, (ph + 1) * kHalfSyms); ++j) {
+                const uint8_t* p = uraw + uint64_t(lane) * 512 + 2 * j;
+                row[lane * kRowBytes + (j - ph * kHalfSyms)] = p[1];
+                ueven[lane * K3HUF_LANE_SYMS + j] = p[0];
+            }
         }
-    } else {
-        for (uint64_t i = r0; i < r1; i += 2) {
-            put(raw[i + 1]);
-            even[(i - r0) / 2] = raw[i];
+        wave_sync();
+        // B. this phase's codes
+        if (has) {
+            const int m = min(max(cnt - ph * kHalfSyms, 0), kHalfSyms);
+            const uint32_t* r = reinterpret_cast<const uint32_t*>(row + lane * kRowBytes);
+            if (m == kHalfSyms && staged) {
+#pragma unroll 4
+                for (int k = 0; k < kHalfSyms / 4; ++k) {
+                    const uint32_t v = r[k];
+                    put2(v & 0xFFu, (v >> 8) & 0xFFu);
+                    put2((v >> 16) & 0xFFu, v >> 24);
+                }
+            } else if (m == kHalfSyms) {
+#pragma unroll 2
+                for (int k = 0; k < kHalfSyms / 4; ++k) {
+                    const uint32_t v = r[k];
+                    put(v & 0xFFu);
+                    put((v >> 8) & 0xFFu);
+                    put((v >> 16) & 0xFFu);
+                    put(v >> 24);
+                }
+            } else {
+                const uint8_t* rb = row + lane * kRowBytes;
+                for (int k = 0; k < m; ++k) put(rb[k]);
+            }
+        }
+        wave_sync();
+    }
+    if (has && nacc > 0) emit(uint32_t(acc >> 32), true);
+    wave_sync();
+    if (staged) {
+        for (uint32_t i = lane; i < nw; i += 64) {
+            const uint32_t v = bswap32(buf[i]);
+            const bool edge = (i == 0 && (u0 & 31u)) || (i == nw - 1 && (u1 & 31u));
+            if (edge)
+                atomicOr(&words[w0 + i], v);
+            else
+                words[w0 + i] = v;
         }
     }
-    if (nacc > 0) atomicOr(&words[w], bswap32(uint32_t(acc >> 32)));
 }
 
 // a kernel launch's status as a return code
@@ -310,6 +453,7 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     auto* hist = reinterpret_cast<unsigned long long*>(work + wl.hist);
     auto* geom = reinterpret_cast<StripeDev*>(work + wl.geom);
     auto* chunk = reinterpret_cast<uint32_t*>(work + wl.chunks);
+    auto* sb_bits = reinterpret_cast<uint32_t*>(work + wl.subblocks);
     auto* status = reinterpret_cast<uint32_t*>(work + wl.status);
 
     // 1. per-stripe histograms (the status word is cleared with them)
@@ -352,10 +496,12 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     hipLaunchKernelGGL(enc_zero_stripes, dim3(64, ns), dim3(256), 0, st, out, geom);
     const unsigned chunk_blocks = unsigned((n_chunks + kChunkThreads - 1) / kChunkThreads);
     hipLaunchKernelGGL(enc_count, dim3(chunk_blocks), dim3(kChunkThreads), 0, st, raw, raw_bytes,
-                       n_chunks, ct, chunk);
-    hipLaunchKernelGGL(enc_scan, dim3(ns), dim3(kScanThreads), 0, st, out, geom, chunk, status);
-    hipLaunchKernelGGL(enc_pack, dim3(chunk_blocks), dim3(kChunkThreads), 0, st, raw, raw_bytes,
-                       n_chunks, ct, geom, chunk, out);
+                       n_chunks, ct, chunk, sb_bits);
+    hipLaunchKernelGGL(enc_scan, dim3(ns), dim3(kScanThreads), 0, st, out, geom, sb_bits, status);
+    const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
+    hipLaunchKernelGGL(enc_pack, dim3(unsigned((n_units + kPackWaves - 1) / kPackWaves)),
+                       dim3(kPackWaves * 64), 0, st, raw, raw_bytes, n_chunks, ct, geom, chunk, sb_bits,
+                       out);
     if (launched()) return K3HUF_E_HIP;
     uint32_t bad = 0;
     if (hipMemcpyAsync(&bad, status, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
