@@ -193,3 +193,11 @@ def small_random(seed: int, n_bytes: int, sigma: float = 0.02) -> np.ndarray:
     if n_bytes % 2:
         raise ValueError("bf16 layer needs an even byte count")
     return f64_to_bf16_bytes(rng.standard_normal(n_bytes // 2) * sigma)
+
+
+def small_trunk_matrix(seed: int, rows: int, cols: int) -> np.ndarray:
+    """One rows x cols bf16 weight drawn like a trunk matrix: N(0, s) with s
+    log-uniform in [0.005, 0.05], both from default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    s = math.exp(rng.uniform(math.log(0.005), math.log(0.05)))
+    return f64_to_bf16_bytes(rng.standard_normal(rows * cols) * s)

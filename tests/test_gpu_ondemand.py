@@ -1,0 +1,140 @@
+"""Decode-on-demand of module weights (ECF8 page, section 2.2: one buffer the
+size of the largest layer, filled by a forward pre-hook before each layer).
+
+The decoded weights are the original bf16 bytes, so a forward pass through
+the hooked modules must equal the dense forward pass bit for bit. Every case
+prints its name before touching the GPU.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from lossless_huffman_decoding_amd import k3huf, synth
+from lossless_huffman_decoding_amd.ondemand import OnDemandWeights
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+def _trunk_like(rows, cols, seed):
+    """A bf16 weight drawn like a trunk matrix (N(0, s), s log-uniform in
+    [0.005, 0.05]); the generator lives in synth."""
+    raw = synth.small_trunk_matrix(seed, rows, cols)
+    return torch.from_numpy(raw).view(torch.bfloat16).view(rows, cols)
+
+
+def _stack(shapes, seed):
+    layers = []
+    for k, (o, i) in enumerate(shapes):
+        lin = torch.nn.Linear(i, o, bias=(k % 2 == 0), dtype=torch.bfloat16, device=DEV)
+        with torch.no_grad():
+            lin.weight.copy_(_trunk_like(o, i, seed + k).to(DEV))
+        layers.append(lin)
+    return torch.nn.Sequential(*layers)
+
+
+@pytest.mark.parametrize("batch,lookahead,n_layers", [(1, False, 4), (7, False, 4), (1, True, 4),
+                                                      (7, True, 3), (2, True, 1)])
+def test_on_demand_forward_equals_dense(batch, lookahead, n_layers):
+    shapes = [(1024, 512), (768, 1024), (1536, 768), (512, 1536)][:n_layers]
+    if n_layers < 4:
+        shapes[-1] = (512, shapes[-1][1])   # the stack still maps 512 -> 512
+    model = _stack(shapes, 600)
+    x = torch.randn(batch, 512, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    dense = [m.weight.detach().clone() for m in model]
+    say("ondemand dense forward", batch)
+    with torch.no_grad():
+        want = model(x)
+        dense_first = model[0](x)
+    od = OnDemandWeights(DEV, lookahead=lookahead)
+    for m in model:
+        od.attach(m)
+    assert od.buffer_bytes == max(o * i for o, i in shapes) * 2 * (2 if lookahead else 1)
+    assert od.resident_bytes < sum(o * i for o, i in shapes) * 2
+    say("ondemand hooked forward", batch, lookahead, n_layers)
+    with torch.no_grad():
+        got = model(x)
+        got2 = model(x)             # buffers reused across passes
+        got3 = model[0](x)          # a module out of order
+    od.check()
+    assert torch.equal(got, want) and torch.equal(got2, want)
+    assert torch.equal(got3, dense_first)
+    assert torch.equal(model[0].weight, dense[0])
+
+
+@pytest.mark.parametrize("lookahead", [False, True])
+def test_on_demand_on_a_side_stream(lookahead):
+    model = _stack([(640, 320), (320, 640)], 700)
+    x = torch.randn(3, 320, generator=torch.Generator().manual_seed(6)).to(torch.bfloat16).to(DEV)
+    with torch.no_grad():
+        want = model(x)
+    od = OnDemandWeights(DEV, lookahead=lookahead)
+    for m in model:
+        od.attach(m)
+    s = torch.cuda.Stream()
+    say("ondemand side stream", lookahead)
+    with torch.cuda.stream(s), torch.no_grad():
+        got = model(x)
+    od.check()
+    assert torch.equal(got, want)
+
+
+def test_on_demand_forward_captured_in_a_graph():
+    """The hooked forward (one buffer, decodes on the capturing stream)
+    captured once and replayed: every replay equals the dense forward, with
+    eager work and synchronizations between replays."""
+    model = _stack([(1024, 512), (768, 1024), (512, 768)], 800)
+    x = torch.randn(4, 512, generator=torch.Generator().manual_seed(8)).to(torch.bfloat16).to(DEV)
+    with torch.no_grad():
+        want = model(x)
+    od = OnDemandWeights(DEV, lookahead=False)
+    for m in model:
+        od.attach(m)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    say("ondemand graph capture")
+    with torch.cuda.stream(s), torch.no_grad():
+        model(x)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g), torch.no_grad():
+        out = model(x)
+    for r in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), r
+        with torch.no_grad():
+            eager = model(x)        # eager decodes between replays
+        torch.cuda.synchronize()
+        assert torch.equal(eager, want), r
+    od.check()
+
+
+@pytest.mark.parametrize("lookahead", [False, True])
+def test_on_demand_groups(lookahead):
+    """Modules packed in groups (one container per group, as a trunk layer
+    packs all its tensors with one table): three groups of mixed sizes, run
+    twice; every output equals the dense forward."""
+    shapes = [(640, 512), (512, 640), (768, 512), (512, 768), (1024, 512), (512, 1024), (512, 512)]
+    model = _stack(shapes, 1000)
+    x = torch.randn(5, 512, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).to(DEV)
+    with torch.no_grad():
+        want = model(x)
+    od = OnDemandWeights(DEV, lookahead=lookahead)
+    groups = [[model[0], model[1]], [model[2], model[3], model[4]], [model[5], model[6]]]
+    for grp in groups:
+        od.attach_group(grp)
+    biggest = max(sum(m.in_features * m.out_features * 2 for m in grp) for grp in groups)
+    assert od.buffer_bytes == biggest * (2 if lookahead else 1)
+    say("ondemand groups", lookahead)
+    with torch.no_grad():
+        a = model(x)
+        b = model(x)
+    od.check()
+    assert torch.equal(a, want) and torch.equal(b, want)
