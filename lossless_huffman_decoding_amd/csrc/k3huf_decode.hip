@@ -516,6 +516,10 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     uint32_t ticket = 0;           // lane 0: the answer to this unit's request
 
     while (h < n_units) {
+        // the last two rounds of units are the grid's critical path: their
+        // waves issue ahead of waves still busy with earlier units
+        if (h + 2 * T >= n_units) __builtin_amdgcn_s_setprio(1);
+        if (h + T >= n_units) __builtin_amdgcn_s_setprio(3);
         // the next unit: static, or handed out now (the answer is read
         // halfway through this unit)
         const bool ask = round + 1 >= stat;
