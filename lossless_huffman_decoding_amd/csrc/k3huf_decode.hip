@@ -16,8 +16,9 @@
 // loads and the output stores of a wave cover whole 128-byte lines.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
+#include <map>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "k3huf.h"
@@ -87,11 +88,15 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // counter. A wave asks for its next unit when it starts the current one and
 // reads the answer halfway through it, so it holds at most one unit ahead;
 // waves that run faster take more units and the grid ends close together.
-// Launches in flight use different counter slots (the host cycles through
-// kSchedSlots); the last workgroup of a launch clears its slot. The
-// counters live in this array, which exists once per device for the life of
-// the process; at most kSchedSlots decodes may run at the same time on a
-// device.
+// The counters live in this array, which exists once per device for the
+// life of the process, in kSchedSlots slots; the last workgroup of a launch
+// clears its slot. Each stream gets a slot of its own on first use: launches
+// on one stream never overlap, so they can share one, and launches on
+// different streams get different slots for the first kSchedSlots streams
+// of a device. Two launches that run at the same time on one slot would
+// take each other's tickets (units left undecoded); that needs more than
+// kSchedSlots streams, or a graph replay overlapping a decode on the stream
+// the graph was captured on.
 constexpr uint32_t kDynRounds = 3;
 constexpr uint32_t kSchedSlots = 256;
 constexpr uint32_t kGroupsPerSlot = 8;
@@ -642,12 +647,19 @@ struct DevInfo {
 
 std::mutex g_mu;
 std::vector<DevInfo> g_dev;
-std::atomic<uint32_t> g_launches{0};
+std::map<std::pair<int, void*>, uint32_t> g_stream_slot;   // (device, stream) -> counter slot
+std::vector<uint32_t> g_next_slot;                        // per device
 
-int device_info(DevInfo* out) {
+// The device's launch geometry and the counter slot of `stream` on it.
+int device_info(void* stream, DevInfo* out, uint32_t* slot) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return K3HUF_E_HIP;
     std::lock_guard<std::mutex> lk(g_mu);
+    if (int(g_next_slot.size()) <= dev) g_next_slot.resize(dev + 1, 0u);
+    auto it = g_stream_slot.find({dev, stream});
+    if (it == g_stream_slot.end())
+        it = g_stream_slot.emplace(std::make_pair(dev, stream), g_next_slot[dev]++ % kSchedSlots).first;
+    *slot = it->second;
     if (int(g_dev.size()) <= dev) g_dev.resize(dev + 1);
     DevInfo& d = g_dev[dev];
     if (!d.cus) {
@@ -681,7 +693,8 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
         uint64_t(blob_bytes) >= (1ull << 36))
         return K3HUF_E_ARG;
     DevInfo di;
-    int rc = device_info(&di);
+    uint32_t slot = 0;
+    int rc = device_info(stream, &di, &slot);
     if (rc) return rc;
     DecodeArgs a;
     a.blob = static_cast<const uint8_t*>(d_blob);
@@ -692,7 +705,7 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     a.n_sub = uint32_t(n_sub);
     a.n_stripes = uint32_t(n_stripes);
     a.status = d_status;
-    a.slot = g_launches.fetch_add(1, std::memory_order_relaxed) % kSchedSlots;
+    a.slot = slot;
     const uint64_t want = (n_sub * kUnitsPerSub + kWaves - 1) / kWaves;
     const uint64_t resident = uint64_t(di.cus) * uint64_t(di.wg_per_cu);
     const unsigned grid = unsigned(want < resident ? want : resident);

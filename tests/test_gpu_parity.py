@@ -306,3 +306,22 @@ def test_host_ring_repeated_containers_and_pageable_memory():
     assert int(status.item()) == 0
     for k, r in enumerate(results):
         assert (r.cpu().numpy() == x).all(), k
+
+
+def test_concurrent_decodes_on_many_streams():
+    """Decodes queued on six streams at once (three layers each, every
+    stream with its own work-counter slot) all give their layers back."""
+    sizes = [2 * 65536 + 10, 5 * 65536 + 4, 3 * 65536 + 514]
+    xs = [synth.small_random(500 + k, sizes[k % 3]) for k in range(18)]
+    blobs = [O.encode_layer(x) for x in xs]
+    dev = [to_dev(b, k3huf.build_table(k3huf.layer_info(b)["codelen"])) for b in blobs]
+    outs = [torch.full((x.size,), 0xA5, dtype=torch.uint8, device=DEV) for x in xs]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    streams = [torch.cuda.Stream() for _ in range(6)]
+    say("concurrent streams", len(streams), len(xs))
+    for k, (db, dl) in enumerate(dev):
+        k3huf.decode_layer(db, dl, outs[k], status, streams[k % 6])
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for k, x in enumerate(xs):
+        assert (outs[k].cpu().numpy() == x).all(), k
