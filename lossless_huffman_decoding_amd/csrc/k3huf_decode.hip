@@ -1,5 +1,6 @@
 // gfx950 decode path of the k3huf library: the decode kernel, its launcher
-// and the layer-ring driver. Container layout: include/k3huf.h.
+// and the layer-ring drivers (device-resident and host-fed containers).
+// Container layout: include/k3huf.h.
 //
 // What is computed (K3 page = "Kimi K3 纯 CPU 推理中的无损 Trunk 压缩…",
 // yfxerp.com/news/153994):
