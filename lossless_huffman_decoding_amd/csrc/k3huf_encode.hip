@@ -164,9 +164,13 @@ __global__ __launch_bounds__(kHistThreads) void enc_hist(const uint8_t* raw, uin
     }
 }
 
-// Code bits of lane chunk c (symbols [256 c, min(256 c + 256, n))): one
-// thread per chunk. A block's 256 chunks are two whole subblocks (stripes
-// hold whole blocks); their sums go to sb_bits.
+// Code bits of lane chunk c (symbols [256 c, min(256 c + 256, n))). A block's
+// 256 chunks are two whole subblocks (stripes hold whole blocks); their sums
+// go to sb_bits. Each wave counts 64 chunks (32 KiB of raw bytes) with
+// whole-wave loads: load i covers chunks 2i (lanes 0-31) and 2i + 1 (lanes
+// 32-63); each half's sum is reduced across its lanes and kept by the lane
+// that owns the chunk. The layer's last wave, whose chunks may be partial or
+// missing, reads its own chunk per lane instead.
 __global__ __launch_bounds__(kChunkThreads) void enc_count(const uint8_t* raw, uint64_t raw_bytes,
                                                            uint64_t n_chunks, CodeTable ct,
                                                            uint32_t* chunk, uint32_t* sb_bits) {
@@ -174,27 +178,33 @@ __global__ __launch_bounds__(kChunkThreads) void enc_count(const uint8_t* raw, u
     __shared__ uint32_t wsum[kChunkThreads / 64];
     if (threadIdx.x < 256) len[threadIdx.x] = uint8_t(ct.e[threadIdx.x] >> 16);
     __syncthreads();
-    const uint64_t c = uint64_t(blockIdx.x) * kChunkThreads + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const uint64_t c0 = uint64_t(blockIdx.x) * kChunkThreads + (threadIdx.x & ~63u);   // wave's first chunk
+    const uint64_t c = c0 + lane;
     uint32_t bits = 0;
-    if (c < n_chunks) {
+    if ((c0 + 64) * 2 * K3HUF_LANE_SYMS <= raw_bytes) {
+        const uint4* p = reinterpret_cast<const uint4*>(raw + c0 * 2 * K3HUF_LANE_SYMS);
+#pragma unroll 4
+        for (int i = 0; i < 32; ++i) {
+            const uint4 v = p[i * 64 + lane];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t b = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) b += len[(w[k] >> 8) & 0xFFu] + len[w[k] >> 24];
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) b += __shfl_xor(b, o);
+            const uint32_t lo = __builtin_amdgcn_readlane(b, 0), hi = __builtin_amdgcn_readlane(b, 32);
+            bits = lane == 2 * i ? lo : (lane == 2 * i + 1 ? hi : bits);
+        }
+        chunk[c] = bits;
+    } else if (c < n_chunks) {
         const uint64_t b0 = c * 2 * K3HUF_LANE_SYMS;
         const uint64_t b1 = min(b0 + 2 * K3HUF_LANE_SYMS, raw_bytes);
-        if (b1 - b0 == 2 * K3HUF_LANE_SYMS) {
-            const uint4* p = reinterpret_cast<const uint4*>(raw + b0);
-#pragma unroll 4
-            for (int i = 0; i < 32; ++i) {
-                const uint4 v = p[i];
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) bits += len[(w[k] >> 8) & 0xFFu] + len[w[k] >> 24];
-            }
-        } else {
-            for (uint64_t i = b0; i < b1; i += 2) bits += len[raw[i + 1]];
-        }
+        for (uint64_t i = b0; i < b1; i += 2) bits += len[raw[i + 1]];
         chunk[c] = bits;
     }
     const uint32_t ws = wave_sum(bits);
-    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ws;
+    if (lane == 0) wsum[threadIdx.x >> 6] = ws;
     __syncthreads();
     if (threadIdx.x < 2) {
         const uint64_t sb = uint64_t(blockIdx.x) * 2 + threadIdx.x;
@@ -244,10 +254,11 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan(uint8_t* out, const Str
 }
 
 // One wave per unit of 64 lane chunks (half a subblock), lane t packing
-// chunk t, in two phases of 128 symbols per chunk:
-//   A. whole-wave loads of the phase's raw bytes (16 lanes cover the 256
-//      bytes of one chunk's half); the odd bytes go to the chunk's LDS row,
-//      the even bytes straight to the even plane (16 lanes write one line);
+// chunk t, in four phases of 64 symbols per chunk (small LDS rows keep 12
+// waves per CU):
+//   A. whole-wave loads of the phase's raw bytes (8 lanes cover the 128
+//      bytes of one chunk's phase); the odd bytes go to the chunk's LDS row,
+//      the even bytes straight to the even plane (8 lanes write half a line);
 //   B. each lane appends its row's codes, MSB first, to the unit's words in
 //      the wave's LDS bit buffer (a lane's first and last words may be
 //      shared with its neighbours and are OR-ed in; the words between are its
@@ -257,8 +268,9 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan(uint8_t* out, const Str
 // (enc_zero_stripes cleared them). A unit whose codes exceed the buffer packs
 // straight into memory with the same rule per lane. The layer's last unit,
 // which may end inside a chunk, stages its rows symbol by symbol.
-constexpr int kRowBytes = 132;          // 128 odd bytes + 4: rows start in distinct LDS banks
-constexpr int kHalfSyms = K3HUF_LANE_SYMS / 2;
+constexpr int kPackPhases = 4;
+constexpr int kPhSyms = K3HUF_LANE_SYMS / kPackPhases;   // 64 symbols per chunk per phase
+constexpr int kRowBytes = kPhSyms + 4;    // 64 odd bytes + 4: rows start in distinct LDS banks
 
 __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, uint64_t raw_bytes,
                                                             uint64_t n_chunks, CodeTable ct,
@@ -355,46 +367,57 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
         }
     };
 
+    // phase ph's raw bytes: chunk i * 8 + sub, bytes [q * 16, q * 16 + 16) of
+    // its phase (8 lanes per chunk phase of 128 raw bytes); the next phase's
+    // are requested as soon as this phase's are staged
+    const int q = lane & 7, sub = lane >> 3;
+    uint4 rv[8];
+    auto load_raw = [&](int ph) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            rv[i] = *reinterpret_cast<const uint4*>(uraw + uint64_t(i * 8 + sub) * 512 + ph * 2 * kPhSyms + q * 16);
+    };
+    if (!tail) load_raw(0);
 #pragma unroll 1
-    for (int ph = 0; ph < 2; ++ph) {
+    for (int ph = 0; ph < kPackPhases; ++ph) {
         // A. stage this phase's odd bytes, write its even bytes
         if (!tail) {
-            const int q = lane & 15, sub = lane >> 4;   // 16 lanes per chunk half
-#pragma unroll 4
-            for (int i = 0; i < 16; ++i) {
-                const int ch = i * 4 + sub;
-                const uint4 v = *reinterpret_cast<const uint4*>(uraw + uint64_t(ch) * 512 + ph * 256 + q * 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int ch = i * 8 + sub;
+                const uint4 v = rv[i];
                 const uint32_t o0 = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
                 const uint32_t o1 = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
                 uint32_t* r = reinterpret_cast<uint32_t*>(row + ch * kRowBytes + q * 8);
                 r[0] = o0;
                 r[1] = o1;
-                *reinterpret_cast<uint2*>(ueven + ch * K3HUF_LANE_SYMS + ph * kHalfSyms + q * 8) =
+                *reinterpret_cast<uint2*>(ueven + ch * K3HUF_LANE_SYMS + ph * kPhSyms + q * 8) =
                     make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
                                __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
             }
+            if (ph + 1 < kPackPhases) load_raw(ph + 1);
         } else {
-            for (int j = ph * kHalfSyms; j < min(cnt, (ph + 1) * kHalfSyms); ++j) {
+            for (int j = ph * kPhSyms; j < min(cnt, (ph + 1) * kPhSyms); ++j) {
                 const uint8_t* p = uraw + uint64_t(lane) * 512 + 2 * j;
-                row[lane * kRowBytes + (j - ph * kHalfSyms)] = p[1];
+                row[lane * kRowBytes + (j - ph * kPhSyms)] = p[1];
                 ueven[lane * K3HUF_LANE_SYMS + j] = p[0];
             }
         }
         wave_sync();
         // B. this phase's codes
         if (has) {
-            const int m = min(max(cnt - ph * kHalfSyms, 0), kHalfSyms);
+            const int m = min(max(cnt - ph * kPhSyms, 0), kPhSyms);
             const uint32_t* r = reinterpret_cast<const uint32_t*>(row + lane * kRowBytes);
-            if (m == kHalfSyms && staged) {
+            if (m == kPhSyms && staged) {
 #pragma unroll 4
-                for (int k = 0; k < kHalfSyms / 4; ++k) {
+                for (int k = 0; k < kPhSyms / 4; ++k) {
                     const uint32_t v = r[k];
                     put2(v & 0xFFu, (v >> 8) & 0xFFu);
                     put2((v >> 16) & 0xFFu, v >> 24);
                 }
-            } else if (m == kHalfSyms) {
+            } else if (m == kPhSyms) {
 #pragma unroll 2
-                for (int k = 0; k < kHalfSyms / 4; ++k) {
+                for (int k = 0; k < kPhSyms / 4; ++k) {
                     const uint32_t v = r[k];
                     put(v & 0xFFu);
                     put((v >> 8) & 0xFFu);
