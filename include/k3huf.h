@@ -139,7 +139,9 @@ int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out);
  *   and reads it after the stream synchronizes. Subblocks with bad records
  *   are left unwritten; no read ever leaves [d_blob, d_blob + blob_bytes).
  * Returns K3HUF_OK once queued, K3HUF_E_ARG for bad sizes or alignment (also
- * for blob_bytes >= 2^36: the kernel keeps stripe offsets in 16-byte units),
+ * for blob_bytes >= 2^36: the kernel keeps stripe offsets in 16-byte units;
+ * and for out_bytes > 2 * blob_bytes, which no blob of this format allows:
+ * its even plane alone is out_bytes / 2),
  * K3HUF_E_HIP if the launch fails. Decoding follows the K3 page's "decode
  * loop" (MSB-first bit window, one table lookup per symbol) and "key design
  * points" (even plane interleaved back at even offsets).

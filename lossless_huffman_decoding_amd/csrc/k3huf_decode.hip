@@ -81,14 +81,23 @@ __device__ __forceinline__ uint32_t ent_len1(uint32_t e) { return (e >> 24) & 15
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-// Work distribution. With T waves in the grid and n units, wave w first
-// decodes units w, w + T, ... for S = max(floor(n / T) - kDynRounds, 0)
-// static rounds. The n - S T remaining units are handed out on demand:
-// unit S T + x + G i goes to whichever wave of workgroup group x (block mod
-// G, G = min(8, blocks): one group per XCD) takes ticket i from group x's
-// counter. A wave asks for its next unit when it starts the current one and
-// reads the answer halfway through it, so it holds at most one unit ahead;
-// waves that run faster take more units and the grid ends close together.
+// Work distribution. Units are handed out in descending order: position p
+// (0, 1, ...) stands for unit n - 1 - p, so the layer's last unit, the only
+// one that can be partial (and decoded by the slower tail path), starts
+// first. With T waves in the grid, wave slot v of workgroup b takes position
+// v * blocks + b first (consecutive positions on different CUs, so a small
+// layer spreads over the chip). Every later position is handed out on
+// demand: position T + x + G i goes to whichever wave of workgroup group x
+// (block mod G, G = min(8, blocks): one group per XCD) takes ticket i from
+// group x's counter. On-demand handout is needed because the waves of a CU
+// do not progress at one rate: a SIMD issues from its oldest wave first, and
+// the first of its three waves runs about 1.5 times as fast as the third. A
+// wave asks for its next position halfway through its current unit, and
+// reads the answer (and requests that unit's record) as its last phase
+// starts, so it holds at most a quarter unit of work ahead and the grid's
+// waves finish within about one unit's time of each other. Each counter has
+// a 256-byte line to itself: atomics on one line are serialised, and eight
+// counters sharing a line delayed the tickets enough to stall every unit.
 // The counters live in this array, which exists once per device for the
 // life of the process, in kSchedSlots slots; the last workgroup of a launch
 // clears its slot. Each stream gets a slot of its own on first use: launches
@@ -98,11 +107,11 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // take each other's tickets (units left undecoded); that needs more than
 // kSchedSlots streams, or a graph replay overlapping a decode on the stream
 // the graph was captured on.
-constexpr uint32_t kDynRounds = 3;
 constexpr uint32_t kSchedSlots = 256;
 constexpr uint32_t kGroupsPerSlot = 8;
-constexpr uint32_t kSlotWords = kGroupsPerSlot + 1;   // tickets per group, workgroups done
-__device__ uint32_t g_sched[kSlotWords * kSchedSlots];
+constexpr uint32_t kCounterStride = 64;                               // words: one 256-byte line
+constexpr uint32_t kSlotWords = (kGroupsPerSlot + 1) * kCounterStride;  // tickets per group, workgroups done
+__device__ __attribute__((aligned(256))) uint32_t g_sched[kSlotWords * kSchedSlots];
 
 struct DecodeArgs {
     const uint8_t* blob;
@@ -128,6 +137,9 @@ __device__ __forceinline__ uint32_t bswap32(uint32_t x) {
 __device__ __forceinline__ void flag(uint32_t* status, uint32_t bit) {
     if (status) atomicOr(status, bit);
 }
+// a test's outcome as a bit, for checks combined with `&` so that every
+// operand (and its load) is evaluated without branches
+__device__ __forceinline__ uint32_t bit(bool c) { return c ? 1u : 0u; }
 __device__ __forceinline__ uint32_t uniform(uint32_t x) {
     return __builtin_amdgcn_readfirstlane(x);
 }
@@ -157,18 +169,22 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) {
     return __builtin_amdgcn_readlane(v, l);
 }
 
-// Table entry for 12-bit index i from the (symbol << 4 | length) table.
-__device__ uint32_t make_entry(const uint16_t* lut, uint32_t i) {
-    const uint32_t a = lut[i];
+// Table entry for 12-bit index i from two words of the (symbol << 4 |
+// length) table: a = lut[i] and, when a's length l is 1..11, the entry of the
+// code that follows, b = lut[(i << l) & 0xFFF] (else b = 0).
+__device__ __forceinline__ uint32_t make_entry(uint32_t a, uint32_t b) {
     const uint32_t l1 = a & 15u;
     if (l1 == 0 || l1 > K3HUF_MAXLEN) return kBad | (12u << 24) | (1u << 12) | (12u << 8);
     const uint32_t e = (l1 << 24) | (1u << 12) | (l1 << 8) | ((a >> 4) & 0xFFu);
-    if (l1 < K3HUF_MAXLEN) {
-        const uint32_t b = lut[(i << l1) & 0xFFFu];
-        const uint32_t l2 = b & 15u;
-        if (l2 && l1 + l2 <= K3HUF_MAXLEN) return e + (((b >> 4) & 0xFFu) << 16) + (1u << 12) + (l2 << 8);
-    }
+    const uint32_t l2 = b & 15u;
+    if (l1 < K3HUF_MAXLEN && l2 && l1 + l2 <= K3HUF_MAXLEN)
+        return e + (((b >> 4) & 0xFFu) << 16) + (1u << 12) + (l2 << 8);
     return e;
+}
+// index of the second word make_entry needs for index i, or -1
+__device__ __forceinline__ int second_index(uint32_t i, uint32_t a) {
+    const uint32_t l1 = a & 15u;
+    return l1 != 0 && l1 < K3HUF_MAXLEN ? int((i << l1) & 0xFFFu) : -1;
 }
 
 __device__ __forceinline__ uint32_t peek(const uint32_t* tab, uint64_t acc) {
@@ -205,7 +221,18 @@ struct LaneState {
     uint32_t cnt;    // symbols decoded in this unit (may pass the end by one)
     uint32_t last;   // the last table entry taken
     uint32_t bad;    // OR of all entries taken
+    uint32_t abs;    // gather path: stripe bit index of the lane's next code
 };
+
+// Gather path, for a unit whose codes exceed the buffer: before each phase,
+// every lane copies the codes it can need into its own slot of the buffer.
+// A phase takes at most 65 table entries of at most 12 bits (780 bits); the
+// slot starts at the 8-byte boundary at or before the bit preceding the
+// lane's next code (its index in the slot, pm1, is at most 63), and a window
+// reads two dwords past the one holding bit pm1 + 1: at most dword
+// (63 + 780) / 32 + 2 = 28, so 29 dwords.
+constexpr int kSlotDw = 30;
+static_assert(64 * kSlotDw * 4 <= kBufBytes, "gather slots fit the buffer");
 
 // Decode one phase of a lane: symbols [64 ph, 64 ph + 64) of its chunk into
 // its stage row. Each 64-bit window feeds kLookups table lookups; each
@@ -240,18 +267,17 @@ __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint32_t
     }
 }
 
-// One super-phase (phases sp and sp + 1) of lanes [l0, l1) of a full unit
-// (64 chunks of 256 symbols) whose bitstream dwords [j0, ...) the caller has
-// placed in `buf`. kAll: the pass covers all 64 lanes (l0 = 0, l1 = 64), the
-// common case; its loads and stores then carry no per-chunk condition, so no
+// One super-phase (phases sp and sp + 1) of a full unit (64 chunks of 256
+// symbols, lane t decoding chunk t). The unit's codes are either in `buf`
+// (kGather false: the caller copied them there) or gathered per lane and
+// phase (kGather true). Loads and stores carry no per-chunk condition, so no
 // store waits for the ones before it to complete (vmcnt counts stores too,
 // and a store behind a branch makes the compiler wait for everything
-// outstanding).
-template <bool kAll>
-__device__ __forceinline__ void decode_super(const uint32_t* tab, const uint32_t* buf,
-                                             uint8_t* stage, const Unit& un, int sp, int l0, int l1,
-                                             int lane, LaneState& ls) {
-    const bool mine = kAll || (lane >= l0 && lane < l1);
+// outstanding). `late` runs after the first phase.
+template <bool kGather, class Late>
+__device__ __forceinline__ void decode_super(const uint32_t* tab, uint32_t* buf, uint8_t* stage,
+                                             const Unit& un, int sp, int lane, LaneState& ls,
+                                             Late&& late) {
     const int sub_line = lane >> 3, part = lane & 7;
     uint2 ev[kRounds][kSuper];
     // the two phases' even-plane bytes: a whole line per chunk
@@ -261,19 +287,35 @@ __device__ __forceinline__ void decode_super(const uint32_t* tab, const uint32_t
 #pragma unroll
         for (int f = 0; f < kSuper; ++f) {
             const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t((sp + f) * kPhase + part * 8);
-            // in bounds for every chunk of a full unit, so not conditional
             ev[rr][f] = *reinterpret_cast<const uint2*>(un.even + u);
         }
     }
 #pragma unroll
     for (int q = 0; q < kSuper; ++q) {
         const int ph = sp + q;
-        if (mine) decode_phase(tab, buf, stage + lane * kStageStride, ph, ls);
+        if (kGather) {
+            // the lane's codes for this phase, into its own slot (in bounds:
+            // the same clamp as fill_buffer)
+            uint32_t* slot = buf + lane * kSlotDw;
+            const int d0 = ((int(ls.abs) - 1) >> 5) & ~1;
+            uint2 g[kSlotDw / 2];
+#pragma unroll
+            for (int i = 0; i < kSlotDw / 2; ++i)
+                g[i] = *reinterpret_cast<const uint2*>(un.bits + 4 * min(d0 + 2 * i, un.dmax));
+#pragma unroll
+            for (int i = 0; i < kSlotDw / 2; ++i)
+                *reinterpret_cast<uint2*>(slot + 2 * i) = make_uint2(bswap32(g[i].x), bswap32(g[i].y));
+            ls.pm1 = (ls.abs - 1u) - 32u * uint32_t(d0);
+            const uint32_t p0 = ls.pm1;
+            decode_phase(tab, slot, stage + lane * kStageStride, ph, ls);
+            ls.abs += ls.pm1 - p0;
+        } else {
+            decode_phase(tab, buf, stage + lane * kStageStride, ph, ls);
+        }
         wave_sync();
 #pragma unroll
         for (int rr = 0; rr < kRounds; ++rr) {
             const int c = rr * 8 + sub_line;
-            if (!kAll && (c < l0 || c >= l1)) continue;
             const uint2 sy = staged8(stage, c, part);
             const uint2 e = ev[rr][q];
             const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
@@ -286,36 +328,36 @@ __device__ __forceinline__ void decode_super(const uint32_t* tab, const uint32_t
             __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(un.out + 2 * u));
         }
         wave_sync();
+        if (q == 0) late();
     }
 }
 
-// Decode lanes [l0, l1) of a full unit: both super-phases, then the lane
-// checks. The all-lanes pass runs `mid` between its two super-phases (the
-// caller requests the next unit's record there). The super-phase loop stays
-// rolled: unrolled, the compiler hoists the second half's addresses and
-// loads and runs out of registers.
-template <bool kAll, class Mid>
-__device__ __forceinline__ void decode_lanes(const DecodeArgs& a, const uint32_t* tab,
-                                             const uint32_t* buf, uint8_t* stage, const Unit& un,
-                                             int j0, uint32_t lane_start, uint32_t lane_bits,
-                                             int l0, int l1, int lane, Mid&& mid) {
+// Decode a full unit: both super-phases, then the lane checks. `mid` runs
+// between the super-phases and `late` after the third phase (the caller asks
+// for its next unit, then learns it and requests its record). kGather false:
+// the caller has copied the unit's codes from stripe dword j0 on into `buf`.
+// The super-phase loop stays rolled: unrolled, the compiler hoists the
+// second half's addresses and loads and runs out of registers.
+template <bool kGather, class Mid, class Late>
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a, const uint32_t* tab, uint32_t* buf,
+                                            uint8_t* stage, const Unit& un, int j0,
+                                            uint32_t lane_start, uint32_t lane_bits, int lane,
+                                            Mid&& mid, Late&& late) {
     // the buffer starts at least one dword before the lane's first code, so
     // pm1 >= 0
-    LaneState ls = {lane_start - 32u * uint32_t(j0) - 1u, 0u, 0u, 0u};
+    LaneState ls = {lane_start - 32u * uint32_t(j0) - 1u, 0u, 0u, 0u, lane_start};
     const uint32_t pm1_0 = ls.pm1;
 #pragma unroll 1
     for (int sp = 0; sp < kPhases; sp += kSuper) {
         if (sp == kSuper) mid();
-        decode_super<kAll>(tab, buf, stage, un, sp, l0, l1, lane, ls);
+        decode_super<kGather>(tab, buf, stage, un, sp, lane, ls, [&] { if (sp == kSuper) late(); });
     }
-    if (kAll || (lane >= l0 && lane < l1)) {
-        // a last lookup that ran one symbol past the chunk took that
-        // symbol's bits too
-        uint32_t used = ls.pm1 - pm1_0;
-        if (ls.cnt > K3HUF_LANE_SYMS) used -= ent_bits(ls.last) - ent_len1(ls.last);
-        if (ls.bad & kBad) flag(a.status, K3HUF_DEV_CODE);
-        if (used != lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
-    }
+    // a last lookup that ran one symbol past the chunk took that symbol's
+    // bits too
+    uint32_t used = kGather ? ls.abs - lane_start : ls.pm1 - pm1_0;
+    if (ls.cnt > K3HUF_LANE_SYMS) used -= ent_bits(ls.last) - ent_len1(ls.last);
+    if (ls.bad & kBad) flag(a.status, K3HUF_DEV_CODE);
+    if (used != lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
 }
 
 // The same for the layer's last unit when it holds fewer than 16384 symbols:
@@ -425,33 +467,36 @@ __device__ __forceinline__ uint32_t stripe_subblocks(uint32_t n_syms) {
     return (n_syms + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
 }
 
+// Branch-free: every lane issues its loads (a stripe that does not exist,
+// or whose offset fails the checks, reads the blob's first 32 bytes instead
+// and is then rejected), and every check is evaluated, so the loads of all
+// lanes go out together instead of one dependent round trip per check.
 __device__ __forceinline__ StripeLane load_stripes(const DecodeArgs& a, uint32_t blk, int lane) {
-    StripeLane t = {0u, 0u, 0u, kNoStripe};
     const uint32_t s = blk * 64u + uint32_t(lane);
-    if (s < a.n_stripes) {
-        const uint64_t soff = ld64(a.blob + K3HUF_HDR_BYTES + 8ull * s);
-        const uint64_t raw_s = stripe_raw(a, s);
-        const uint32_t n = uint32_t(raw_s / 2);
-        const uint32_t nsb = stripe_subblocks(n);
-        if ((soff & 15) == 0 && soff + K3HUF_STRIPE_HDR_BYTES <= a.blob_bytes) {
-            const uint4 r0 = *reinterpret_cast<const uint4*>(a.blob + soff);
-            const uint4 r1 = *reinterpret_cast<const uint4*>(a.blob + soff + 16);
-            const uint32_t n_bits = r0.z, bit_bytes = r0.w, bits_off = r1.z, even_off = r1.w;
-            const bool ok = r0.x == uint32_t(raw_s) && r0.y == n && r1.x == s * kSubPerStripe &&
-                            r1.y == nsb && (bits_off & 15) == 0 && (even_off & 15) == 0 &&
-                            bits_off >= K3HUF_STRIPE_HDR_BYTES + K3HUF_SUBBLOCK_REC_BYTES * nsb &&
-                            uint64_t(n_bits) <= 8ull * bit_bytes &&
-                            uint64_t(n_bits) <= uint64_t(K3HUF_MAXLEN) * n &&
-                            uint64_t(even_off) >= uint64_t(bits_off) + bit_bytes &&
-                            soff + even_off + ((uint64_t(n) + 15) & ~15ull) <= a.blob_bytes;
-            if (ok) {
-                t.off16 = uint32_t(soff >> 4);
-                t.bits_off = bits_off;
-                t.even_off = even_off;
-                t.n_bits = n_bits;
-            }
-        }
-    }
+    const bool has = s < a.n_stripes;
+    const uint32_t sc = has ? s : 0u;
+    const uint64_t soff = ld64(a.blob + K3HUF_HDR_BYTES + 8ull * sc);
+    const uint64_t raw_s = stripe_raw(a, sc);
+    const uint32_t n = uint32_t(raw_s / 2);
+    const uint32_t nsb = stripe_subblocks(n);
+    const uint32_t in = bit((soff & 15) == 0) & bit(soff + K3HUF_STRIPE_HDR_BYTES <= a.blob_bytes);
+    const uint64_t so = in ? soff : 0ull;
+    const uint4 r0 = *reinterpret_cast<const uint4*>(a.blob + so);
+    const uint4 r1 = *reinterpret_cast<const uint4*>(a.blob + so + 16);
+    const uint32_t n_bits = r0.z, bit_bytes = r0.w, bits_off = r1.z, even_off = r1.w;
+    const uint32_t ok = bit(has) & in & bit(r0.x == uint32_t(raw_s)) & bit(r0.y == n) &
+                        bit(r1.x == sc * kSubPerStripe) & bit(r1.y == nsb) & bit((bits_off & 15) == 0) &
+                        bit((even_off & 15) == 0) &
+                        bit(bits_off >= K3HUF_STRIPE_HDR_BYTES + K3HUF_SUBBLOCK_REC_BYTES * nsb) &
+                        bit(uint64_t(n_bits) <= 8ull * bit_bytes) &
+                        bit(uint64_t(n_bits) <= uint64_t(K3HUF_MAXLEN) * n) &
+                        bit(uint64_t(even_off) >= uint64_t(bits_off) + bit_bytes) &
+                        bit(so + even_off + ((uint64_t(n) + 15) & ~15ull) <= a.blob_bytes);
+    StripeLane t;
+    t.off16 = ok ? uint32_t(so >> 4) : 0u;
+    t.bits_off = ok ? bits_off : 0u;
+    t.even_off = ok ? even_off : 0u;
+    t.n_bits = ok ? n_bits : kNoStripe;
     return t;
 }
 
@@ -477,13 +522,14 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
     uint32_t* tab = reinterpret_cast<uint32_t*>(lds);  // at LDS address 0
 
-    // layer header must describe exactly this call (uniform over the grid)
+    // layer header must describe exactly this call (uniform over the grid;
+    // every field is tested, so the loads go out together)
     const uint8_t* b = a.blob;
-    const bool hdr_ok = ld32(b) == 0x4648334Bu /* "K3HF" */ && ld32(b + 4) == (1u | (12u << 16)) &&
-                        ld32(b + 8) == K3HUF_STRIPE_BYTES && ld32(b + 12) == K3HUF_SUBBLOCK_BYTES &&
-                        ld32(b + 16) == K3HUF_LANE_SYMS && ld32(b + 20) == a.n_stripes &&
-                        ld64(b + 24) == a.out_bytes && ld32(b + 32) == a.n_sub &&
-                        ld64(b + 40) <= a.blob_bytes;
+    const uint32_t hdr_ok = bit(ld32(b) == 0x4648334Bu /* "K3HF" */) & bit(ld32(b + 4) == (1u | (12u << 16))) &
+                            bit(ld32(b + 8) == K3HUF_STRIPE_BYTES) & bit(ld32(b + 12) == K3HUF_SUBBLOCK_BYTES) &
+                            bit(ld32(b + 16) == K3HUF_LANE_SYMS) & bit(ld32(b + 20) == a.n_stripes) &
+                            bit(ld64(b + 24) == a.out_bytes) & bit(ld32(b + 32) == a.n_sub) &
+                            bit(ld64(b + 40) <= a.blob_bytes);
     if (!hdr_ok) {
         if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, K3HUF_DEV_HEADER);
         return;
@@ -493,32 +539,58 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const uint32_t n_units = a.n_sub * kUnitsPerSub;
     const uint32_t T = gridDim.x * kWaves;
-    const uint32_t rounds = n_units / T;
-    const uint32_t stat = rounds > kDynRounds ? rounds - kDynRounds : 0u;   // static rounds
-    const uint32_t dyn0 = stat * T;                                          // first handed-out unit
     const uint32_t groups = min(kGroupsPerSlot, gridDim.x);
     const uint32_t group = blockIdx.x % groups;
     uint32_t* slot = &g_sched[kSlotWords * a.slot];
-    uint32_t h = blockIdx.x * kWaves + wave;
-    if (stat == 0) {
-        uint32_t t = 0;
-        if (lane == 0) t = atomicAdd(&slot[group], 1u);
-        h = uniform(dyn0 + group + groups * lane_value(t, 0));
-    }
-    // stripe values of the block holding this wave's first unit, requested
-    // before the table build so that their latency overlaps it
-    uint32_t blk = h < n_units ? h / (kUnitsPerSub * kSubPerStripe * 64u) : 0u;
-    StripeLane sl = load_stripes(a, blk, lane);
+    auto unit_of = [&](uint32_t p) { return n_units - 1u - p; };   // p < n_units
+    uint32_t h = wave * gridDim.x + blockIdx.x;                    // position of this wave's unit
 
-    for (int i = threadIdx.x; i < K3HUF_LUT_ENTRIES; i += kThreads) tab[i] = make_entry(a.lut, i);
+    // The set-up's loads go out in three round trips: the table's first
+    // words with the stripe offsets, then the stripe records, then the first
+    // unit's record with the table's second words.
+    constexpr int kPerThread = (K3HUF_LUT_ENTRIES + kThreads - 1) / kThreads;
+    uint32_t ta[kPerThread], tb[kPerThread];
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int i = int(threadIdx.x) + q * kThreads;
+        ta[q] = i < K3HUF_LUT_ENTRIES ? uint32_t(a.lut[i]) : 0u;
+    }
+    // stripe values of the block holding this wave's first unit
+    uint32_t blk = h < n_units ? unit_of(h) / (kUnitsPerSub * kSubPerStripe * 64u) : 0u;
+    StripeLane sl = load_stripes(a, blk, lane);
+    uint32_t pf_h = 0xFFFFFFFFu;   // position whose unit's record `pf` holds
+    RecLanes pf = {0u, 0u, 0u};
+    // request the record of position p's unit (when its stripe is in `sl`)
+    auto request_rec = [&](uint32_t p) {
+        pf_h = 0xFFFFFFFFu;
+        if (p < n_units) {
+            const uint32_t kn = unit_of(p) / kUnitsPerSub;
+            const uint32_t sn = kn / kSubPerStripe, jn = kn % kSubPerStripe;
+            if ((sn >> 6) == blk && lane_value(sl.n_bits, sn & 63u) != kNoStripe) {
+                const uint8_t* stn = b + (uint64_t(lane_value(sl.off16, sn & 63u)) << 4);
+                pf = load_rec(stn + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jn,
+                              jn + 1 < stripe_subblocks(uint32_t(stripe_raw(a, sn) / 2)), lane);
+                pf_h = p;
+            }
+        }
+    };
+    request_rec(h);
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int i = int(threadIdx.x) + q * kThreads;
+        const int i2 = i < K3HUF_LUT_ENTRIES ? second_index(uint32_t(i), ta[q]) : -1;
+        tb[q] = i2 >= 0 ? uint32_t(a.lut[i2]) : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int i = int(threadIdx.x) + q * kThreads;
+        if (i < K3HUF_LUT_ENTRIES) tab[i] = make_entry(ta[q], tb[q]);
+    }
     __syncthreads();
 
     uint8_t* wl = lds + kTabBytes + wave * kWaveLds;
     uint32_t* buf = reinterpret_cast<uint32_t*>(wl);
     uint8_t* stage = wl + kBufBytes;
-    uint32_t round = 0;
-    uint32_t pf_h = 0xFFFFFFFFu;   // unit whose record `pf` holds
-    RecLanes pf = {0u, 0u, 0u};
     uint32_t ticket = 0;           // lane 0: the answer to this unit's request
 
     while (h < n_units) {
@@ -526,31 +598,22 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         // waves issue ahead of waves still busy with earlier units
         if (h + 2 * T >= n_units) __builtin_amdgcn_s_setprio(1);
         if (h + T >= n_units) __builtin_amdgcn_s_setprio(3);
-        // the next unit: static, or handed out now (the answer is read
-        // halfway through this unit)
-        const bool ask = round + 1 >= stat;
-        if (ask && lane == 0) ticket = atomicAdd(&slot[group], 1u);
+        // the next position: asked for halfway through a full unit (`ask`),
+        // read and its record requested as the unit's last phase starts
+        // (`learn`); other units do both at their end
+        bool asked = false;
         uint32_t h_next = 0xFFFFFFFFu;
-        auto next_unit = [&]() -> uint32_t {
-            return ask ? dyn0 + group + groups * lane_value(ticket, 0) : h + T;
+        auto ask = [&]() {
+            if (lane == 0) ticket = atomicAdd(&slot[group * kCounterStride], 1u);
+            asked = true;
         };
-        // learn the next unit and request its record (called between the two
-        // super-phases of a full single-pass unit)
-        auto mid = [&]() {
-            h_next = next_unit();
-            pf_h = 0xFFFFFFFFu;
-            if (h_next < n_units) {
-                const uint32_t kn = h_next / kUnitsPerSub;
-                const uint32_t sn = kn / kSubPerStripe, jn = kn % kSubPerStripe;
-                if ((sn >> 6) == blk && lane_value(sl.n_bits, sn & 63u) != kNoStripe) {
-                    const uint8_t* stn = b + (uint64_t(lane_value(sl.off16, sn & 63u)) << 4);
-                    pf = load_rec(stn + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jn,
-                                  jn + 1 < stripe_subblocks(uint32_t(stripe_raw(a, sn) / 2)), lane);
-                    pf_h = h_next;
-                }
-            }
+        auto next_pos = [&]() { return uniform(T + group + groups * lane_value(ticket, 0)); };
+        auto learn = [&]() {
+            h_next = next_pos();
+            request_rec(h_next);
         };
-        const uint32_t k = h / kUnitsPerSub, half = h % kUnitsPerSub;
+        const uint32_t un_idx = unit_of(h);
+        const uint32_t k = un_idx / kUnitsPerSub, half = un_idx % kUnitsPerSub;
         const uint32_t s = k / kSubPerStripe, jsb = k % kSubPerStripe;
         if ((s >> 6) != blk) {
             blk = s >> 6;
@@ -606,38 +669,47 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         un.out = a.out + uint64_t(k) * K3HUF_SUBBLOCK_BYTES + 2ull * half * kUnitSyms;
         const uint32_t lane_start = unit_start + incl - lb;
         const uint32_t lane_end = unit_start + incl;
-        const bool full = un.nsyms == uint32_t(kUnitSyms);
 
-        // passes over consecutive lane ranges whose codes fit the buffer
-        // (one pass unless the unit's codes exceed kBufBytes)
-        for (int l0 = 0; l0 < 64;) {
-            const int j0 = first_dword(lane_value(lane_start, l0));
-            const bool over = lane >= l0 && (end_dword(lane_end) - j0) * 4 > kBufBytes;
-            const uint64_t m = __ballot(over);
-            const int l1 = m ? int(__builtin_ctzll(m)) : 64;   // > l0: one chunk always fits
-            const int units = (end_dword(lane_value(lane_end, l1 - 1)) - j0) / 4;
-            fill_buffer(buf, un, j0, units, lane);
-            if (full && l0 == 0 && l1 == 64) {
+        if (un.nsyms == uint32_t(kUnitSyms)) {
+            const int j0 = first_dword(lane_value(lane_start, 0));
+            const int units = (end_dword(lane_value(lane_end, 63)) - j0) / 4;
+            if (units * 16 <= kBufBytes) {
+                fill_buffer(buf, un, j0, units, lane);
                 drain_vm();   // fill_buffer has just drained it
-                decode_lanes<true>(a, tab, buf, stage, un, j0, lane_start, lb, 0, 64, lane, mid);
-            } else if (full)
-                decode_lanes<false>(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane, [] {});
-            else
+                decode_unit<false>(a, tab, buf, stage, un, j0, lane_start, lb, lane, ask, learn);
+            } else {
+                // codes exceed the buffer (long codes, e.g. a vector of
+                // norm gains): each lane gathers its codes phase by phase
+                decode_unit<true>(a, tab, buf, stage, un, 0, lane_start, lb, lane, ask, learn);
+            }
+        } else {
+            // the layer's partial last unit: passes over consecutive lane
+            // ranges whose codes fit the buffer
+            for (int l0 = 0; l0 < 64;) {
+                const int j0 = first_dword(lane_value(lane_start, l0));
+                const bool over = lane >= l0 && (end_dword(lane_end) - j0) * 4 > kBufBytes;
+                const uint64_t m = __ballot(over);
+                const int l1 = m ? int(__builtin_ctzll(m)) : 64;   // > l0: one chunk always fits
+                const int units = (end_dword(lane_value(lane_end, l1 - 1)) - j0) / 4;
+                fill_buffer(buf, un, j0, units, lane);
                 decode_lanes_tail(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
-            l0 = l1;
+                l0 = l1;
+            }
         }
         } while (false);   // the checks above leave a bad unit with `continue`
-        if (h_next == 0xFFFFFFFFu) h_next = next_unit();   // no mid-unit step ran
-        h = uniform(h_next);
-        ++round;
+        if (h_next == 0xFFFFFFFFu) {   // no mid-unit steps ran
+            if (!asked) ask();
+            h_next = next_pos();
+        }
+        h = h_next;
     }
 
     // the last workgroup to finish clears this launch's counter slot
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t done = atomicAdd(&slot[kGroupsPerSlot], 1u);
+        const uint32_t done = atomicAdd(&slot[kGroupsPerSlot * kCounterStride], 1u);
         if (done == gridDim.x - 1)
-            for (uint32_t g = 0; g <= kGroupsPerSlot; ++g) atomicExch(&slot[g], 0u);
+            for (uint32_t g = 0; g <= kGroupsPerSlot; ++g) atomicExch(&slot[g * kCounterStride], 0u);
     }
 }
 
@@ -691,7 +763,7 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     const uint64_t n_sub = (uint64_t(out_bytes) + K3HUF_SUBBLOCK_BYTES - 1) / K3HUF_SUBBLOCK_BYTES;
     const uint64_t n_stripes = (uint64_t(out_bytes) + K3HUF_STRIPE_BYTES - 1) / K3HUF_STRIPE_BYTES;
     if (n_sub > 0xFFFFFFFFull || blob_bytes < K3HUF_HDR_BYTES + 8 * n_stripes ||
-        uint64_t(blob_bytes) >= (1ull << 36))
+        uint64_t(blob_bytes) >= (1ull << 36) || uint64_t(out_bytes) > 2ull * blob_bytes)
         return K3HUF_E_ARG;
     DevInfo di;
     uint32_t slot = 0;

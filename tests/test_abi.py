@@ -132,6 +132,9 @@ def test_decode_layer_rejects_bad_arguments_before_any_device_call():
     assert raw(blob, 304 + 16, lut, out, three, 0, None) == k3huf.E_ARG
     # offsets are kept in 16-byte units by the kernel: blobs stop below 64 GiB
     assert raw(blob, 1 << 36, lut, out, 2, 0, None) == k3huf.E_ARG
+    # a blob holds its layer's even plane (raw / 2 bytes): no blob of 1 KiB
+    # decodes to 4 KiB
+    assert raw(blob, 1024, lut, out, 4096, 0, None) == k3huf.E_ARG
 
 
 def test_host_ring_rejects_bad_arguments_before_any_device_call():

@@ -205,6 +205,8 @@ def test_bad_arguments_raise_before_launch():
         k3huf.decode_layer(d_blob, d_lut, d_out[:4095])         # odd size
     with pytest.raises(k3huf.K3HufError):
         k3huf.decode_layer(d_blob[:100], d_lut, d_out[:4096])   # blob shorter than a header
+    with pytest.raises(k3huf.K3HufError):
+        k3huf.decode_layer(d_blob[:1024], d_lut, d_out[:4096])  # output above twice the blob
 
 
 # ---------------------------------------------------------------------------
