@@ -76,6 +76,37 @@ def test_edge_parity(layer):
     assert (got == want).all()
 
 
+@pytest.mark.parametrize("n_bytes", [65536, 65536 + 2 * 12000, 3 * 65536 + 2 * 20000 + 2,
+                                     2 * 65536 - 2, 4 * 65536 + 2 * 7000])
+def test_units_over_the_lds_buffer(n_bytes):
+    """Uniform high bytes take 8-bit codes, so a full unit's codes (16 KiB)
+    exceed the kernel's 7.5 KiB bitstream buffer (each lane then gathers its
+    codes phase by phase), and a partial last unit of more than 7680 symbols
+    decodes in several passes over lane ranges."""
+    x = synth.edge_uniform(seed=700 + n_bytes % 97, n_bytes=n_bytes)
+    blob = O.encode_layer(x)
+    say("over buffer", n_bytes)
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got == x).all()
+    assert (got == O.decode_layer(blob)).all()
+
+
+def test_some_units_over_the_lds_buffer():
+    """Weights with two half-subblocks of uniform high bytes: those units'
+    codes are long (the rare symbols get long codes) and exceed the buffer,
+    while their neighbours fit it."""
+    x = synth.small_random(21, 8 * 65536 + 4098).copy()
+    rng = np.random.default_rng(5)
+    for start in (65536 + 32768, 5 * 65536):   # a second-half and a first-half unit
+        x[start + 1: start + 32768: 2] = rng.integers(0, 256, 16384, dtype=np.uint8)
+    blob = O.encode_layer(x)
+    say("some units over buffer")
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got == x).all()
+
+
 def test_heavy_parity():
     x, blob = oracle_container("heavy", synth.heavy)
     say("heavy", x.size)
