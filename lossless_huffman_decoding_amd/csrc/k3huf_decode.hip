@@ -30,8 +30,10 @@ namespace {
 // chunks of 256 symbols, lane t decoding chunk t. Every HBM line is read or
 // written in one burst:
 //   - the unit's bitstream is copied into the wave's LDS buffer with
-//     coalesced 16-byte loads before its lanes decode (a unit whose codes
-//     exceed the buffer is decoded in passes over consecutive lane ranges);
+//     coalesced 16-byte loads before its lanes decode (when a full unit's
+//     codes exceed the buffer, each lane gathers its own codes phase by
+//     phase instead; the layer's partial last unit is decoded in passes over
+//     consecutive lane ranges);
 //   - the even-plane bytes of two phases (a whole 128-byte line per chunk)
 //     are requested together into registers;
 //   - each phase's 64 symbols per chunk are staged in LDS, so every output
@@ -364,10 +366,9 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const uint32_t*
 // lane t decodes clamp(nsyms - 256 t, 0, 256) symbols one code per table
 // step; kept plain (it runs at most once per layer).
 __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uint32_t* tab,
-                                                            const uint32_t* buf, uint8_t* stage,
-                                                            const Unit& un, int j0,
-                                                            uint32_t lane_start, uint32_t lane_bits,
-                                                            int l0, int l1, int lane) {
+                                                  const uint32_t* buf, uint8_t* stage, const Unit& un,
+                                                  int j0, uint32_t lane_start, uint32_t lane_bits,
+                                                  int l0, int l1, int lane) {
     const bool mine = lane >= l0 && lane < l1;
     const int lane_cnt = min(max(int(un.nsyms) - lane * int(K3HUF_LANE_SYMS), 0), int(K3HUF_LANE_SYMS));
     uint32_t pm1 = lane_start - 32u * uint32_t(j0) - 1u;
