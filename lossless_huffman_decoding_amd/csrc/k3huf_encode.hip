@@ -10,7 +10,7 @@
 // and whose even bytes are copied raw ("key design points"), plus the
 // subblock/lane index. The code lengths and the layout are computed on the
 // host from the GPU's histograms (they are 256-entry problems); the byte work
-// runs in four kernels:
+// runs in five kernels:
 //   enc_hist   per-stripe histograms of the odd bytes;
 //   enc_count  code bits of every 256-symbol lane chunk, and of every
 //              subblock (128 chunks);
@@ -19,9 +19,10 @@
 //   enc_pack   one wave per half subblock (64 lane chunks, one per lane): the
 //              lanes' start bits (a wave prefix sum), their lane bit counts,
 //              their codes packed into a per-wave LDS buffer (words two lanes
-//              share are OR-ed), then copied out with whole-wave stores (the
-//              unit's first and last words, which a neighbouring unit may
-//              share, are OR-ed into memory), and the even bytes.
+//              share are OR-ed), then copied out with whole-wave stores, and
+//              the even bytes; a unit's first and last words, which a
+//              neighbouring unit may share, are set aside;
+//   enc_edges  one thread per unit: the words units share, from both sides.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -60,21 +61,30 @@ struct CodeTable {
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct WorkLayout {
-    uint64_t hist, geom, chunks, subblocks, status, total;
+    uint64_t hist, geom, chunks, subblocks, edges, status, total;
+};
+
+// Per packing unit: its first and last bitstream words when another unit
+// shares them (0 otherwise), and its start and end bits.
+struct UnitEdges {
+    uint32_t first, last, b0, b1;
 };
 
 // work buffer: per-stripe histograms (u64), stripe geometry, lane-chunk bit
-// counts (u32), subblock bit counts then start bits (u32), a status word
+// counts (u32), subblock bit counts then start bits (u32), unit edges, a
+// status word
 WorkLayout work_layout(uint64_t raw_bytes) {
     const uint64_t ns = k3huf_detail::stripes_for(raw_bytes);
     const uint64_t n_chunks = (raw_bytes / 2 + K3HUF_LANE_SYMS - 1) / K3HUF_LANE_SYMS;
     const uint64_t n_sub = (raw_bytes + K3HUF_SUBBLOCK_BYTES - 1) / K3HUF_SUBBLOCK_BYTES;
+    const uint64_t n_units = (n_chunks + 63) / 64;
     WorkLayout w;
     w.hist = 0;
     w.geom = align256(w.hist + 256 * 8 * ns);
     w.chunks = align256(w.geom + sizeof(StripeDev) * ns);
     w.subblocks = align256(w.chunks + 4 * n_chunks);
-    w.status = align256(w.subblocks + 4 * n_sub);
+    w.edges = align256(w.subblocks + 4 * n_sub);
+    w.status = align256(w.edges + sizeof(UnitEdges) * n_units);
     w.total = w.status + 256;
     return w;
 }
@@ -263,11 +273,14 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan(uint8_t* out, const Str
 //      the wave's LDS bit buffer (a lane's first and last words may be
 //      shared with its neighbours and are OR-ed in; the words between are its
 //      own).
-// Then the buffer is written out with whole-wave stores; the unit's first and
-// last words may hold a neighbouring unit's bits and are OR-ed into memory
-// (enc_zero_stripes cleared them). A unit whose codes exceed the buffer packs
-// straight into memory with the same rule per lane. The layer's last unit,
-// which may end inside a chunk, stages its rows symbol by symbol.
+// Then the buffer is written out with whole-wave stores, except the unit's
+// first and last words when a neighbouring unit shares them: those go to the
+// unit's edge record, and enc_edges writes each shared word once from both
+// halves (atomics on words another CU is writing cost more than the rest of
+// the copy). A unit whose codes exceed the buffer packs straight into memory,
+// OR-ing every shared word (enc_zero_stripes cleared the bitstream), and
+// leaves its edge record zero. The layer's last unit, which may end inside a
+// chunk, stages its rows symbol by symbol.
 constexpr int kPackPhases = 4;
 constexpr int kPhSyms = K3HUF_LANE_SYMS / kPackPhases;   // 64 symbols per chunk per phase
 constexpr int kRowBytes = kPhSyms + 4;    // 64 odd bytes + 4: rows start in distinct LDS banks
@@ -275,7 +288,8 @@ constexpr int kRowBytes = kPhSyms + 4;    // 64 odd bytes + 4: rows start in dis
 __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, uint64_t raw_bytes,
                                                             uint64_t n_chunks, CodeTable ct,
                                                             const StripeDev* g, const uint32_t* chunk,
-                                                            const uint32_t* sb_start, uint8_t* out) {
+                                                            const uint32_t* sb_start, UnitEdges* edges,
+                                                            uint8_t* out) {
     __shared__ uint32_t tab[256];
     __shared__ uint32_t stage[kPackWaves][kPackWords];
     __shared__ __attribute__((aligned(16))) uint8_t rows[kPackWaves][64 * kRowBytes];
@@ -377,72 +391,107 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
         for (int i = 0; i < 8; ++i)
             rv[i] = *reinterpret_cast<const uint4*>(uraw + uint64_t(i * 8 + sub) * 512 + ph * 2 * kPhSyms + q * 16);
     };
-    if (!tail) load_raw(0);
-#pragma unroll 1
-    for (int ph = 0; ph < kPackPhases; ++ph) {
-        // A. stage this phase's odd bytes, write its even bytes
-        if (!tail) {
+    // B. phase ph's codes, from the lane's row
+    auto pack_phase = [&](int ph) {
+        if (!has) return;
+        const int m = min(max(cnt - ph * kPhSyms, 0), kPhSyms);
+        const uint32_t* r = reinterpret_cast<const uint32_t*>(row + lane * kRowBytes);
+        if (m == kPhSyms && staged) {
+#pragma unroll 4
+            for (int k = 0; k < kPhSyms / 4; ++k) {
+                const uint32_t v = r[k];
+                put2(v & 0xFFu, (v >> 8) & 0xFFu);
+                put2((v >> 16) & 0xFFu, v >> 24);
+            }
+        } else if (m == kPhSyms) {
+#pragma unroll 2
+            for (int k = 0; k < kPhSyms / 4; ++k) {
+                const uint32_t v = r[k];
+                put(v & 0xFFu);
+                put((v >> 8) & 0xFFu);
+                put((v >> 16) & 0xFFu);
+                put(v >> 24);
+            }
+        } else {
+            const uint8_t* rb = row + lane * kRowBytes;
+            for (int k = 0; k < m; ++k) put(rb[k]);
+        }
+    };
+    if (!tail) {
+        load_raw(0);
+        // unrolled, so the raw registers need no copies between phases (a
+        // copy waits for every outstanding load and store)
+#pragma unroll
+        for (int ph = 0; ph < kPackPhases; ++ph) {
+            // A. stage this phase's odd bytes and keep its even bytes; the
+            // next phase's raw bytes are requested before the even bytes are
+            // written, so waiting for those loads never waits for these
+            // stores (loads and stores retire in issue order)
+            uint2 ev[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int ch = i * 8 + sub;
                 const uint4 v = rv[i];
-                const uint32_t o0 = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
-                const uint32_t o1 = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
                 uint32_t* r = reinterpret_cast<uint32_t*>(row + ch * kRowBytes + q * 8);
-                r[0] = o0;
-                r[1] = o1;
-                *reinterpret_cast<uint2*>(ueven + ch * K3HUF_LANE_SYMS + ph * kPhSyms + q * 8) =
-                    make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
-                               __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
+                r[0] = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
+                r[1] = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
+                ev[i] = make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
+                                   __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
             }
             if (ph + 1 < kPackPhases) load_raw(ph + 1);
-        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<uint2*>(ueven + (i * 8 + sub) * K3HUF_LANE_SYMS + ph * kPhSyms + q * 8) = ev[i];
+            wave_sync();
+            pack_phase(ph);
+            wave_sync();
+        }
+    } else {
+#pragma unroll 1
+        for (int ph = 0; ph < kPackPhases; ++ph) {
             for (int j = ph * kPhSyms; j < min(cnt, (ph + 1) * kPhSyms); ++j) {
                 const uint8_t* p = uraw + uint64_t(lane) * 512 + 2 * j;
                 row[lane * kRowBytes + (j - ph * kPhSyms)] = p[1];
                 ueven[lane * K3HUF_LANE_SYMS + j] = p[0];
             }
+            wave_sync();
+            pack_phase(ph);
+            wave_sync();
         }
-        wave_sync();
-        // B. this phase's codes
-        if (has) {
-            const int m = min(max(cnt - ph * kPhSyms, 0), kPhSyms);
-            const uint32_t* r = reinterpret_cast<const uint32_t*>(row + lane * kRowBytes);
-            if (m == kPhSyms && staged) {
-#pragma unroll 4
-                for (int k = 0; k < kPhSyms / 4; ++k) {
-                    const uint32_t v = r[k];
-                    put2(v & 0xFFu, (v >> 8) & 0xFFu);
-                    put2((v >> 16) & 0xFFu, v >> 24);
-                }
-            } else if (m == kPhSyms) {
-#pragma unroll 2
-                for (int k = 0; k < kPhSyms / 4; ++k) {
-                    const uint32_t v = r[k];
-                    put(v & 0xFFu);
-                    put((v >> 8) & 0xFFu);
-                    put((v >> 16) & 0xFFu);
-                    put(v >> 24);
-                }
-            } else {
-                const uint8_t* rb = row + lane * kRowBytes;
-                for (int k = 0; k < m; ++k) put(rb[k]);
-            }
-        }
-        wave_sync();
     }
     if (has && nacc > 0) emit(uint32_t(acc >> 32), true);
     wave_sync();
-    if (staged) {
-        for (uint32_t i = lane; i < nw; i += 64) {
-            const uint32_t v = bswap32(buf[i]);
-            const bool edge = (i == 0 && (u0 & 31u)) || (i == nw - 1 && (u1 & 31u));
-            if (edge)
-                atomicOr(&words[w0 + i], v);
-            else
-                words[w0 + i] = v;
-        }
+    // the unit's edge record: its shared first and last words (staged units)
+    // and its bit range
+    uint32_t* er = reinterpret_cast<uint32_t*>(edges + u);
+    if (lane < 4) {
+        const uint32_t f = staged && (u0 & 31u) ? bswap32(buf[0]) : 0u;
+        const uint32_t l = staged && (u1 & 31u) ? bswap32(buf[min(nw, uint32_t(kPackWords)) - 1]) : 0u;
+        er[lane] = lane == 0 ? f : lane == 1 ? l : lane == 2 ? u0 : u1;
     }
+    if (staged) {
+        const uint32_t i0 = (u0 & 31u) ? 1u : 0u, i1 = (u1 & 31u) ? nw - 1 : nw;
+        for (uint32_t i = i0 + lane; i < i1; i += 64) words[w0 + i] = bswap32(buf[i]);
+    }
+}
+
+// One thread per packing unit: the word holding the unit's first bit, when
+// the unit before it (same stripe) ends inside it, is the OR of both units'
+// parts, and the stripe's last unit also writes its own last word. Each such
+// word is written by exactly one thread; a unit that packed straight into
+// memory has already OR-ed its part in (its edge record is zero), so the
+// parts are OR-ed onto what memory holds.
+__global__ void enc_edges(const UnitEdges* edges, uint64_t n_units, const StripeDev* g, uint8_t* out) {
+    const uint64_t u = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (u >= n_units) return;
+    const UnitEdges e = edges[u];
+    const StripeDev G = g[u / kUnitsPerStripe];
+    uint32_t* words = reinterpret_cast<uint32_t*>(out + G.off + G.bits_off);
+    const bool first_in_stripe = u % kUnitsPerStripe == 0;
+    const bool last_in_stripe = u + 1 == n_units || (u + 1) % kUnitsPerStripe == 0;
+    if ((e.b0 & 31u) && !first_in_stripe)
+        words[e.b0 >> 5] |= e.first | edges[u - 1].last;
+    if ((e.b1 & 31u) && last_in_stripe) words[e.b1 >> 5] |= e.last;
 }
 
 // a kernel launch's status as a return code
@@ -478,6 +527,7 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     auto* chunk = reinterpret_cast<uint32_t*>(work + wl.chunks);
     auto* sb_bits = reinterpret_cast<uint32_t*>(work + wl.subblocks);
     auto* status = reinterpret_cast<uint32_t*>(work + wl.status);
+    auto* edges = reinterpret_cast<UnitEdges*>(work + wl.edges);
 
     // 1. per-stripe histograms (the status word is cleared with them)
     hipLaunchKernelGGL(enc_fill_zero, dim3(64), dim3(256), 0, st, reinterpret_cast<uint4*>(work),
@@ -524,7 +574,9 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
     hipLaunchKernelGGL(enc_pack, dim3(unsigned((n_units + kPackWaves - 1) / kPackWaves)),
                        dim3(kPackWaves * 64), 0, st, raw, raw_bytes, n_chunks, ct, geom, chunk, sb_bits,
-                       out);
+                       edges, out);
+    hipLaunchKernelGGL(enc_edges, dim3(unsigned((n_units + 255) / 256)), dim3(256), 0, st, edges,
+                       n_units, geom, out);
     if (launched()) return K3HUF_E_HIP;
     uint32_t bad = 0;
     if (hipMemcpyAsync(&bad, status, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
