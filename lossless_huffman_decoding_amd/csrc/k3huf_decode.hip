@@ -780,7 +780,9 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     a.n_stripes = uint32_t(n_stripes);
     a.status = d_status;
     a.slot = slot;
-    const uint64_t want = (n_sub * kUnitsPerSub + kWaves - 1) / kWaves;
+    // one workgroup per unit up to a full chip: the first round's positions
+    // are wave-major, so a layer of fewer units than CUs gets a CU per unit
+    const uint64_t want = n_sub * kUnitsPerSub;
     const uint64_t resident = uint64_t(di.cus) * uint64_t(di.wg_per_cu);
     const unsigned grid = unsigned(want < resident ? want : resident);
     hipLaunchKernelGGL(k3huf_decode_kernel, dim3(grid), dim3(kThreads), 0,
