@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     uint32_t* buf = stage[wave];
     uint8_t* row = rows[wave];
     const uint32_t w0 = u0 >> 5, nw = ((u1 + 31) >> 5) - w0;
-    const bool staged = __builtin_amdgcn_readfirstlane(nw) <= uint32_t(kPackWords);   // uniform
+    const bool staged = uint32_t(__builtin_amdgcn_readfirstlane(nw)) <= uint32_t(kPackWords);   // uniform
     if (staged)
         for (uint32_t i = lane; i < nw; i += 64) buf[i] = 0u;
     // the unit's raw bytes, symbols and even plane (stripe symbol index)

@@ -6,11 +6,10 @@ the hooked modules must equal the dense forward pass bit for bit. Every case
 prints its name before touching the GPU.
 """
 
-import numpy as np
 import pytest
 import torch
 
-from lossless_huffman_decoding_amd import k3huf, synth
+from lossless_huffman_decoding_amd import synth
 from lossless_huffman_decoding_amd.ondemand import OnDemandWeights
 
 pytestmark = pytest.mark.gpu
