@@ -26,7 +26,9 @@
 
 namespace {
 
-// One 12-wave workgroup per CU. A work unit is half a subblock: 64 lane
+// One 7-wave workgroup per CU (measured on the trunk layer: 7 waves per CU
+// ran 6% faster than 12, and 6, 8, 9 or 10 were in between; 4 or 5 cannot
+// hide the table lookups' latency). A work unit is half a subblock: 64 lane
 // chunks of 256 symbols, lane t decoding chunk t. Every HBM line is read or
 // written in one burst:
 //   - the unit's bitstream is copied into the wave's LDS buffer with
@@ -34,18 +36,18 @@ namespace {
 //     codes exceed the buffer, each lane gathers its own codes phase by
 //     phase instead; the layer's partial last unit is decoded in passes over
 //     consecutive lane ranges);
-//   - the even-plane bytes of two phases (a whole 128-byte line per chunk)
-//     are requested together into registers;
+//   - the even-plane bytes of all four phases (two whole 128-byte lines per
+//     chunk) are requested together into registers as the unit starts;
 //   - each phase's 64 symbols per chunk are staged in LDS, so every output
 //     store instruction writes whole 128-byte lines.
-constexpr int kWaves = 12;
+constexpr int kWaves = 7;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kUnitLanes = 64;                        // lane chunks per work unit
 constexpr int kUnitSyms = kUnitLanes * K3HUF_LANE_SYMS;  // 16384
 constexpr int kUnitsPerSub = K3HUF_LANES / kUnitLanes;   // 2
 constexpr int kPhase = 64;                            // symbols per lane per phase
 constexpr int kPhases = K3HUF_LANE_SYMS / kPhase;    // 4
-constexpr int kSuper = 2;                             // phases per even-plane prefetch
+constexpr int kSuper = 4;                             // phases per even-plane prefetch
 constexpr int kGroups = kPhase / 4;                   // 4-symbol groups per phase (tail path)
 constexpr int kRounds = 64 / 8;                       // write-out rounds (8 chunks each)
 constexpr int kBufBytes = 7680;                       // per-wave bitstream buffer
@@ -269,20 +271,20 @@ __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint32_t
     }
 }
 
-// One super-phase (phases sp and sp + 1) of a full unit (64 chunks of 256
+// One super-phase (kSuper phases from sp) of a full unit (64 chunks of 256
 // symbols, lane t decoding chunk t). The unit's codes are either in `buf`
 // (kGather false: the caller copied them there) or gathered per lane and
 // phase (kGather true). Loads and stores carry no per-chunk condition, so no
 // store waits for the ones before it to complete (vmcnt counts stores too,
 // and a store behind a branch makes the compiler wait for everything
-// outstanding). `late` runs after the first phase.
-template <bool kGather, class Late>
+// outstanding). `after(ph)` runs after each phase ph.
+template <bool kGather, class After>
 __device__ __forceinline__ void decode_super(const uint32_t* tab, uint32_t* buf, uint8_t* stage,
                                              const Unit& un, int sp, int lane, LaneState& ls,
-                                             Late&& late) {
+                                             After&& after) {
     const int sub_line = lane >> 3, part = lane & 7;
     uint2 ev[kRounds][kSuper];
-    // the two phases' even-plane bytes: a whole line per chunk
+    // the super-phase's even-plane bytes: whole lines per chunk
 #pragma unroll
     for (int rr = 0; rr < kRounds; ++rr) {
         const int c = rr * 8 + sub_line;
@@ -330,16 +332,14 @@ __device__ __forceinline__ void decode_super(const uint32_t* tab, uint32_t* buf,
             __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(un.out + 2 * u));
         }
         wave_sync();
-        if (q == 0) late();
+        after(ph);
     }
 }
 
-// Decode a full unit: both super-phases, then the lane checks. `mid` runs
-// between the super-phases and `late` after the third phase (the caller asks
-// for its next unit, then learns it and requests its record). kGather false:
-// the caller has copied the unit's codes from stripe dword j0 on into `buf`.
-// The super-phase loop stays rolled: unrolled, the compiler hoists the
-// second half's addresses and loads and runs out of registers.
+// Decode a full unit: its super-phases, then the lane checks. `mid` runs
+// after the second phase and `late` after the third (the caller asks for its
+// next unit, then learns it and requests its record). kGather false: the
+// caller has copied the unit's codes from stripe dword j0 on into `buf`.
 template <bool kGather, class Mid, class Late>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const uint32_t* tab, uint32_t* buf,
                                             uint8_t* stage, const Unit& un, int j0,
@@ -351,8 +351,10 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const uint32_t*
     const uint32_t pm1_0 = ls.pm1;
 #pragma unroll 1
     for (int sp = 0; sp < kPhases; sp += kSuper) {
-        if (sp == kSuper) mid();
-        decode_super<kGather>(tab, buf, stage, un, sp, lane, ls, [&] { if (sp == kSuper) late(); });
+        decode_super<kGather>(tab, buf, stage, un, sp, lane, ls, [&](int ph) {
+            if (ph == 1) mid();
+            if (ph == 2) late();
+        });
     }
     // a last lookup that ran one symbol past the chunk took that symbol's
     // bits too
