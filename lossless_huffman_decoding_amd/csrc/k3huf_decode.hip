@@ -360,8 +360,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const uint32_t*
     // bits too
     uint32_t used = kGather ? ls.abs - lane_start : ls.pm1 - pm1_0;
     if (ls.cnt > K3HUF_LANE_SYMS) used -= ent_bits(ls.last) - ent_len1(ls.last);
-    if (ls.bad & kBad) flag(a.status, K3HUF_DEV_CODE);
-    if (used != lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
+    // one status update per wave (a corrupt layer would otherwise send an
+    // atomic per lane to the one status word)
+    const bool code_bad = __any((ls.bad & kBad) != 0u), end_bad = __any(used != lane_bits);
+    if (lane == 0 && code_bad) flag(a.status, K3HUF_DEV_CODE);
+    if (lane == 0 && end_bad) flag(a.status, K3HUF_DEV_LANE_END);
 }
 
 // The same for the layer's last unit when it holds fewer than 16384 symbols:
@@ -417,10 +420,9 @@ __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uin
         }
         wave_sync();
     }
-    if (mine) {
-        if (bad & kBad) flag(a.status, K3HUF_DEV_CODE);
-        if (pm1 - pm1_0 != lane_bits) flag(a.status, K3HUF_DEV_LANE_END);
-    }
+    const bool code_bad = __any(mine && (bad & kBad)), end_bad = __any(mine && pm1 - pm1_0 != lane_bits);
+    if (lane == 0 && code_bad) flag(a.status, K3HUF_DEV_CODE);
+    if (lane == 0 && end_bad) flag(a.status, K3HUF_DEV_LANE_END);
 }
 
 // Copy bitstream dwords [j0, j0 + 4 * units) into `buf`, byte-swapped so

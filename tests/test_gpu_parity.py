@@ -211,6 +211,22 @@ def test_corrupt_bits_are_detectable():
     assert st != 0 or not (got == x).all()
 
 
+def test_bitstream_of_noise_is_flagged():
+    """Every code bit replaced by noise over a 16 MiB layer: every unit's
+    lanes end off their index; the kernel flags it and finishes (status is
+    set once per wave, not once per lane)."""
+    x = synth.small_random(14, 16 << 20)
+    blob = O.encode_layer(x).copy()
+    off = _hdr_field_off(blob, 0)
+    bits_off = int(np.frombuffer(bytes(blob[off + 24: off + 28]), "<u4")[0])
+    even_off = int(np.frombuffer(bytes(blob[off + 28: off + 32]), "<u4")[0])
+    rng = np.random.default_rng(15)
+    blob[off + bits_off: off + even_off] = rng.integers(0, 256, even_off - bits_off, dtype=np.uint8)
+    say("noise bitstream")
+    got, st = gpu_decode(blob)
+    assert st & (k3huf.DEV_CODE | k3huf.DEV_LANE_END)
+
+
 def test_unused_slot_is_flagged():
     # one-symbol table: codes are '0'; a '1' bit hits an unused slot
     x = synth.edge_single(n_bytes=65536)
