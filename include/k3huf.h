@@ -246,10 +246,10 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
  * histogram and codelen[256] for the whole layer's odd bytes, MSB-first
  * Huffman bitstream per stripe, even plane raw; "canonical code assignment
  * and Kraft check": depths limited to 12 bits, longest-first canonical codes.
- * The histogram, the lane-chunk bit counts, their per-stripe prefix sums (the
- * subblock index), the bit packing and the even-plane copy run on the GPU;
- * the code lengths and the layout are computed on the host from the GPU's
- * 256-bin histograms.
+ * The histogram, the lane-chunk bit counts, the subblock index (each unit's
+ * start bit from the units before it in its stripe), the bit packing and the
+ * even-plane copy run on the GPU; the code lengths and the layout are
+ * computed on the host from the GPU's 256-bin histograms.
  * d_raw: device, 16-byte aligned, raw_bytes (even, > 0). d_out: device,
  *   16-byte aligned, cap >= k3huf_encode_bound(raw_bytes). d_work: device,
  *   16-byte aligned, work_bytes >= k3huf_encode_work_bytes(raw_bytes); its
@@ -258,8 +258,10 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
  *   histograms, then queues the rest and waits for it, so the container is
  *   complete on return. It allocates no device memory.
  * Returns the container size, K3HUF_E_ARG (bad sizes, alignment or
- * capacity), K3HUF_E_HIP, or K3HUF_E_CORRUPT if d_raw changed during the
- * call (the GPU's bit counts disagree with its histograms).
+ * capacity), K3HUF_E_HIP (a HIP call failed, or a packing wave waited too
+ * long for the start bit of its unit), or K3HUF_E_CORRUPT if d_raw changed
+ * during the call (the GPU's bit counts disagree with its histograms; no
+ * bitstream word is then written past a stripe's bits).
  */
 int64_t k3huf_encode_work_bytes(uint64_t raw_bytes);
 int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,

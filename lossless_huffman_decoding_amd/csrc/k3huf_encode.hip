@@ -10,19 +10,17 @@
 // and whose even bytes are copied raw ("key design points"), plus the
 // subblock/lane index. The code lengths and the layout are computed on the
 // host from the GPU's histograms (they are 256-entry problems); the byte work
-// runs in five kernels:
-//   enc_hist   per-stripe histograms of the odd bytes;
-//   enc_count  code bits of every 256-symbol lane chunk, and of every
-//              subblock (128 chunks);
-//   enc_scan   per stripe: subblock start bits (the subblock records) and
-//              the stripe record;
-//   enc_pack   one wave per half subblock (64 lane chunks, one per lane): the
-//              lanes' start bits (a wave prefix sum), their lane bit counts,
-//              their codes packed into a per-wave LDS buffer (words two lanes
-//              share are OR-ed), then copied out with whole-wave stores, and
-//              the even bytes; a unit's first and last words, which a
-//              neighbouring unit may share, are set aside;
-//   enc_edges  one thread per unit: the words units share, from both sides.
+// runs in four kernels:
+//   enc_hist          per-stripe histograms of the odd bytes;
+//   enc_zero_stripes  clears the stripes' record areas and bitstreams;
+//   enc_pack          one wave per half subblock (64 lane chunks, one per
+//                     lane): the chunks' code bits, the unit's start bit from
+//                     the units before it (a look-back), its codes packed in
+//                     LDS and written out, its records and its even bytes; a
+//                     unit's first and last words, which a neighbouring unit
+//                     may share, are set aside;
+//   enc_edges         one thread per unit: the words units share, from both
+//                     sides.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -40,13 +38,11 @@ using k3huf_detail::StripeGeom;
 constexpr uint32_t kChunksPerStripe = (K3HUF_STRIPE_BYTES / 2) / K3HUF_LANE_SYMS;   // 131072
 constexpr int kHistThreads = 1024;
 constexpr int kHistCopies = 32;        // sub-histograms per block (lane mod 32)
-constexpr int kScanThreads = 1024;     // = subblocks per stripe
-constexpr int kChunkThreads = 256;
-constexpr int kPackWaves = 4;       // waves (units) per packing block
+constexpr uint32_t kSubPerStripe = K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES;   // 1024
+constexpr int kPackWaves = 4;          // waves (units) per packing block
 constexpr int kPackWords = 2048;       // per-wave LDS bit buffer (8 KiB)
 constexpr uint32_t kUnitChunks = 64;   // lane chunks per packing unit
 constexpr uint32_t kUnitsPerStripe = kChunksPerStripe / kUnitChunks;
-static_assert(kScanThreads == K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES, "one scan thread per subblock");
 
 // stripe geometry as the kernels read it
 struct StripeDev {
@@ -61,7 +57,7 @@ struct CodeTable {
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct WorkLayout {
-    uint64_t hist, geom, chunks, subblocks, edges, status, total;
+    uint64_t hist, geom, edges, look, status, total;
 };
 
 // Per packing unit: its first and last bitstream words when another unit
@@ -70,21 +66,19 @@ struct UnitEdges {
     uint32_t first, last, b0, b1;
 };
 
-// work buffer: per-stripe histograms (u64), stripe geometry, lane-chunk bit
-// counts (u32), subblock bit counts then start bits (u32), unit edges, a
-// status word
+// work buffer: per-stripe histograms (u64), stripe geometry, unit edges,
+// the units' look-back words (u64), then a status word and the packing
+// kernel's block ticket
 WorkLayout work_layout(uint64_t raw_bytes) {
     const uint64_t ns = k3huf_detail::stripes_for(raw_bytes);
     const uint64_t n_chunks = (raw_bytes / 2 + K3HUF_LANE_SYMS - 1) / K3HUF_LANE_SYMS;
-    const uint64_t n_sub = (raw_bytes + K3HUF_SUBBLOCK_BYTES - 1) / K3HUF_SUBBLOCK_BYTES;
     const uint64_t n_units = (n_chunks + 63) / 64;
     WorkLayout w;
     w.hist = 0;
     w.geom = align256(w.hist + 256 * 8 * ns);
-    w.chunks = align256(w.geom + sizeof(StripeDev) * ns);
-    w.subblocks = align256(w.chunks + 4 * n_chunks);
-    w.edges = align256(w.subblocks + 4 * n_sub);
-    w.status = align256(w.edges + sizeof(UnitEdges) * n_units);
+    w.edges = align256(w.geom + sizeof(StripeDev) * ns);
+    w.look = align256(w.edges + sizeof(UnitEdges) * n_units);
+    w.status = align256(w.look + 8 * n_units);
     w.total = w.status + 256;
     return w;
 }
@@ -119,7 +113,7 @@ __global__ void enc_fill_zero(uint4* p, uint64_t n16) {
         p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Zero what enc_scan and enc_pack do not overwrite whole: stripe s's record
+// Zero what enc_pack does not overwrite whole: stripe s's record
 // area and bitstream [off, off + even_off) (the stripe header, subblock
 // records and codes are written later; codes are OR-ed into it), and the
 // padding after its even plane. Grid (blocks, stripes).
@@ -175,177 +169,234 @@ __global__ __launch_bounds__(kHistThreads) void enc_hist(const uint8_t* raw, uin
     }
 }
 
-// Code bits of lane chunk c (symbols [256 c, min(256 c + 256, n))). A block's
-// 256 chunks are two whole subblocks (stripes hold whole blocks); their sums
-// go to sb_bits. Each wave counts 64 chunks (32 KiB of raw bytes) with
-// whole-wave loads: load i covers chunks 2i (lanes 0-31) and 2i + 1 (lanes
-// 32-63); each half's sum is reduced across its lanes and kept by the lane
-// that owns the chunk. The layer's last wave, whose chunks may be partial or
-// missing, reads its own chunk per lane instead.
-__global__ __launch_bounds__(kChunkThreads) void enc_count(const uint8_t* raw, uint64_t raw_bytes,
-                                                           uint64_t n_chunks, CodeTable ct,
-                                                           uint32_t* chunk, uint32_t* sb_bits) {
-    __shared__ uint8_t len[256];
-    __shared__ uint32_t wsum[kChunkThreads / 64];
-    if (threadIdx.x < 256) len[threadIdx.x] = uint8_t(ct.e[threadIdx.x] >> 16);
-    __syncthreads();
-    const int lane = threadIdx.x & 63;
-    const uint64_t c0 = uint64_t(blockIdx.x) * kChunkThreads + (threadIdx.x & ~63u);   // wave's first chunk
-    const uint64_t c = c0 + lane;
-    uint32_t bits = 0;
-    if ((c0 + 64) * 2 * K3HUF_LANE_SYMS <= raw_bytes) {
-        const uint4* p = reinterpret_cast<const uint4*>(raw + c0 * 2 * K3HUF_LANE_SYMS);
-#pragma unroll 4
-        for (int i = 0; i < 32; ++i) {
-            const uint4 v = p[i * 64 + lane];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            uint32_t b = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) b += len[(w[k] >> 8) & 0xFFu] + len[w[k] >> 24];
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) b += __shfl_xor(b, o);
-            const uint32_t lo = __builtin_amdgcn_readlane(b, 0), hi = __builtin_amdgcn_readlane(b, 32);
-            bits = lane == 2 * i ? lo : (lane == 2 * i + 1 ? hi : bits);
-        }
-        chunk[c] = bits;
-    } else if (c < n_chunks) {
-        const uint64_t b0 = c * 2 * K3HUF_LANE_SYMS;
-        const uint64_t b1 = min(b0 + 2 * K3HUF_LANE_SYMS, raw_bytes);
-        for (uint64_t i = b0; i < b1; i += 2) bits += len[raw[i + 1]];
-        chunk[c] = bits;
-    }
-    const uint32_t ws = wave_sum(bits);
-    if (lane == 0) wsum[threadIdx.x >> 6] = ws;
-    __syncthreads();
-    if (threadIdx.x < 2) {
-        const uint64_t sb = uint64_t(blockIdx.x) * 2 + threadIdx.x;
-        if (sb * K3HUF_LANES < n_chunks) sb_bits[sb] = wsum[2 * threadIdx.x] + wsum[2 * threadIdx.x + 1];
-    }
-}
-
-// Per stripe (one block, thread j = subblock j): exclusive prefix of the
-// subblock bit counts. Writes each subblock record's start bit and symbol
-// count, the stripe record, and replaces sb_bits[] with the start bits. A
-// total that differs from the host's count (the input changed during the
-// call) sets *status.
-__global__ __launch_bounds__(kScanThreads) void enc_scan(uint8_t* out, const StripeDev* g,
-                                                         uint32_t* sb_bits, uint32_t* status) {
-    __shared__ uint32_t part[kScanThreads];
-    const uint32_t s = blockIdx.x, j = threadIdx.x;
-    const StripeDev G = g[s];
-    uint32_t* sb = sb_bits + uint64_t(s) * kScanThreads;
-    const uint32_t v = j < G.nsb ? sb[j] : 0u;
-    part[j] = v;
-    __syncthreads();
-    for (int d = 1; d < kScanThreads; d <<= 1) {
-        const uint32_t t = j >= uint32_t(d) ? part[j - d] : 0u;
-        __syncthreads();
-        part[j] += t;
-        __syncthreads();
-    }
-    const uint32_t start = part[j] - v;
-    if (j < G.nsb) {
-        uint8_t* rec = out + G.off + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * j;
-        reinterpret_cast<uint32_t*>(rec)[0] = start;
-        reinterpret_cast<uint32_t*>(rec)[1] = min(uint32_t(K3HUF_SUBBLOCK_SYMS), G.n - j * K3HUF_SUBBLOCK_SYMS);
-        sb[j] = start;
-    }
-    if (j == kScanThreads - 1) {
-        if (part[j] != G.nbits) atomicOr(status, 1u);
-        uint32_t* hd = reinterpret_cast<uint32_t*>(out + G.off);
-        hd[0] = G.raw;
-        hd[1] = G.n;
-        hd[2] = G.nbits;
-        hd[3] = G.bit_bytes;
-        hd[4] = s * (K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES);
-        hd[5] = G.nsb;
-        hd[6] = G.bits_off;
-        hd[7] = G.even_off;
-    }
-}
-
 // One wave per unit of 64 lane chunks (half a subblock), lane t packing
-// chunk t, in four phases of 64 symbols per chunk (small LDS rows keep 12
-// waves per CU):
-//   A. whole-wave loads of the phase's raw bytes (8 lanes cover the 128
-//      bytes of one chunk's phase); the odd bytes go to the chunk's LDS row,
-//      the even bytes straight to the even plane (8 lanes write half a line);
-//   B. each lane appends its row's codes, MSB first, to the unit's words in
-//      the wave's LDS bit buffer (a lane's first and last words may be
-//      shared with its neighbours and are OR-ed in; the words between are its
-//      own).
-// Then the buffer is written out with whole-wave stores, except the unit's
-// first and last words when a neighbouring unit shares them: those go to the
-// unit's edge record, and enc_edges writes each shared word once from both
-// halves (atomics on words another CU is writing cost more than the rest of
-// the copy). A unit whose codes exceed the buffer packs straight into memory,
-// OR-ing every shared word (enc_zero_stripes cleared the bitstream), and
-// leaves its edge record zero. The layer's last unit, which may end inside a
-// chunk, stages its rows symbol by symbol.
+// chunk t:
+//   A. the chunks' code bits: whole-wave loads of the unit's raw bytes (8
+//      lanes cover the 128 raw bytes of one chunk's quarter), each lane adding
+//      up the code lengths of the odd bytes it holds; the sums over each
+//      chunk's 8 lanes and their prefix sum give every lane its start bit
+//      within the unit and the unit's bit count;
+//   B. the start bit: the unit publishes its bit count in its look-back word
+//      (state << 32 | bits; state 1: the unit's own count, 2: the stripe's
+//      bits up to and including the unit) and reads the words of the units
+//      before it back to the nearest one holding a stripe prefix; units
+//      without one yet add their counts. A stripe's first unit publishes its
+//      prefix at once;
+//   C. in four phases of 64 symbols per chunk (small LDS rows keep 12 waves
+//      per CU), the odd bytes go to the chunks' LDS rows and the even bytes
+//      straight to the even plane; each lane appends its row's codes, MSB
+//      first, to the unit's words in the wave's LDS bit buffer from bit 0 of
+//      the buffer (a lane's first and last words may be shared with its
+//      neighbours and are OR-ed in);
+//   D. the buffer is shifted to the start bit's place in its word as it is
+//      written out with whole-wave stores, except the unit's first and last
+//      words when a neighbouring unit shares them: those go to the unit's
+//      edge record, and enc_edges writes each shared word once from both
+//      halves (atomics on words another CU is writing cost more than the rest
+//      of the copy).
+// The look-back is requested before the packing and resolved after it, so
+// the wait is mostly covered. A unit whose codes exceed the buffer resolves
+// its start bit first and packs straight into memory, OR-ing every shared
+// word (enc_zero_stripes cleared the bitstream), and leaves its edge words
+// zero. The layer's last unit, which may end inside a chunk, stages its rows
+// symbol by symbol. Blocks take their units in ticket order, so a unit only
+// waits for units of blocks that are already running, which publish their
+// counts before they wait for anything; the wait is bounded all the same (a
+// wave that gives up flags bit 2 of *status).
+constexpr uint32_t kSpinLimit = 1u << 22;   // look-back re-reads before a wave gives up (~0.2 s)
+
+// look-back words are read and written whole at device scope (every XCD
+// sees them)
+__device__ __forceinline__ uint64_t look_load(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void look_store(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 constexpr int kPackPhases = 4;
 constexpr int kPhSyms = K3HUF_LANE_SYMS / kPackPhases;   // 64 symbols per chunk per phase
 constexpr int kRowBytes = kPhSyms + 4;    // 64 odd bytes + 4: rows start in distinct LDS banks
 
 __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, uint64_t raw_bytes,
                                                             uint64_t n_chunks, CodeTable ct,
-                                                            const StripeDev* g, const uint32_t* chunk,
-                                                            const uint32_t* sb_start, UnitEdges* edges,
-                                                            uint8_t* out) {
+                                                            const StripeDev* g, UnitEdges* edges,
+                                                            uint64_t* look, uint32_t* ticket,
+                                                            uint32_t* status, uint8_t* out) {
     __shared__ uint32_t tab[256];
+    __shared__ uint8_t lens[256];
+    __shared__ uint32_t blk;
     __shared__ uint32_t stage[kPackWaves][kPackWords];
     __shared__ __attribute__((aligned(16))) uint8_t rows[kPackWaves][64 * kRowBytes];
-    if (threadIdx.x < 256) tab[threadIdx.x] = ct.e[threadIdx.x];
+    for (int i = threadIdx.x; i < 256; i += kPackWaves * 64) {
+        tab[i] = ct.e[i];
+        lens[i] = uint8_t(ct.e[i] >> 16);
+    }
+    if (threadIdx.x == 0) blk = atomicAdd(ticket, 1u);
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint64_t u = uint64_t(blockIdx.x) * kPackWaves + wave;   // unit
+    const uint64_t u = uint64_t(blk) * kPackWaves + wave;   // unit
     const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
     if (u >= n_units) return;
     const uint32_t s = uint32_t(u / kUnitsPerStripe);
     const StripeDev G = g[s];
     const uint64_t sbg = u / 2;                         // global subblock
     const uint32_t half = uint32_t(u & 1);
-    const uint32_t sbl = uint32_t(sbg % kScanThreads);  // subblock within the stripe
-    // bit counts of both halves of the subblock: this unit starts after the
-    // first half when it is the second
-    const uint64_t ca = sbg * K3HUF_LANES + lane, cb = ca + kUnitChunks;
-    const uint32_t ba = ca < n_chunks ? chunk[ca] : 0u, bb = cb < n_chunks ? chunk[cb] : 0u;
-    const uint32_t ia = wave_incl_scan(ba, lane), ib = wave_incl_scan(bb, lane);
-    const uint32_t bits = half ? bb : ba, incl = half ? ib : ia;
-    const uint32_t u0 = sb_start[sbg] + (half ? __shfl(ia, 63) : 0u);
-    const uint32_t u1 = u0 + __shfl(incl, 63);
+    const uint32_t sbl = uint32_t(sbg % kSubPerStripe);  // subblock within the stripe
+    const uint64_t us0 = uint64_t(s) * kUnitsPerStripe;  // the stripe's first unit
     const uint64_t c0 = u * kUnitChunks;                // first chunk of the unit
     const uint64_t c = c0 + lane;
     const bool has = c < n_chunks;
-    uint8_t* rec = out + G.off + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * sbl;
-    if (has) reinterpret_cast<uint16_t*>(rec + 8)[half * kUnitChunks + lane] = uint16_t(bits);
-
-    uint32_t* words = reinterpret_cast<uint32_t*>(out + G.off + G.bits_off);
-    uint32_t* buf = stage[wave];
-    uint8_t* row = rows[wave];
-    const uint32_t w0 = u0 >> 5, nw = ((u1 + 31) >> 5) - w0;
-    const bool staged = uint32_t(__builtin_amdgcn_readfirstlane(nw)) <= uint32_t(kPackWords);   // uniform
-    if (staged)
-        for (uint32_t i = lane; i < nw; i += 64) buf[i] = 0u;
-    // the unit's raw bytes, symbols and even plane (stripe symbol index)
     const uint8_t* uraw = raw + c0 * 2 * K3HUF_LANE_SYMS;
     const uint64_t n_syms = raw_bytes / 2;
     const bool tail = (c0 + kUnitChunks) * K3HUF_LANE_SYMS > n_syms;   // layer's last unit, partial
-    uint8_t* ueven = out + G.off + G.even_off + uint32_t(c0 % kChunksPerStripe) * K3HUF_LANE_SYMS;
     const int cnt = has ? int(min(uint64_t(K3HUF_LANE_SYMS), n_syms - c * K3HUF_LANE_SYMS)) : 0;
 
-    const uint32_t b0 = u0 + incl - bits;
+    // phase ph's raw bytes: chunk i * 8 + sub, bytes [q * 16, q * 16 + 16) of
+    // its phase (8 lanes per chunk phase of 128 raw bytes)
+    const int q = lane & 7, sub = lane >> 3;
+    uint4 rv[8];
+    auto load_into = [&](uint4* r, int ph) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r[i] = *reinterpret_cast<const uint4*>(uraw + uint64_t(i * 8 + sub) * 512 + ph * 2 * kPhSyms + q * 16);
+    };
+    auto load_raw = [&](int ph) { load_into(rv, ph); };
+
+    // A. the lane chunks' code bits: every lane adds up the code lengths of
+    // the odd bytes it loads (phases 3, 2, 1, 0, two in flight at a time;
+    // phase 0's bytes stay in registers for C), then the 8 lanes of each
+    // chunk are summed and lane t takes chunk t's sum
+    uint32_t bits = 0;
+    if (!tail) {
+        uint32_t part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        uint4 ra[8];
+        auto count = [&](const uint4* r) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t o0 = __builtin_amdgcn_perm(r[i].y, r[i].x, 0x07050301u);
+                const uint32_t o1 = __builtin_amdgcn_perm(r[i].w, r[i].z, 0x07050301u);
+                part[i] += lens[o0 & 0xFFu] + lens[(o0 >> 8) & 0xFFu] + lens[(o0 >> 16) & 0xFFu] + lens[o0 >> 24] +
+                           lens[o1 & 0xFFu] + lens[(o1 >> 8) & 0xFFu] + lens[(o1 >> 16) & 0xFFu] + lens[o1 >> 24];
+            }
+        };
+        load_into(ra, 3);
+        load_into(rv, 2);
+        count(ra);
+        load_into(ra, 1);
+        count(rv);
+        load_into(rv, 0);
+        count(ra);
+        count(rv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t p = part[i];
+            p += __shfl_xor(p, 1);
+            p += __shfl_xor(p, 2);
+            p += __shfl_xor(p, 4);
+            const uint32_t x = __shfl(p, (lane & 7) * 8);
+            bits = (lane >> 3) == i ? x : bits;
+        }
+    } else {
+        for (int j = 0; j < cnt; ++j) bits += lens[uraw[uint64_t(lane) * 512 + 2 * j + 1]];
+    }
+
+    // B. the unit's bits, published; the look-back's first window (64 units,
+    // a word per lane) is requested now and resolved after the packing
+    const uint32_t incl = wave_incl_scan(bits, lane);
+    const uint32_t total = __shfl(incl, 63);
+    const bool first_unit = u == us0;
+    if (lane == 0) look_store(&look[u], (uint64_t(first_unit ? 2u : 1u) << 32) | total);
+    const uint32_t nrel = (total + 31) >> 5;   // words of the unit's own stream
+    const bool staged = uint32_t(__builtin_amdgcn_readfirstlane(nrel)) + 1 <= uint32_t(kPackWords);   // uniform
+    int64_t base = int64_t(u) - 1;
+    uint64_t lw = 0;
+    auto request = [&]() {
+        const int64_t j = base - lane;
+        lw = j >= int64_t(us0) ? look_load(&look[j]) : (2ull << 32);
+    };
+    uint32_t u0 = 0;
+    // sums the window back to the nearest stripe prefix, re-reading words
+    // not yet published (bounded: a wave that gives up flags *status)
+    auto resolve = [&]() {
+        uint32_t spins = 0;
+        for (;;) {
+            const uint32_t f = uint32_t(lw >> 32), v = uint32_t(lw);
+            const uint64_t pm = __ballot(f == 2u), zm = __ballot(f == 0u);
+            if (pm) {
+                const int lp = __builtin_ctzll(pm);
+                if ((zm & ((2ull << lp) - 1ull)) == 0) {
+                    u0 += wave_sum(lane <= lp ? v : 0u);
+                    break;
+                }
+            } else if (zm == 0) {
+                u0 += wave_sum(v);
+                base -= 64;
+                request();
+                continue;
+            }
+            if (++spins > kSpinLimit) {
+                if (lane == 0) atomicOr(status, 2u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            request();
+        }
+        if (lane == 0) look_store(&look[u], (2ull << 32) | uint64_t(u0 + total));
+    };
+    // records: lane bit counts, the subblock's start bit and symbol count,
+    // the stripe record (its first unit) and the stripe's total (its last);
+    // false when the unit would pass the stripe's bits (its input changed
+    // since the histogram): it then writes no bitstream words
+    auto records = [&]() -> bool {
+        const uint32_t u1 = u0 + total;
+        uint8_t* rec = out + G.off + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * sbl;
+        if (has) reinterpret_cast<uint16_t*>(rec + 8)[half * kUnitChunks + lane] = uint16_t(bits);
+        if (half == 0 && lane == 0) {
+            reinterpret_cast<uint32_t*>(rec)[0] = u0;
+            reinterpret_cast<uint32_t*>(rec)[1] = min(uint32_t(K3HUF_SUBBLOCK_SYMS), G.n - sbl * K3HUF_SUBBLOCK_SYMS);
+        }
+        if (first_unit && lane < 8) {
+            const uint32_t hv[8] = {G.raw, G.n, G.nbits, G.bit_bytes, s * kSubPerStripe, G.nsb, G.bits_off, G.even_off};
+            uint32_t x = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x = lane == k ? hv[k] : x;
+            reinterpret_cast<uint32_t*>(out + G.off)[lane] = x;
+        }
+        const bool last_unit = u + 1 == n_units || (u + 1) % kUnitsPerStripe == 0;
+        if (lane == 0 && ((last_unit && u1 != G.nbits) || u1 > G.nbits)) atomicOr(status, 1u);
+        return u1 <= G.nbits;
+    };
+    if (!first_unit) request();
+    if (!staged) {
+        if (!first_unit) resolve();
+        if (!records()) return;
+    }
+
+    // C. the codes: into the wave's LDS buffer from bit 0 (staged), or
+    // straight into the stripe's bitstream at the unit's start bit
+    uint32_t* words = reinterpret_cast<uint32_t*>(out + G.off + G.bits_off);
+    uint32_t* buf = stage[wave];
+    uint8_t* row = rows[wave];
+    if (staged)
+        for (uint32_t i = lane; i <= nrel; i += 64) buf[i] = 0u;
+    // the unit's even plane (stripe symbol index)
+    uint8_t* ueven = out + G.off + G.even_off + uint32_t(c0 % kChunksPerStripe) * K3HUF_LANE_SYMS;
+
+    const uint32_t b0 = (staged ? 0u : u0) + incl - bits;
     uint32_t w = b0 >> 5;
     uint64_t acc = 0;            // pending bits, the earliest at bit 63
     uint32_t nacc = b0 & 31u;    // word w's bits before acc's top belong to the previous lane
     bool first = true;
-    // word w of the stripe's bitstream (bit 31 = earliest); shared words are OR-ed
+    // word w of the unit's buffer or of the stripe's bitstream (bit 31 =
+    // earliest); words two lanes share are OR-ed
     auto emit = [&](uint32_t v, bool shared) {
         if (staged) {
             if (shared)
-                atomicOr(&buf[w - w0], v);
+                atomicOr(&buf[w], v);
             else
-                buf[w - w0] = v;
+                buf[w] = v;
         } else {
             if (shared)
                 atomicOr(&words[w], bswap32(v));
@@ -363,7 +414,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
         acc |= uint64_t(code) << (64u - nacc - l);
         nacc += l;
         const bool full = nacc >= 32;
-        atomicOr(&buf[w - w0], full ? uint32_t(acc >> 32) : 0u);
+        atomicOr(&buf[w], full ? uint32_t(acc >> 32) : 0u);
         w += full ? 1u : 0u;
         acc = full ? acc << 32 : acc;
         nacc -= full ? 32u : 0u;
@@ -382,17 +433,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
         }
     };
 
-    // phase ph's raw bytes: chunk i * 8 + sub, bytes [q * 16, q * 16 + 16) of
-    // its phase (8 lanes per chunk phase of 128 raw bytes); the next phase's
-    // are requested as soon as this phase's are staged
-    const int q = lane & 7, sub = lane >> 3;
-    uint4 rv[8];
-    auto load_raw = [&](int ph) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            rv[i] = *reinterpret_cast<const uint4*>(uraw + uint64_t(i * 8 + sub) * 512 + ph * 2 * kPhSyms + q * 16);
-    };
-    // B. phase ph's codes, from the lane's row
+    // phase ph's codes, from the lane's row
     auto pack_phase = [&](int ph) {
         if (!has) return;
         const int m = min(max(cnt - ph * kPhSyms, 0), kPhSyms);
@@ -419,13 +460,13 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
         }
     };
     if (!tail) {
-        load_raw(0);
-        // unrolled, so the raw registers need no copies between phases (a
-        // copy waits for every outstanding load and store)
+        // phase 0's raw bytes are in rv from A; unrolled, so the raw
+        // registers need no copies between phases (a copy waits for every
+        // outstanding load and store)
 #pragma unroll
         for (int ph = 0; ph < kPackPhases; ++ph) {
-            // A. stage this phase's odd bytes and keep its even bytes; the
-            // next phase's raw bytes are requested before the even bytes are
+            // stage this phase's odd bytes and keep its even bytes; the next
+            // phase's raw bytes are requested before the even bytes are
             // written, so waiting for those loads never waits for these
             // stores (loads and stores retire in issue order)
             uint2 ev[8];
@@ -462,18 +503,33 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     }
     if (has && nacc > 0) emit(uint32_t(acc >> 32), true);
     wave_sync();
-    // the unit's edge record: its shared first and last words (staged units)
-    // and its bit range
-    uint32_t* er = reinterpret_cast<uint32_t*>(edges + u);
+    if (!staged) {
+        // packed in place: the edge record holds only the bit range
+        if (lane < 4) reinterpret_cast<uint32_t*>(edges + u)[lane] = lane < 2 ? 0u : lane == 2 ? u0 : u0 + total;
+        return;
+    }
+
+    // D. the start bit, the records, then the buffer shifted to the start
+    // bit's position in its word and written out: word w0 + i of the stripe
+    // takes the low r bits of buffer word i - 1 and the high 32 - r bits of
+    // buffer word i (r = u0 mod 32; buf[nrel] is zero)
+    if (!first_unit) resolve();
+    if (!records()) return;
+    const uint32_t u1 = u0 + total;
+    const uint32_t r = u0 & 31u, w0 = u0 >> 5, nw = ((u1 + 31) >> 5) - w0;
+    auto word = [&](uint32_t i) -> uint32_t {
+        const uint32_t hi = buf[i], lo = i ? buf[i - 1] : 0u;
+        return r ? (lo << (32u - r)) | (hi >> r) : hi;
+    };
+    // the unit's edge record: its first and last words when a neighbouring
+    // unit shares them, and its bit range
     if (lane < 4) {
-        const uint32_t f = staged && (u0 & 31u) ? bswap32(buf[0]) : 0u;
-        const uint32_t l = staged && (u1 & 31u) ? bswap32(buf[min(nw, uint32_t(kPackWords)) - 1]) : 0u;
-        er[lane] = lane == 0 ? f : lane == 1 ? l : lane == 2 ? u0 : u1;
+        const uint32_t first_w = r ? bswap32(word(0)) : 0u;
+        const uint32_t last_w = (u1 & 31u) ? bswap32(word(nw - 1)) : 0u;
+        reinterpret_cast<uint32_t*>(edges + u)[lane] = lane == 0 ? first_w : lane == 1 ? last_w : lane == 2 ? u0 : u1;
     }
-    if (staged) {
-        const uint32_t i0 = (u0 & 31u) ? 1u : 0u, i1 = (u1 & 31u) ? nw - 1 : nw;
-        for (uint32_t i = i0 + lane; i < i1; i += 64) words[w0 + i] = bswap32(buf[i]);
-    }
+    const uint32_t i0 = r ? 1u : 0u, i1 = (u1 & 31u) ? nw - 1 : nw;
+    for (uint32_t i = i0 + lane; i < i1; i += 64) words[w0 + i] = bswap32(word(i));
 }
 
 // One thread per packing unit: the word holding the unit's first bit, when
@@ -537,12 +593,12 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     const uint64_t n_chunks = (raw_bytes / 2 + K3HUF_LANE_SYMS - 1) / K3HUF_LANE_SYMS;
     auto* hist = reinterpret_cast<unsigned long long*>(work + wl.hist);
     auto* geom = reinterpret_cast<StripeDev*>(work + wl.geom);
-    auto* chunk = reinterpret_cast<uint32_t*>(work + wl.chunks);
-    auto* sb_bits = reinterpret_cast<uint32_t*>(work + wl.subblocks);
-    auto* status = reinterpret_cast<uint32_t*>(work + wl.status);
+    auto* look = reinterpret_cast<uint64_t*>(work + wl.look);
+    auto* status = reinterpret_cast<uint32_t*>(work + wl.status);   // [0] status, [1] block ticket
     auto* edges = reinterpret_cast<UnitEdges*>(work + wl.edges);
 
-    // 1. per-stripe histograms (the status word is cleared with them)
+    // 1. per-stripe histograms (the look-back words, the status word and the
+    // block ticket are cleared with them)
     hipLaunchKernelGGL(enc_fill_zero, dim3(64), dim3(256), 0, st, reinterpret_cast<uint4*>(work),
                        wl.total / 16);
     const int hist_res = resident_blocks(enc_hist, kHistThreads);
@@ -582,14 +638,10 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
             hipSuccess)
         return K3HUF_E_HIP;
     hipLaunchKernelGGL(enc_zero_stripes, dim3(64, ns), dim3(256), 0, st, out, geom);
-    const unsigned chunk_blocks = unsigned((n_chunks + kChunkThreads - 1) / kChunkThreads);
-    hipLaunchKernelGGL(enc_count, dim3(chunk_blocks), dim3(kChunkThreads), 0, st, raw, raw_bytes,
-                       n_chunks, ct, chunk, sb_bits);
-    hipLaunchKernelGGL(enc_scan, dim3(ns), dim3(kScanThreads), 0, st, out, geom, sb_bits, status);
     const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
     hipLaunchKernelGGL(enc_pack, dim3(unsigned((n_units + kPackWaves - 1) / kPackWaves)),
-                       dim3(kPackWaves * 64), 0, st, raw, raw_bytes, n_chunks, ct, geom, chunk, sb_bits,
-                       edges, out);
+                       dim3(kPackWaves * 64), 0, st, raw, raw_bytes, n_chunks, ct, geom, edges, look,
+                       status + 1, status, out);
     hipLaunchKernelGGL(enc_edges, dim3(unsigned((n_units + 255) / 256)), dim3(256), 0, st, edges,
                        n_units, geom, out);
     if (launched()) return K3HUF_E_HIP;
@@ -597,7 +649,7 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     if (hipMemcpyAsync(&bad, status, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
         return K3HUF_E_HIP;
-    return bad ? K3HUF_E_CORRUPT : int64_t(total);
+    return (bad & 2u) ? K3HUF_E_HIP : bad ? K3HUF_E_CORRUPT : int64_t(total);
 }
 
 }  // extern "C"
