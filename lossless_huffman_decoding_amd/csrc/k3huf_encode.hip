@@ -176,12 +176,13 @@ __global__ __launch_bounds__(kHistThreads) void enc_hist(const uint8_t* raw, uin
 //      up the code lengths of the odd bytes it holds; the sums over each
 //      chunk's 8 lanes and their prefix sum give every lane its start bit
 //      within the unit and the unit's bit count;
-//   B. the start bit: the unit publishes its bit count in its look-back word
-//      (state << 32 | bits; state 1: the unit's own count, 2: the stripe's
-//      bits up to and including the unit) and reads the words of the units
-//      before it back to the nearest one holding a stripe prefix; units
-//      without one yet add their counts. A stripe's first unit publishes its
-//      prefix at once;
+//   B. the start bit, by a decoupled look-back (the single-pass prefix scan
+//      of Merrill and Garland, 2016): the unit publishes its bit count in its
+//      look-back word (state << 32 | bits; state 1: the unit's own count, 2:
+//      the stripe's bits up to and including the unit) and reads the words
+//      of the units before it back to the nearest one holding a stripe
+//      prefix, adding the counts of those without one yet. A stripe's first
+//      unit publishes its prefix at once;
 //   C. in four phases of 64 symbols per chunk (small LDS rows keep 12 waves
 //      per CU), the odd bytes go to the chunks' LDS rows and the even bytes
 //      straight to the even plane; each lane appends its row's codes, MSB
