@@ -10,17 +10,17 @@
 // and whose even bytes are copied raw ("key design points"), plus the
 // subblock/lane index. The code lengths and the layout are computed on the
 // host from the GPU's histograms (they are 256-entry problems); the byte work
-// runs in four kernels:
-//   enc_hist          per-stripe histograms of the odd bytes;
-//   enc_zero_stripes  clears the stripes' record areas and bitstreams;
-//   enc_pack          one wave per half subblock (64 lane chunks, one per
-//                     lane): the chunks' code bits, the unit's start bit from
-//                     the units before it (a look-back), its codes packed in
-//                     LDS and written out, its records and its even bytes; a
-//                     unit's first and last words, which a neighbouring unit
-//                     may share, are set aside;
-//   enc_edges         one thread per unit: the words units share, from both
-//                     sides.
+// runs in three kernels:
+//   enc_hist   per-stripe histograms of the odd bytes;
+//   enc_pack   one wave per half subblock (64 lane chunks, one per lane): the
+//              chunks' code bits, the unit's start bit from the units before
+//              it (a look-back), its codes packed in LDS and written out, its
+//              records, its even bytes and the stripe's zero padding; a
+//              unit's first and last words, which a neighbouring unit may
+//              share, are set aside;
+//   enc_edges  one thread per unit: the words units share, OR-ed from both
+//              sides.
+// Every byte of the container is written; nothing is cleared beforehand.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -113,22 +113,6 @@ __global__ void enc_fill_zero(uint4* p, uint64_t n16) {
         p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Zero what enc_pack does not overwrite whole: stripe s's record
-// area and bitstream [off, off + even_off) (the stripe header, subblock
-// records and codes are written later; codes are OR-ed into it), and the
-// padding after its even plane. Grid (blocks, stripes).
-__global__ void enc_zero_stripes(uint8_t* out, const StripeDev* g) {
-    const StripeDev G = g[blockIdx.y];
-    uint4* p = reinterpret_cast<uint4*>(out + G.off);
-    const uint32_t n16 = G.even_off / 16;
-    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x)
-        p[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (blockIdx.x == 0) {
-        const uint64_t e0 = G.off + G.even_off + G.n, e1 = G.off + ((uint64_t(G.even_off) + G.n + 255) & ~255ull);
-        for (uint64_t i = e0 + threadIdx.x; i < e1; i += blockDim.x) out[i] = 0;
-    }
-}
-
 // Per-stripe histograms of the odd bytes: grid (blocks per stripe, stripes),
 // sized so that the whole grid is resident at once (a partial last round of
 // blocks left most CUs idle: 64 blocks per stripe took 7% longer than 28). Each block counts a slice of its stripe into 32 interleaved LDS
@@ -197,9 +181,9 @@ __global__ __launch_bounds__(kHistThreads) void enc_hist(const uint8_t* raw, uin
 //      of the copy).
 // The look-back is requested before the packing and resolved after it, so
 // the wait is mostly covered. A unit whose codes exceed the buffer resolves
-// its start bit first and packs straight into memory, OR-ing every shared
-// word (enc_zero_stripes cleared the bitstream), and leaves its edge words
-// zero. The layer's last unit, which may end inside a chunk, stages its rows
+// its start bit first, clears its own words and packs straight into memory
+// (the words its lanes share are OR-ed), setting aside the words it shares
+// with neighbouring units as a buffered unit does. The layer's last unit, which may end inside a chunk, stages its rows
 // symbol by symbol. Blocks take their units in ticket order, so a unit only
 // waits for units of blocks that are already running, which publish their
 // counts before they wait for anything; the wait is bounded all the same (a
@@ -350,10 +334,14 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     // the stripe record (its first unit) and the stripe's total (its last);
     // false when the unit would pass the stripe's bits (its input changed
     // since the histogram): it then writes no bitstream words
+    const bool last_unit = u + 1 == n_units || (u + 1) % kUnitsPerStripe == 0;
+    uint32_t* words = reinterpret_cast<uint32_t*>(out + G.off + G.bits_off);
     auto records = [&]() -> bool {
         const uint32_t u1 = u0 + total;
         uint8_t* rec = out + G.off + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * sbl;
-        if (has) reinterpret_cast<uint16_t*>(rec + 8)[half * kUnitChunks + lane] = uint16_t(bits);
+        uint16_t* lane_bits = reinterpret_cast<uint16_t*>(rec + 8);
+        lane_bits[half * kUnitChunks + lane] = uint16_t(bits);   // 0 for lanes past the layer's end
+        if (u + 1 == n_units && half == 0) lane_bits[kUnitChunks + lane] = 0;
         if (half == 0 && lane == 0) {
             reinterpret_cast<uint32_t*>(rec)[0] = u0;
             reinterpret_cast<uint32_t*>(rec)[1] = min(uint32_t(K3HUF_SUBBLOCK_SYMS), G.n - sbl * K3HUF_SUBBLOCK_SYMS);
@@ -365,20 +353,42 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
             for (int k = 0; k < 8; ++k) x = lane == k ? hv[k] : x;
             reinterpret_cast<uint32_t*>(out + G.off)[lane] = x;
         }
-        const bool last_unit = u + 1 == n_units || (u + 1) % kUnitsPerStripe == 0;
+        // the zero padding: after the subblock records (the stripe's first
+        // unit), after the bitstream's last word and after the even plane
+        // (its last unit)
+        if (first_unit)
+            for (uint32_t i = K3HUF_STRIPE_HDR_BYTES + K3HUF_SUBBLOCK_REC_BYTES * G.nsb + lane; i < G.bits_off; i += 64)
+                out[G.off + i] = 0;
+        if (last_unit) {
+            for (uint32_t i = ((G.nbits + 31) >> 5) + lane; i < (G.even_off - G.bits_off) / 4; i += 64) words[i] = 0u;
+            const uint64_t e0 = G.off + G.even_off + G.n, e1 = G.off + ((uint64_t(G.even_off) + G.n + 255) & ~255ull);
+            for (uint64_t i = e0 + lane; i < e1; i += 64) out[i] = 0;
+        }
         if (lane == 0 && ((last_unit && u1 != G.nbits) || u1 > G.nbits)) atomicOr(status, 1u);
-        return u1 <= G.nbits;
+        if (u1 > G.nbits) return false;
+        // the unit's last word, when it ends inside it, is the OR of its part
+        // and the next unit's (enc_edges): cleared here, where no other unit
+        // writes it (the first word of a unit is the last of the one before)
+        if (lane == 0 && (u1 & 31u)) words[u1 >> 5] = 0u;
+        return true;
     };
     if (!first_unit) request();
+    uint32_t* buf = stage[wave];
     if (!staged) {
         if (!first_unit) resolve();
         if (!records()) return;
+        // the words only this unit writes start at zero (its lanes OR the
+        // words they share); its first and last words, when neighbouring units
+        // share them, are collected in buf[0] and buf[1] for its edge record
+        const uint32_t u1 = u0 + total;
+        for (uint32_t i = (u0 >> 5) + ((u0 & 31u) ? 1u : 0u) + lane; i < (u1 >> 5); i += 64) words[i] = 0u;
+        if (lane < 2) buf[lane] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+        wave_sync();
     }
 
     // C. the codes: into the wave's LDS buffer from bit 0 (staged), or
     // straight into the stripe's bitstream at the unit's start bit
-    uint32_t* words = reinterpret_cast<uint32_t*>(out + G.off + G.bits_off);
-    uint32_t* buf = stage[wave];
     uint8_t* row = rows[wave];
     if (staged)
         for (uint32_t i = lane; i <= nrel; i += 64) buf[i] = 0u;
@@ -386,6 +396,8 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     uint8_t* ueven = out + G.off + G.even_off + uint32_t(c0 % kChunksPerStripe) * K3HUF_LANE_SYMS;
 
     const uint32_t b0 = (staged ? 0u : u0) + incl - bits;
+    // in-place packing: the unit's first and last words when shared
+    const uint32_t wf = (u0 & 31u) ? (u0 >> 5) : ~0u, wl = ((u0 + total) & 31u) ? ((u0 + total) >> 5) : ~0u;
     uint32_t w = b0 >> 5;
     uint64_t acc = 0;            // pending bits, the earliest at bit 63
     uint32_t nacc = b0 & 31u;    // word w's bits before acc's top belong to the previous lane
@@ -398,6 +410,10 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
                 atomicOr(&buf[w], v);
             else
                 buf[w] = v;
+        } else if (w == wf) {
+            atomicOr(&buf[0], v);
+        } else if (w == wl) {
+            atomicOr(&buf[1], v);
         } else {
             if (shared)
                 atomicOr(&words[w], bswap32(v));
@@ -505,8 +521,12 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     if (has && nacc > 0) emit(uint32_t(acc >> 32), true);
     wave_sync();
     if (!staged) {
-        // packed in place: the edge record holds only the bit range
-        if (lane < 4) reinterpret_cast<uint32_t*>(edges + u)[lane] = lane < 2 ? 0u : lane == 2 ? u0 : u0 + total;
+        // packed in place: the edge record holds the shared words and the bit range
+        if (lane < 4) {
+            const uint32_t first_w = (u0 & 31u) ? bswap32(buf[0]) : 0u;
+            const uint32_t last_w = ((u0 + total) & 31u) ? bswap32(buf[1]) : 0u;
+            reinterpret_cast<uint32_t*>(edges + u)[lane] = lane == 0 ? first_w : lane == 1 ? last_w : lane == 2 ? u0 : u0 + total;
+        }
         return;
     }
 
@@ -536,9 +556,10 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
 // One thread per packing unit: the word holding the unit's first bit, when
 // the unit before it (same stripe) ends inside it, is the OR of both units'
 // parts, and the stripe's last unit also writes its own last word. Each such
-// word is written by exactly one thread; a unit that packed straight into
-// memory has already OR-ed its part in (its edge record is zero), so the
-// parts are OR-ed onto what memory holds.
+// word is written by exactly one thread. enc_pack left every such word zero
+// (a unit clears its last word when it ends inside it), so the parts are
+// OR-ed onto zero; OR-ing also gives the right word when a unit's first and
+// last words are one word.
 __global__ void enc_edges(const UnitEdges* edges, uint64_t n_units, const StripeDev* g, uint8_t* out) {
     const uint64_t u = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (u >= n_units) return;
@@ -638,7 +659,6 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
         hipMemcpyAsync(geom, gd.data(), gd.size() * sizeof(StripeDev), hipMemcpyHostToDevice, st) !=
             hipSuccess)
         return K3HUF_E_HIP;
-    hipLaunchKernelGGL(enc_zero_stripes, dim3(64, ns), dim3(256), 0, st, out, geom);
     const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
     hipLaunchKernelGGL(enc_pack, dim3(unsigned((n_units + kPackWaves - 1) / kPackWaves)),
                        dim3(kPackWaves * 64), 0, st, raw, raw_bytes, n_chunks, ct, geom, edges, look,

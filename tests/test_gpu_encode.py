@@ -24,8 +24,19 @@ def say(*a):
     print("[gpu-case]", *a, flush=True)
 
 
+def garbage_buffers(n_bytes):
+    """Output and work buffers for an encode of n_bytes, filled with a
+    non-zero pattern: a container byte the kernels fail to write then shows
+    up as a mismatch against the oracle."""
+    d_out = torch.full((k3huf.encode_bound(n_bytes),), 0x5A, dtype=torch.uint8, device=DEV)
+    d_work = torch.full((k3huf.encode_work_bytes(n_bytes),), 0xC3, dtype=torch.uint8, device=DEV)
+    return d_out, d_work
+
+
 def gpu_encode(x, d_out=None, d_work=None):
     d_x = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    if d_out is None:
+        d_out, d_work = garbage_buffers(x.size)
     blob = k3huf.encode_layer_dev(d_x, d_out, d_work)
     return blob.cpu().numpy(), d_x
 
@@ -66,7 +77,7 @@ def test_encode_trunk_layer_matches_oracle_and_round_trips():
     x, want = oracle_container("trunk", synth.trunk_layer)
     say("encode trunk", x.size)
     d_x = torch.from_numpy(x).to(DEV)
-    d_blob = k3huf.encode_layer_dev(d_x)
+    d_blob = k3huf.encode_layer_dev(d_x, *garbage_buffers(x.size))
     got = d_blob.cpu().numpy()
     assert got.size == want.size
     assert (got == want).all()
@@ -82,10 +93,7 @@ def test_encode_reuses_buffers_across_calls():
     the first call must not leak into the second)."""
     big = synth.small_random(901, 5 * 65536 + 66)
     small = synth.small_random(902, 2 * 65536 + 10)
-    d_out = torch.empty(k3huf.encode_bound(big.size), dtype=torch.uint8, device=DEV)
-    d_work = torch.empty(k3huf.encode_work_bytes(big.size), dtype=torch.uint8, device=DEV)
-    d_out.fill_(0x5A)
-    d_work.fill_(0xC3)
+    d_out, d_work = garbage_buffers(big.size)
     say("encode reuse")
     a, _ = gpu_encode(big, d_out, d_work)
     b, _ = gpu_encode(small, d_out, d_work)
