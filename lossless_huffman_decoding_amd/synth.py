@@ -195,6 +195,28 @@ def small_random(seed: int, n_bytes: int, sigma: float = 0.02) -> np.ndarray:
     return f64_to_bf16_bytes(rng.standard_normal(n_bytes // 2) * sigma)
 
 
+def mixed_spans(seed: int, n_bytes: int, lo: int = 4 << 10, hi: int = 160 << 10) -> np.ndarray:
+    """Spans of N(0, 0.02) bf16 values alternating with spans of uniform
+    random bytes, span lengths uniform over even sizes in [lo, hi] (the first
+    span's kind drawn too). With one code table per layer the uniform spans
+    take long codes and the weight spans short ones, so stretches of dense
+    and sparse bitstream meet at arbitrary offsets."""
+    if n_bytes % 2:
+        raise ValueError("bf16 layer needs an even byte count")
+    rng = np.random.default_rng(seed)
+    out = np.empty(n_bytes, dtype=np.uint8)
+    pos, uniform = 0, bool(rng.integers(0, 2))
+    while pos < n_bytes:
+        m = min(n_bytes - pos, 2 * int(rng.integers(lo // 2, hi // 2 + 1)))
+        if uniform:
+            out[pos:pos + m] = rng.integers(0, 256, m, dtype=np.uint8)
+        else:
+            out[pos:pos + m] = f64_to_bf16_bytes(rng.standard_normal(m // 2) * 0.02)
+        pos += m
+        uniform = not uniform
+    return out
+
+
 def small_trunk_matrix(seed: int, rows: int, cols: int) -> np.ndarray:
     """One rows x cols bf16 weight drawn like a trunk matrix: N(0, s) with s
     log-uniform in [0.005, 0.05], both from default_rng(seed)."""

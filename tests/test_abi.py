@@ -105,6 +105,13 @@ def test_packer_edge_layers_decode_with_oracle():
         assert a.size == b.size and (a == b).all(), name
 
 
+def test_packer_mixed_spans_matches_oracle():
+    x = synth.mixed_spans(77, (8 << 20) + 2 * 65536 + 118)
+    a = O.encode_layer(x)
+    b = k3huf.encode_layer(x)
+    assert a.size == b.size and (a == b).all()
+
+
 def test_packer_bad_args():
     assert k3huf.lib().k3huf_encode_bound(3) == k3huf.E_ARG
     assert k3huf.lib().k3huf_encode_bound(0) == k3huf.E_ARG

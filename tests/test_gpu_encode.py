@@ -87,6 +87,24 @@ def test_encode_trunk_layer_matches_oracle_and_round_trips():
     assert torch.equal(d_dec, d_x)
 
 
+def test_encode_mixed_spans_matches_oracle_and_round_trips():
+    """Spans of uniform bytes (units too large for the packing kernel's LDS
+    buffer, which pack straight into memory) alternate with weight spans
+    (buffered units) across three stripes, so the two kinds of unit meet at
+    about 1100 unit boundaries and share their boundary words."""
+    x = synth.mixed_spans(78, (2 << 26) + 3 * 65536 + 1234)
+    want = O.encode_layer(x)
+    say("encode mixed spans", x.size)
+    got, d_x = gpu_encode(x)
+    assert got.size == want.size
+    assert (got == want).all()
+    say("encode mixed spans: decode back")
+    d_blob = torch.from_numpy(got).to(DEV)
+    d_dec, st = gpu_decode_dev(d_blob, x.size)
+    assert st == 0
+    assert torch.equal(d_dec, d_x)
+
+
 def test_encode_reuses_buffers_across_calls():
     """Two calls in a row on the same output and work buffers, the second
     with a smaller layer: both containers equal the oracle's (scratch state of

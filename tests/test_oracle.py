@@ -350,6 +350,16 @@ def test_roundtrip_edge_layers():
             assert set(h["codelen"].tolist()) == {8}
 
 
+def test_roundtrip_mixed_spans():
+    """Weight spans and uniform-byte spans alternating at arbitrary even
+    offsets: one table serves short and long codes, and dense and sparse
+    stretches of bitstream meet inside subblocks and lane chunks."""
+    x = synth.mixed_spans(77, (8 << 20) + 2 * 65536 + 118)
+    blob = _roundtrip_checks(x)
+    h = hdr(blob)
+    assert (h["codelen"] > 0).sum() == 256 and h["codelen"].max() >= 9 and h["codelen"].min() >= 1
+
+
 @pytest.mark.slow
 def test_roundtrip_heavy():
     x = synth.heavy()
