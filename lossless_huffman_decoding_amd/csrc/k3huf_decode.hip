@@ -104,13 +104,15 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // counters sharing a line delayed the tickets enough to stall every unit.
 // The counters live in this array, which exists once per device for the
 // life of the process, in kSchedSlots slots; the last workgroup of a launch
-// clears its slot. Each stream gets a slot of its own on first use: launches
-// on one stream never overlap, so they can share one, and launches on
-// different streams get different slots for the first kSchedSlots streams
-// of a device. Two launches that run at the same time on one slot would
-// take each other's tickets (units left undecoded); that needs more than
-// kSchedSlots streams, or a graph replay overlapping a decode on the stream
-// the graph was captured on.
+// clears its slot. The first kSchedSlots streams of a device each get a slot
+// of their own on first use: launches on one stream never overlap, so they
+// can share it. Two launches running at the same time on one slot would take
+// each other's tickets and leave units undecoded, so a launch that cannot
+// have a slot to itself takes no tickets at all: launches on later streams,
+// and launches captured into a graph (a graph may be replayed on any stream,
+// beside a decode on the one it was captured on), hand out every position
+// statically (wave slot v of workgroup b takes positions v * blocks + b + i T
+// for i = 0, 1, ...), which is slower but shares nothing.
 constexpr uint32_t kSchedSlots = 256;
 constexpr uint32_t kGroupsPerSlot = 8;
 constexpr uint32_t kCounterStride = 64;                               // words: one 256-byte line
@@ -126,7 +128,8 @@ struct DecodeArgs {
     uint32_t n_sub;
     uint32_t n_stripes;
     uint32_t* status;
-    uint32_t slot;        // work-counter slot of this launch
+    uint32_t slot;        // work-counter slot of this launch (when dyn)
+    uint32_t dyn;         // 1: positions after the first round from the slot's tickets; 0: static
 };
 
 __device__ __forceinline__ uint32_t ld32(const uint8_t* p) {
@@ -609,10 +612,10 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         bool asked = false;
         uint32_t h_next = 0xFFFFFFFFu;
         auto ask = [&]() {
-            if (lane == 0) ticket = atomicAdd(&slot[group * kCounterStride], 1u);
+            if (a.dyn && lane == 0) ticket = atomicAdd(&slot[group * kCounterStride], 1u);
             asked = true;
         };
-        auto next_pos = [&]() { return uniform(T + group + groups * lane_value(ticket, 0)); };
+        auto next_pos = [&]() { return a.dyn ? uniform(T + group + groups * lane_value(ticket, 0)) : h + T; };
         auto learn = [&]() {
             h_next = next_pos();
             request_rec(h_next);
@@ -711,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
 
     // the last workgroup to finish clears this launch's counter slot
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (a.dyn && threadIdx.x == 0) {
         const uint32_t done = atomicAdd(&slot[kGroupsPerSlot * kCounterStride], 1u);
         if (done == gridDim.x - 1)
             for (uint32_t g = 0; g <= kGroupsPerSlot; ++g) atomicExch(&slot[g * kCounterStride], 0u);
@@ -725,18 +728,22 @@ struct DevInfo {
 
 std::mutex g_mu;
 std::vector<DevInfo> g_dev;
-std::map<std::pair<int, void*>, uint32_t> g_stream_slot;   // (device, stream) -> counter slot
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+std::map<std::pair<int, void*>, uint32_t> g_stream_slot;   // (device, stream) -> counter slot or kNoSlot
 std::vector<uint32_t> g_next_slot;                        // per device
 
-// The device's launch geometry and the counter slot of `stream` on it.
+// The device's launch geometry and the counter slot of `stream` on it
+// (kNoSlot once the device's kSchedSlots slots are taken).
 int device_info(void* stream, DevInfo* out, uint32_t* slot) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return K3HUF_E_HIP;
     std::lock_guard<std::mutex> lk(g_mu);
     if (int(g_next_slot.size()) <= dev) g_next_slot.resize(dev + 1, 0u);
     auto it = g_stream_slot.find({dev, stream});
-    if (it == g_stream_slot.end())
-        it = g_stream_slot.emplace(std::make_pair(dev, stream), g_next_slot[dev]++ % kSchedSlots).first;
+    if (it == g_stream_slot.end()) {
+        const uint32_t s = g_next_slot[dev] < kSchedSlots ? g_next_slot[dev]++ : kNoSlot;
+        it = g_stream_slot.emplace(std::make_pair(dev, stream), s).first;
+    }
     *slot = it->second;
     if (int(g_dev.size()) <= dev) g_dev.resize(dev + 1);
     DevInfo& d = g_dev[dev];
@@ -774,6 +781,15 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     uint32_t slot = 0;
     int rc = device_info(stream, &di, &slot);
     if (rc) return rc;
+    // a launch captured into a graph may later run beside any other launch:
+    // it takes the static schedule (so does one whose capture state cannot be
+    // read; the failed query's error is cleared)
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &capture) != hipSuccess) {
+        (void)hipGetLastError();
+        capture = hipStreamCaptureStatusActive;
+    }
+    const bool dyn = slot != kNoSlot && capture == hipStreamCaptureStatusNone;
     DecodeArgs a;
     a.blob = static_cast<const uint8_t*>(d_blob);
     a.blob_bytes = blob_bytes;
@@ -783,7 +799,8 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     a.n_sub = uint32_t(n_sub);
     a.n_stripes = uint32_t(n_stripes);
     a.status = d_status;
-    a.slot = slot;
+    a.slot = dyn ? slot : 0u;
+    a.dyn = dyn ? 1u : 0u;
     // one workgroup per unit up to a full chip: the first round's positions
     // are wave-major, so a layer of fewer units than CUs gets a CU per unit
     const uint64_t want = n_sub * kUnitsPerSub;

@@ -61,6 +61,8 @@ class OnDemandWeights:
         self._handles = []
         self._pending = [None] * n   # group whose decode each buffer holds or awaits
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
+        # decodes may run on any stream: the cleared status must be in place
+        torch.cuda.current_stream(self.device).synchronize()
         self._lib = k3huf.lib()
         self._decoded = [torch.cuda.Event() for _ in range(n)]
         if lookahead:

@@ -76,6 +76,7 @@ def test_on_demand_on_a_side_stream(lookahead):
     for m in model:
         od.attach(m)
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())   # x and the weights were made on the current stream
     say("ondemand side stream", lookahead)
     with torch.cuda.stream(s), torch.no_grad():
         got = model(x)

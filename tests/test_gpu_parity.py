@@ -38,6 +38,9 @@ def gpu_decode(blob, lut=None, out_bytes=None, stream=None):
     n = out_bytes
     d_out = torch.full((n,), 0xA5, dtype=torch.uint8, device=DEV)  # poison
     d_status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    if stream is not None:
+        # the poison and the cleared status are queued on the current stream
+        stream.wait_stream(torch.cuda.current_stream())
     k3huf.decode_layer(d_blob, d_lut, d_out, d_status, stream)
     torch.cuda.synchronize()
     return d_out.cpu().numpy(), int(d_status.item())
@@ -278,6 +281,7 @@ def test_ring_decodes_layers_in_order(n_slots, n_streams):
         with torch.cuda.stream(by_handle[handle]):
             results[k].copy_(slots[slot][: sizes[k]])
 
+    torch.cuda.synchronize()   # buffers prepared on the current stream
     say("ring", n_slots, n_streams)
     k3huf.decode_ring(layers, slots, streams, consume, status)
     torch.cuda.synchronize()
@@ -319,6 +323,7 @@ def test_host_ring_decodes_layers_in_order(n_stage, n_slots, n_streams):
         with torch.cuda.stream(by_handle[handle]):
             results[k].copy_(slots[slot][: sizes[k]])
 
+    torch.cuda.synchronize()   # buffers prepared on the current stream
     say("host ring", n_stage, n_slots, n_streams)
     k3huf.decode_ring_host(layers, stages, slots, copy_stream, streams, consume, status)
     torch.cuda.synchronize()
@@ -349,6 +354,7 @@ def test_host_ring_repeated_containers_and_pageable_memory():
         with torch.cuda.stream(by_handle[handle]):
             results[k].copy_(slots[slot])
 
+    torch.cuda.synchronize()   # buffers prepared on the current stream
     say("host ring repeat/pageable")
     k3huf.decode_ring_host(layers, stages, slots, copy_stream, streams, consume, status)
     torch.cuda.synchronize()
@@ -367,6 +373,7 @@ def test_concurrent_decodes_on_many_streams():
     outs = [torch.full((x.size,), 0xA5, dtype=torch.uint8, device=DEV) for x in xs]
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     streams = [torch.cuda.Stream() for _ in range(6)]
+    torch.cuda.synchronize()   # poison and status prepared on the current stream
     say("concurrent streams", len(streams), len(xs))
     for k, (db, dl) in enumerate(dev):
         k3huf.decode_layer(db, dl, outs[k], status, streams[k % 6])
@@ -374,3 +381,98 @@ def test_concurrent_decodes_on_many_streams():
     assert int(status.item()) == 0
     for k, x in enumerate(xs):
         assert (outs[k].cpu().numpy() == x).all(), k
+
+
+@pytest.fixture(scope="module")
+def many_streams():
+    """300 new streams, each registered by a decode (a stream takes one of
+    the device's 256 work-counter slots at its first decode), so that the
+    last ones are past the slot limit whatever streams earlier tests used."""
+    x = synth.small_random(611, 3 * 65536 + 514)
+    blob = O.encode_layer(x)
+    db, dl = to_dev(blob, k3huf.build_table(k3huf.layer_info(blob)["codelen"]))
+    streams = [torch.cuda.Stream() for _ in range(300)]
+    outs = [torch.full((x.size,), 0xA5, dtype=torch.uint8, device=DEV) for _ in streams]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()   # poison and status prepared on the current stream
+    say("register 300 streams")
+    for s, o in zip(streams, outs):
+        k3huf.decode_layer(db, dl, o, status, s)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for k, o in enumerate(outs):
+        assert (o.cpu().numpy() == x).all(), k
+    return streams
+
+
+def test_concurrent_decodes_past_the_counter_slots(many_streams):
+    """Decodes queued at once on a stream with a counter slot and on streams
+    past the slot limit (static schedule) all give their layers back."""
+    xs = [synth.small_random(620 + k, (24 << 20) + 2 * k * 65536 + 6) for k in range(3)]
+    blobs = [O.encode_layer(x) for x in xs]
+    dev = [to_dev(b, k3huf.build_table(k3huf.layer_info(b)["codelen"])) for b in blobs]
+    outs = [torch.empty(x.size, dtype=torch.uint8, device=DEV) for x in xs]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    streams = [many_streams[0], many_streams[-1], many_streams[-2]]
+    for rep in range(3):
+        for o in outs:
+            o.fill_(0xA5)
+        torch.cuda.synchronize()
+        say("concurrent past the slot limit, round", rep)
+        for k in range(3):
+            k3huf.decode_layer(dev[k][0], dev[k][1], outs[k], status, streams[k])
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        for k, x in enumerate(xs):
+            assert (outs[k].cpu().numpy() == x).all(), (rep, k)
+
+
+@pytest.mark.parametrize("layer", ["tiny", "edge_fib40", "edge_single", "edge_uniform", "heavy", "trunk"])
+def test_static_schedule_parity(many_streams, layer):
+    """Every config decodes right on a stream past the counter slots (all
+    positions handed out statically)."""
+    gen = {"tiny": synth.tiny, "heavy": synth.heavy, "trunk": synth.trunk_layer,
+           **dict(synth.CONFIGS["edge"])}[layer]
+    x, blob = oracle_container(layer, gen)
+    say("static schedule", layer, x.size)
+    got, st = gpu_decode(blob, stream=many_streams[-1])
+    assert st == 0
+    assert (got == x).all()
+
+
+def test_graph_replays_beside_decodes_on_the_capture_stream():
+    """A decode captured into a graph on stream s, replayed on the default
+    stream while another decode runs on s: both layers come back, on every
+    replay (eager work and synchronization between replays)."""
+    x1 = synth.small_random(631, (16 << 20) + 2 * 65536 + 18)
+    x2 = synth.small_random(632, (24 << 20) + 6)
+    b1, b2 = O.encode_layer(x1), O.encode_layer(x2)
+    d1 = to_dev(b1, k3huf.build_table(k3huf.layer_info(b1)["codelen"]))
+    d2 = to_dev(b2, k3huf.build_table(k3huf.layer_info(b2)["codelen"]))
+    out1 = torch.empty(x1.size, dtype=torch.uint8, device=DEV)
+    out2 = torch.empty(x2.size, dtype=torch.uint8, device=DEV)
+    st1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    st2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()   # status words cleared on the current stream
+    say("graph capture of a decode")
+    with torch.cuda.stream(s):
+        k3huf.decode_layer(d2[0], d2[1], out2, st2)     # the stream's first decode takes its slot
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        k3huf.decode_layer(d1[0], d1[1], out1, st1)
+    for rep in range(3):
+        out1.fill_(0xA5)
+        out2.fill_(0x5A)
+        st1.zero_()
+        st2.zero_()
+        torch.cuda.synchronize()
+        say("graph replay beside a decode on the capture stream", rep)
+        with torch.cuda.stream(s):
+            k3huf.decode_layer(d2[0], d2[1], out2, st2)
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(st1.item()) == 0 and int(st2.item()) == 0
+        assert (out1.cpu().numpy() == x1).all(), rep
+        assert (out2.cpu().numpy() == x2).all(), rep
