@@ -146,12 +146,15 @@ int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out);
  * loop" (MSB-first bit window, one table lookup per symbol) and "key design
  * points" (even plane interleaved back at even offsets).
  * Concurrency: any number of decodes may be queued and may run at the same
- * time, on any streams and from graph replays. Launches on the first 256
- * distinct streams of a device hand out most of their work through counters
- * of their stream's own (per-device, process-lifetime) slot. Launches on
- * later streams, and launches made while the stream is being captured into
- * a graph, use a static schedule that shares nothing (0.383 ms against
- * 0.352 ms on the trunk layer); so do all of a graph's replays.
+ * time, on any streams and from graph replays. A layer of more than five
+ * rounds of work units (above about 290 MB of output on MI355X) launched on
+ * one of the first 256 distinct streams of a device hands out its later
+ * units through counters of its stream's own (per-device, process-lifetime)
+ * slot. Every other launch uses a static schedule that shares nothing: for
+ * smaller layers it is as fast or faster, for larger ones slower (0.383 ms
+ * against 0.352 ms on the trunk layer). That covers launches on later
+ * streams and launches made while the stream is being captured into a graph
+ * (and so all of a graph's replays).
  */
 int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut,
                        void* d_out, size_t out_bytes, void* stream, uint32_t* d_status);

@@ -112,8 +112,10 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // and launches captured into a graph (a graph may be replayed on any stream,
 // beside a decode on the one it was captured on), hand out every position
 // statically (wave slot v of workgroup b takes positions v * blocks + b + i T
-// for i = 0, 1, ...), which is slower but shares nothing.
+// for i = 0, 1, ...), which shares nothing. So do layers of at most
+// kDynRounds rounds of units, for which the static schedule is as fast.
 constexpr uint32_t kSchedSlots = 256;
+constexpr uint32_t kDynRounds = 5;   // tickets only for layers of more rounds of units than this
 constexpr uint32_t kGroupsPerSlot = 8;
 constexpr uint32_t kCounterStride = 64;                               // words: one 256-byte line
 constexpr uint32_t kSlotWords = (kGroupsPerSlot + 1) * kCounterStride;  // tickets per group, workgroups done
@@ -789,7 +791,15 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
         (void)hipGetLastError();
         capture = hipStreamCaptureStatusActive;
     }
-    const bool dyn = slot != kNoSlot && capture == hipStreamCaptureStatusNone;
+    // tickets pay off only over many rounds of units: at up to about five
+    // rounds the static schedule measured as fast or faster (trunk-recipe
+    // layers: 0.97-1.01x of the ticketed time at 1.1-4.6 rounds, 1.03-1.08x
+    // at 6.9-20 rounds)
+    const uint64_t want = n_sub * kUnitsPerSub;
+    const uint64_t resident = uint64_t(di.cus) * uint64_t(di.wg_per_cu);
+    const unsigned grid = unsigned(want < resident ? want : resident);
+    const bool dyn = slot != kNoSlot && capture == hipStreamCaptureStatusNone &&
+                     want > uint64_t(kDynRounds) * grid * kWaves;
     DecodeArgs a;
     a.blob = static_cast<const uint8_t*>(d_blob);
     a.blob_bytes = blob_bytes;
@@ -801,11 +811,9 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     a.status = d_status;
     a.slot = dyn ? slot : 0u;
     a.dyn = dyn ? 1u : 0u;
-    // one workgroup per unit up to a full chip: the first round's positions
-    // are wave-major, so a layer of fewer units than CUs gets a CU per unit
-    const uint64_t want = n_sub * kUnitsPerSub;
-    const uint64_t resident = uint64_t(di.cus) * uint64_t(di.wg_per_cu);
-    const unsigned grid = unsigned(want < resident ? want : resident);
+    // one workgroup per unit up to a full chip (grid above): the first round's
+    // positions are wave-major, so a layer of fewer units than CUs gets a CU
+    // per unit
     hipLaunchKernelGGL(k3huf_decode_kernel, dim3(grid), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? K3HUF_OK : K3HUF_E_HIP;

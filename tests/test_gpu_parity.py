@@ -406,9 +406,10 @@ def many_streams():
 
 
 def test_concurrent_decodes_past_the_counter_slots(many_streams):
-    """Decodes queued at once on a stream with a counter slot and on streams
-    past the slot limit (static schedule) all give their layers back."""
-    xs = [synth.small_random(620 + k, (24 << 20) + 2 * k * 65536 + 6) for k in range(3)]
+    """Decodes queued at once on a stream with a counter slot (layers of
+    more than five rounds of units take tickets) and on streams past the slot
+    limit (static schedule) all give their layers back."""
+    xs = [synth.small_random(620 + k, (330 << 20) + 2 * k * 65536 + 6) for k in range(3)]
     blobs = [O.encode_layer(x) for x in xs]
     dev = [to_dev(b, k3huf.build_table(k3huf.layer_info(b)["codelen"])) for b in blobs]
     outs = [torch.empty(x.size, dtype=torch.uint8, device=DEV) for x in xs]
@@ -425,6 +426,20 @@ def test_concurrent_decodes_past_the_counter_slots(many_streams):
         assert int(status.item()) == 0
         for k, x in enumerate(xs):
             assert (outs[k].cpu().numpy() == x).all(), (rep, k)
+
+
+@pytest.mark.parametrize("kind", ["weights", "mixed_spans"])
+def test_ticketed_schedule_parity(kind):
+    """Layers of more than five rounds of units (about 12,800 units against
+    1,792 wave slots) take their later units from the counters; ragged
+    tails, three stripes plus a partial one."""
+    n = (400 << 20) + 2 * 65536 + 514
+    x = synth.small_random(641, n) if kind == "weights" else synth.mixed_spans(642, n)
+    blob = O.encode_layer(x)
+    say("ticketed schedule", kind, x.size)
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got == x).all()
 
 
 @pytest.mark.parametrize("layer", ["tiny", "edge_fib40", "edge_single", "edge_uniform", "heavy", "trunk"])
