@@ -94,8 +94,9 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // demand: position T + x + G i goes to whichever wave of workgroup group x
 // (block mod G, G = min(8, blocks): one group per XCD) takes ticket i from
 // group x's counter. On-demand handout is needed because the waves of a CU
-// do not progress at one rate: a SIMD issues from its oldest wave first, and
-// the first of its three waves runs about 1.5 times as fast as the third. A
+// do not progress at one rate: a SIMD issues from its oldest wave first (with
+// three waves per SIMD the first ran about 1.5 times as fast as the third),
+// and over many rounds the static order leaves some waves far behind. A
 // wave asks for its next position halfway through its current unit, and
 // reads the answer (and requests that unit's record) as its last phase
 // starts, so it holds at most a quarter unit of work ahead and the grid's
