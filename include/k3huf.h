@@ -150,9 +150,10 @@ int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out);
  * rounds of work units (above about 290 MB of output on MI355X) launched on
  * one of the first 256 distinct streams of a device hands out its later
  * units through counters of its stream's own (per-device, process-lifetime)
- * slot. Every other launch uses a static schedule that shares nothing: for
- * smaller layers it is as fast or faster, for larger ones slower (0.383 ms
- * against 0.352 ms on the trunk layer). That covers launches on later
+ * slot. Every other launch hands each workgroup's share of units to its
+ * waves from a counter in the workgroup's own LDS, which shares nothing: for
+ * smaller layers it is as fast or faster, for larger ones slower (about
+ * 1.05 times the time on the trunk layer). That covers launches on later
  * streams and launches made while the stream is being captured into a graph
  * (and so all of a graph's replays).
  */

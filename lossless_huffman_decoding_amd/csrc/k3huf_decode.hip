@@ -109,14 +109,17 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // of their own on first use: launches on one stream never overlap, so they
 // can share it. Two launches running at the same time on one slot would take
 // each other's tickets and leave units undecoded, so a launch that cannot
-// have a slot to itself takes no tickets at all: launches on later streams,
+// have a slot to itself uses no device counter: launches on later streams,
 // and launches captured into a graph (a graph may be replayed on any stream,
-// beside a decode on the one it was captured on), hand out every position
-// statically (wave slot v of workgroup b takes positions v * blocks + b + i T
-// for i = 0, 1, ...), which shares nothing. So do layers of at most
-// kDynRounds rounds of units, for which the static schedule is as fast.
+// beside a decode on the one it was captured on), keep each workgroup to its
+// own share of positions (b, b + blocks, b + 2 blocks, ...) and hand that
+// share to its waves from a counter in the workgroup's LDS, which shares
+// nothing. That evens out the waves of a CU but not the CUs: on the trunk
+// layer it takes 1.048 times as long as the device counters (every position
+// handed out statically: 1.089 times). Layers of at most kDynRounds rounds of
+// units take the workgroup counters too, as they are as fast there.
 constexpr uint32_t kSchedSlots = 256;
-constexpr uint32_t kDynRounds = 5;   // tickets only for layers of more rounds of units than this
+constexpr uint32_t kDynRounds = 5;   // device counters only for layers of more rounds of units than this
 constexpr uint32_t kGroupsPerSlot = 8;
 constexpr uint32_t kCounterStride = 64;                               // words: one 256-byte line
 constexpr uint32_t kSlotWords = (kGroupsPerSlot + 1) * kCounterStride;  // tickets per group, workgroups done
@@ -132,7 +135,7 @@ struct DecodeArgs {
     uint32_t n_stripes;
     uint32_t* status;
     uint32_t slot;        // work-counter slot of this launch (when dyn)
-    uint32_t dyn;         // 1: positions after the first round from the slot's tickets; 0: static
+    uint32_t dyn;         // positions after the first round: 1 from the slot's counters, 0 from the workgroup's
 };
 
 __device__ __forceinline__ uint32_t ld32(const uint8_t* p) {
@@ -531,6 +534,7 @@ __device__ __forceinline__ RecLanes load_rec(const uint8_t* rec, bool has_next, 
 
 __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    __shared__ uint32_t local_ticket;   // the workgroup's own counter (launches without a slot)
     uint32_t* tab = reinterpret_cast<uint32_t*>(lds);  // at LDS address 0
 
     // layer header must describe exactly this call (uniform over the grid;
@@ -586,6 +590,7 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         }
     };
     request_rec(h);
+    if (threadIdx.x == 0) local_ticket = 0u;
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
         const int i = int(threadIdx.x) + q * kThreads;
@@ -615,10 +620,17 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         bool asked = false;
         uint32_t h_next = 0xFFFFFFFFu;
         auto ask = [&]() {
-            if (a.dyn && lane == 0) ticket = atomicAdd(&slot[group * kCounterStride], 1u);
+            if (lane == 0)
+                ticket = a.dyn ? atomicAdd(&slot[group * kCounterStride], 1u) : atomicAdd(&local_ticket, 1u);
             asked = true;
         };
-        auto next_pos = [&]() { return a.dyn ? uniform(T + group + groups * lane_value(ticket, 0)) : h + T; };
+        // with the device counters: position T + group + groups * ticket;
+        // with the workgroup's own: the workgroup's share b + blocks * j, j
+        // past the first round's kWaves
+        auto next_pos = [&]() {
+            return a.dyn ? uniform(T + group + groups * lane_value(ticket, 0))
+                         : uniform(blockIdx.x + gridDim.x * (kWaves + lane_value(ticket, 0)));
+        };
         auto learn = [&]() {
             h_next = next_pos();
             request_rec(h_next);
@@ -785,17 +797,17 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     int rc = device_info(stream, &di, &slot);
     if (rc) return rc;
     // a launch captured into a graph may later run beside any other launch:
-    // it takes the static schedule (so does one whose capture state cannot be
-    // read; the failed query's error is cleared)
+    // it uses the workgroup counters (so does one whose capture state cannot
+    // be read; the failed query's error is cleared)
     hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &capture) != hipSuccess) {
         (void)hipGetLastError();
         capture = hipStreamCaptureStatusActive;
     }
-    // tickets pay off only over many rounds of units: at up to about five
-    // rounds the static schedule measured as fast or faster (trunk-recipe
-    // layers: 0.97-1.01x of the ticketed time at 1.1-4.6 rounds, 1.03-1.08x
-    // at 6.9-20 rounds)
+    // device counters pay off only over many rounds of units: at up to about
+    // five rounds the workgroup counters measured as fast or faster
+    // (trunk-recipe layers: 0.94-1.00x of the device-counter time at 1.1-4.6
+    // rounds, 1.03-1.05x at 6.9-20 rounds)
     const uint64_t want = n_sub * kUnitsPerSub;
     const uint64_t resident = uint64_t(di.cus) * uint64_t(di.wg_per_cu);
     const unsigned grid = unsigned(want < resident ? want : resident);

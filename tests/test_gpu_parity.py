@@ -407,8 +407,8 @@ def many_streams():
 
 def test_concurrent_decodes_past_the_counter_slots(many_streams):
     """Decodes queued at once on a stream with a counter slot (layers of
-    more than five rounds of units take tickets) and on streams past the slot
-    limit (static schedule) all give their layers back."""
+    more than five rounds of units take its counters) and on streams past the
+    slot limit (workgroup counters) all give their layers back."""
     xs = [synth.small_random(620 + k, (330 << 20) + 2 * k * 65536 + 6) for k in range(3)]
     blobs = [O.encode_layer(x) for x in xs]
     dev = [to_dev(b, k3huf.build_table(k3huf.layer_info(b)["codelen"])) for b in blobs]
@@ -431,8 +431,8 @@ def test_concurrent_decodes_past_the_counter_slots(many_streams):
 @pytest.mark.parametrize("kind", ["weights", "mixed_spans"])
 def test_ticketed_schedule_parity(kind):
     """Layers of more than five rounds of units (about 12,800 units against
-    1,792 wave slots) take their later units from the counters; ragged
-    tails, three stripes plus a partial one."""
+    1,792 wave slots) take their later units from the device counters;
+    ragged tails, six stripes plus a partial one."""
     n = (400 << 20) + 2 * 65536 + 514
     x = synth.small_random(641, n) if kind == "weights" else synth.mixed_spans(642, n)
     blob = O.encode_layer(x)
@@ -443,13 +443,13 @@ def test_ticketed_schedule_parity(kind):
 
 
 @pytest.mark.parametrize("layer", ["tiny", "edge_fib40", "edge_single", "edge_uniform", "heavy", "trunk"])
-def test_static_schedule_parity(many_streams, layer):
-    """Every config decodes right on a stream past the counter slots (all
-    positions handed out statically)."""
+def test_unslotted_stream_parity(many_streams, layer):
+    """Every config decodes right on a stream past the counter slots (each
+    workgroup's share of units handed to its waves from its own counter)."""
     gen = {"tiny": synth.tiny, "heavy": synth.heavy, "trunk": synth.trunk_layer,
            **dict(synth.CONFIGS["edge"])}[layer]
     x, blob = oracle_container(layer, gen)
-    say("static schedule", layer, x.size)
+    say("unslotted stream", layer, x.size)
     got, st = gpu_decode(blob, stream=many_streams[-1])
     assert st == 0
     assert (got == x).all()
