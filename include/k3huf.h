@@ -261,7 +261,9 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
  *   contents are scratch. All buffers are caller-owned.
  * stream: hipStream_t as void*. The call is synchronous: it waits for the
  *   histograms, then queues the rest and waits for it, so the container is
- *   complete on return. It allocates no device memory.
+ *   complete on return. It allocates no device memory. Its host round trips
+ *   go through pinned host buffers (about 2.1 KB per stripe) leased from a
+ *   process-wide pool that keeps them until the process ends.
  * Returns the container size, K3HUF_E_ARG (bad sizes, alignment or
  * capacity), K3HUF_E_HIP (a HIP call failed, or a packing wave waited too
  * long for the start bit of its unit), or K3HUF_E_CORRUPT if d_raw changed

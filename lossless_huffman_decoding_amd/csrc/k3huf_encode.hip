@@ -25,6 +25,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "k3huf.h"
@@ -576,6 +577,50 @@ __global__ void enc_edges(const UnitEdges* edges, uint64_t n_units, const Stripe
 // a kernel launch's status as a return code
 int launched() { return hipGetLastError() == hipSuccess ? K3HUF_OK : K3HUF_E_HIP; }
 
+// Pinned host staging for the encoder's round trips through the host (the
+// histograms in, the layer header and stripe geometry out, the status word
+// in), so that they run as DMA in stream order: copies from pageable memory
+// are staged by the host, which first waits for the stream. Buffers are
+// leased from a process-wide pool (a call takes one and gives it back) and
+// are never freed while the process runs; a lease given back while copies
+// from it may be queued (an error path) waits for its stream first.
+std::mutex g_pin_mu;
+std::vector<std::pair<void*, size_t>> g_pin_pool;
+
+struct PinnedLease {
+    void* p = nullptr;
+    size_t n = 0;
+    hipStream_t pending = nullptr;   // stream with copies queued from p, if any
+    bool queued = false;
+    explicit PinnedLease(size_t want) {
+        std::lock_guard<std::mutex> lk(g_pin_mu);
+        for (size_t i = 0; i < g_pin_pool.size(); ++i)
+            if (g_pin_pool[i].second >= want) {
+                p = g_pin_pool[i].first;
+                n = g_pin_pool[i].second;
+                g_pin_pool.erase(g_pin_pool.begin() + long(i));
+                return;
+            }
+        if (!g_pin_pool.empty()) {   // too small for this call: replace it
+            (void)hipHostFree(g_pin_pool.back().first);
+            g_pin_pool.pop_back();
+        }
+        if (hipHostMalloc(&p, want, hipHostMallocDefault) != hipSuccess) {
+            p = nullptr;
+            return;
+        }
+        n = want;
+    }
+    ~PinnedLease() {
+        if (!p) return;
+        if (queued) (void)hipStreamSynchronize(pending);
+        std::lock_guard<std::mutex> lk(g_pin_mu);
+        g_pin_pool.emplace_back(p, n);
+    }
+    PinnedLease(const PinnedLease&) = delete;
+    PinnedLease& operator=(const PinnedLease&) = delete;
+};
+
 // blocks of `kernel` (block size `threads`, no dynamic LDS) resident on the
 // current device at once, or 0 when the runtime cannot tell
 template <class K>
@@ -628,10 +673,22 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     hipLaunchKernelGGL(enc_hist, dim3(hist_per_stripe, ns), dim3(kHistThreads), 0, st, raw,
                        raw_bytes, hist);
     if (launched()) return K3HUF_E_HIP;
-    std::vector<uint64_t> h(size_t(ns) * 256);
-    if (hipMemcpyAsync(h.data(), hist, h.size() * 8, hipMemcpyDeviceToHost, st) != hipSuccess ||
+    // pinned staging: histograms, layer header, stripe geometry, status word
+    const size_t hist_b = size_t(ns) * 256 * 8, hdr_b = pad256(K3HUF_HDR_BYTES + 8ull * ns);
+    const size_t geom_b = (size_t(ns) * sizeof(StripeDev) + 15) & ~size_t(15);
+    PinnedLease pin(hist_b + hdr_b + geom_b + 16);
+    if (!pin.p) return K3HUF_E_HIP;
+    uint8_t* pin_b = static_cast<uint8_t*>(pin.p);
+    const uint64_t* h = reinterpret_cast<const uint64_t*>(pin_b);
+    uint8_t* pin_hdr = pin_b + hist_b;
+    StripeDev* gd = reinterpret_cast<StripeDev*>(pin_hdr + hdr_b);
+    uint32_t* pin_status = reinterpret_cast<uint32_t*>(pin_hdr + hdr_b + geom_b);
+    pin.pending = st;
+    pin.queued = true;
+    if (hipMemcpyAsync(pin_b, hist, hist_b, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
         return K3HUF_E_HIP;
+    pin.queued = false;
 
     // 2. code lengths, canonical codes and the layout, on the host
     uint64_t count[256] = {};
@@ -645,19 +702,17 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     for (int v = 0; v < 256; ++v) ct.e[v] = (uint32_t(len[v]) << 16) | code[v];
     std::vector<StripeGeom> g;
     uint32_t nsb_total = 0;
-    const uint64_t total = k3huf_detail::layout(raw_bytes, h.data(), len, g, &nsb_total);
+    const uint64_t total = k3huf_detail::layout(raw_bytes, h, len, g, &nsb_total);
     if (total > cap) return K3HUF_E_ARG;
-    std::vector<uint8_t> hdr(pad256(K3HUF_HDR_BYTES + 8ull * ns));
-    k3huf_detail::write_layer_header(hdr.data(), raw_bytes, len, g, nsb_total, total);
-    std::vector<StripeDev> gd(ns);
+    k3huf_detail::write_layer_header(pin_hdr, raw_bytes, len, g, nsb_total, total);
     for (uint32_t s = 0; s < ns; ++s)
         gd[s] = StripeDev{g[s].raw0, g[s].off, g[s].raw, g[s].n, g[s].nsb, g[s].nbits,
                           g[s].bit_bytes, g[s].bits_off, g[s].even_off, 0u};
 
     // 3. headers, then the byte work
-    if (hipMemcpyAsync(out, hdr.data(), hdr.size(), hipMemcpyHostToDevice, st) != hipSuccess ||
-        hipMemcpyAsync(geom, gd.data(), gd.size() * sizeof(StripeDev), hipMemcpyHostToDevice, st) !=
-            hipSuccess)
+    pin.queued = true;
+    if (hipMemcpyAsync(out, pin_hdr, hdr_b, hipMemcpyHostToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(geom, gd, size_t(ns) * sizeof(StripeDev), hipMemcpyHostToDevice, st) != hipSuccess)
         return K3HUF_E_HIP;
     const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
     hipLaunchKernelGGL(enc_pack, dim3(unsigned((n_units + kPackWaves - 1) / kPackWaves)),
@@ -666,10 +721,11 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     hipLaunchKernelGGL(enc_edges, dim3(unsigned((n_units + 255) / 256)), dim3(256), 0, st, edges,
                        n_units, geom, out);
     if (launched()) return K3HUF_E_HIP;
-    uint32_t bad = 0;
-    if (hipMemcpyAsync(&bad, status, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+    if (hipMemcpyAsync(pin_status, status, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
         return K3HUF_E_HIP;
+    pin.queued = false;
+    const uint32_t bad = *pin_status;
     return (bad & 2u) ? K3HUF_E_HIP : bad ? K3HUF_E_CORRUPT : int64_t(total);
 }
 
