@@ -217,6 +217,34 @@ def mixed_spans(seed: int, n_bytes: int, lo: int = 4 << 10, hi: int = 160 << 10)
     return out
 
 
+def fuzz_layer(seed: int, max_bytes: int = 24 << 20) -> tuple[np.ndarray, str]:
+    """A seeded random layer for sweeps: an even size log-uniform in
+    [2, max_bytes] and one of several high-byte laws (bf16 normals of very
+    different scales, uniform bytes, 1-255 live high bytes with Dirichlet
+    weights, a Zipf-like law); low bytes uniform unless drawn from bf16
+    values. Returns the bytes and a short description."""
+    rng = np.random.default_rng((SEED_BASE, 9000, seed))
+    n = 2 * max(1, int(math.exp(rng.uniform(0.0, math.log(max_bytes / 2)))))
+    law = int(rng.integers(0, 4))
+    if law == 0:
+        sigma = float(10.0 ** rng.uniform(-5, 3))
+        return f64_to_bf16_bytes(rng.standard_normal(n // 2) * sigma), "normal sigma %.3g, %d B" % (sigma, n)
+    if law == 1:
+        return rng.integers(0, 256, n, dtype=np.uint8), "uniform bytes, %d B" % n
+    out = rng.integers(0, 256, n, dtype=np.uint8)
+    if law == 2:
+        k = int(rng.choice([1, 2, 3, 5, 17, 64, 255]))
+        syms = rng.choice(256, size=k, replace=False)
+        w = rng.dirichlet(np.full(k, 0.3))
+        out[1::2] = syms[rng.choice(k, size=n // 2, p=w)].astype(np.uint8)
+        return out, "%d live high bytes (Dirichlet 0.3), %d B" % (k, n)
+    a = float(rng.uniform(1.05, 3.0))
+    ranks = np.minimum(rng.zipf(a, size=n // 2), 256) - 1
+    perm = rng.permutation(256)
+    out[1::2] = perm[ranks].astype(np.uint8)
+    return out, "Zipf a=%.2f high bytes, %d B" % (a, n)
+
+
 def small_trunk_matrix(seed: int, rows: int, cols: int) -> np.ndarray:
     """One rows x cols bf16 weight drawn like a trunk matrix: N(0, s) with s
     log-uniform in [0.005, 0.05], both from default_rng(seed)."""

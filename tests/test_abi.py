@@ -194,3 +194,14 @@ def test_gpu_encoder_rejects_bad_arguments_before_any_device_call():
     assert f(raw, n, out + 4, cap, work, wb, None) == k3huf.E_ARG       # misaligned output
     assert f(raw, n, out, cap - 1, work, wb, None) == k3huf.E_ARG       # output too small
     assert f(raw, n, out, cap, work, wb - 1, None) == k3huf.E_ARG       # work too small
+
+
+def test_packer_fuzz_matches_oracle():
+    """The native packer against the oracle's encoder on the seeded random
+    sweep of the GPU tests (random sizes and high-byte laws)."""
+    for seed in range(48):
+        x, what = synth.fuzz_layer(seed)
+        a = O.encode_layer(x)
+        b = k3huf.encode_layer(x)
+        assert a.size == b.size and (a == b).all(), (seed, what)
+        assert O.check_index(b) == O.OK, (seed, what)
