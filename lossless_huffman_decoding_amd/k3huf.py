@@ -161,15 +161,19 @@ def encode_layer_dev(d_raw, d_out=None, d_work=None, stream=None):
     (device uint8, at least encode_work_bytes) are allocated when None.
     Returns the container as a view of d_out (synchronous call)."""
     import torch
-    n = d_raw.numel() * d_raw.element_size()
+    n = _nbytes(d_raw)
     if d_out is None:
         d_out = torch.empty(encode_bound(n), dtype=torch.uint8, device=d_raw.device)
     if d_work is None:
         d_work = torch.empty(encode_work_bytes(n), dtype=torch.uint8, device=d_raw.device)
-    size = _check(lib().k3huf_encode_layer_dev(d_raw.data_ptr(), n, d_out.data_ptr(), d_out.numel(),
-                                               d_work.data_ptr(), d_work.numel(),
+    size = _check(lib().k3huf_encode_layer_dev(d_raw.data_ptr(), n, d_out.data_ptr(), _nbytes(d_out),
+                                               d_work.data_ptr(), _nbytes(d_work),
                                                _stream_handle(stream)), "k3huf_encode_layer_dev")
     return d_out[:size]
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
 
 
 def _stream_handle(stream) -> int:
@@ -185,8 +189,8 @@ def decode_layer(d_blob, d_lut, d_out, d_status=None, stream=None) -> None:
     a 32-bit device word or None. Runs on ``stream`` (default: torch's
     current stream)."""
     rc = lib().k3huf_decode_layer(
-        d_blob.data_ptr(), d_blob.numel() * d_blob.element_size(), d_lut.data_ptr(),
-        d_out.data_ptr(), d_out.numel() * d_out.element_size(), _stream_handle(stream),
+        d_blob.data_ptr(), _nbytes(d_blob), d_lut.data_ptr(),
+        d_out.data_ptr(), _nbytes(d_out), _stream_handle(stream),
         d_status.data_ptr() if d_status is not None else None)
     _check(rc, "k3huf_decode_layer")
 
@@ -206,10 +210,10 @@ def decode_ring(layers, slots, streams, cb=None, d_status=None) -> None:
     n = len(layers)
     arr = (RingLayer * max(n, 1))()
     for k, (blob, lut, raw) in enumerate(layers):
-        arr[k] = RingLayer(blob.data_ptr(), blob.numel(), lut.data_ptr(), raw)
+        arr[k] = RingLayer(blob.data_ptr(), _nbytes(blob), lut.data_ptr(), raw)
     slot_ptrs = (ctypes.c_void_p * len(slots))(*[s.data_ptr() for s in slots])
     stream_ptrs = (ctypes.c_void_p * len(streams))(*[_stream_handle(s) for s in streams])
-    slot_bytes = min(s.numel() for s in slots)
+    slot_bytes = min(_nbytes(s) for s in slots)
     c_cb = _ring_cb(cb, slots)
     rc = lib().k3huf_decode_ring(arr, n, slot_ptrs, len(slots), slot_bytes, stream_ptrs,
                                  len(streams), c_cb, None,
@@ -236,13 +240,13 @@ def decode_ring_host(layers, stages, slots, copy_stream, streams, cb=None, d_sta
     n = len(layers)
     arr = (HostLayer * max(n, 1))()
     for k, (blob, lut, raw) in enumerate(layers):
-        arr[k] = HostLayer(blob.data_ptr(), blob.numel(), lut.data_ptr(), raw)
+        arr[k] = HostLayer(blob.data_ptr(), _nbytes(blob), lut.data_ptr(), raw)
     stage_ptrs = (ctypes.c_void_p * len(stages))(*[s.data_ptr() for s in stages])
     slot_ptrs = (ctypes.c_void_p * len(slots))(*[s.data_ptr() for s in slots])
     stream_ptrs = (ctypes.c_void_p * len(streams))(*[_stream_handle(s) for s in streams])
     c_cb = _ring_cb(cb, slots)
-    rc = lib().k3huf_decode_ring_host(arr, n, stage_ptrs, len(stages), min(s.numel() for s in stages),
-                                      slot_ptrs, len(slots), min(s.numel() for s in slots),
+    rc = lib().k3huf_decode_ring_host(arr, n, stage_ptrs, len(stages), min(_nbytes(s) for s in stages),
+                                      slot_ptrs, len(slots), min(_nbytes(s) for s in slots),
                                       _stream_handle(copy_stream), stream_ptrs, len(streams), c_cb,
                                       None, d_status.data_ptr() if d_status is not None else None)
     _check(rc, "k3huf_decode_ring_host")
