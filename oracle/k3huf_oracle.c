@@ -36,6 +36,12 @@
  * per 65,536-byte subblock, code bits per 256-symbol lane chunk) is an addition
  * for parallel decoding, counted in the container size.
  *
+ * Parity unpinned: the exact code lengths the length limit and the repay pass
+ * give. They are a heuristic, so the tests pin only their invariants (no
+ * length above 12, an exactly full table for two or more symbols, a cost at
+ * least the optimal limited cost) and every decode reads the lengths from the
+ * container, so decoding does not depend on them.
+ *
  * The decoder here ignores the index entirely: it reads the stripe bitstream
  * one bit at a time and matches the growing code against the canonical ranges.
  *
