@@ -744,7 +744,7 @@ struct DevInfo {
 std::mutex g_mu;
 std::vector<DevInfo> g_dev;
 constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
-std::map<std::pair<int, void*>, uint32_t> g_stream_slot;   // (device, stream) -> counter slot or kNoSlot
+std::map<std::pair<int, void*>, uint32_t> g_stream_slot;   // (device, stream) -> counter slot
 std::vector<uint32_t> g_next_slot;                        // per device
 
 // The device's launch geometry and the counter slot of `stream` on it
@@ -754,12 +754,15 @@ int device_info(void* stream, DevInfo* out, uint32_t* slot) {
     if (hipGetDevice(&dev) != hipSuccess) return K3HUF_E_HIP;
     std::lock_guard<std::mutex> lk(g_mu);
     if (int(g_next_slot.size()) <= dev) g_next_slot.resize(dev + 1, 0u);
+    // streams past the slots are not recorded, so the map stays bounded
+    // however many streams a process creates
     auto it = g_stream_slot.find({dev, stream});
-    if (it == g_stream_slot.end()) {
-        const uint32_t s = g_next_slot[dev] < kSchedSlots ? g_next_slot[dev]++ : kNoSlot;
-        it = g_stream_slot.emplace(std::make_pair(dev, stream), s).first;
-    }
-    *slot = it->second;
+    if (it != g_stream_slot.end())
+        *slot = it->second;
+    else if (g_next_slot[dev] < kSchedSlots)
+        *slot = g_stream_slot.emplace(std::make_pair(dev, stream), g_next_slot[dev]++).first->second;
+    else
+        *slot = kNoSlot;
     if (int(g_dev.size()) <= dev) g_dev.resize(dev + 1);
     DevInfo& d = g_dev[dev];
     if (!d.cus) {
