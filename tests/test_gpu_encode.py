@@ -105,6 +105,29 @@ def test_encode_mixed_spans_matches_oracle_and_round_trips():
     assert torch.equal(d_dec, d_x)
 
 
+def test_layer_of_more_than_64_stripes():
+    """A 4.36 GB trunk-recipe layer: 65 full stripes and a partial one. The
+    decoder keeps stripe values for blocks of 64 stripes and must reload them
+    when a unit falls in the next block; the GPU encoder's look-back restarts
+    in every stripe. The GPU encoder's container must equal the native
+    packer's (which equals the oracle's byte for byte on every other layer
+    here; the oracle needs about two minutes for this size), and decoding it
+    must give the layer back."""
+    n = (65 << 26) + 3 * 65536 + 1234
+    x = synth.trunk_layer(synth.SEED_BASE + 77, n_bytes=n)
+    want = k3huf.encode_layer(x)
+    assert k3huf.layer_info(want)["n_stripes"] == 66
+    say("encode and decode 66 stripes", x.size)
+    d_x = torch.from_numpy(x).to(DEV)
+    d_blob = k3huf.encode_layer_dev(d_x, *garbage_buffers(x.size))
+    assert d_blob.numel() == want.size
+    assert torch.equal(d_blob, torch.from_numpy(want).to(DEV))
+    say("66 stripes: decode")
+    d_dec, st = gpu_decode_dev(d_blob, x.size)
+    assert st == 0
+    assert torch.equal(d_dec, d_x)
+
+
 def test_encode_reuses_buffers_across_calls():
     """Two calls in a row on the same output and work buffers, the second
     with a smaller layer: both containers equal the oracle's (scratch state of
