@@ -174,6 +174,24 @@ def test_corrupt_header_is_flagged_and_nothing_written():
     assert (got == 0xA5).all()
 
 
+def test_decode_without_a_status_word():
+    """d_status may be null: a good layer decodes, and a corrupt header
+    (which the kernel would flag) leaves the output unwritten."""
+    x = synth.small_random(19, 3 * 65536 + 514)
+    good = O.encode_layer(x)
+    lut = k3huf.build_table(k3huf.layer_info(good)["codelen"])
+    bad = good.copy()
+    bad[0] ^= 0xFF
+    for blob, ok in ((good, True), (bad, False)):
+        d_blob, d_lut = to_dev(blob, lut)
+        d_out = torch.full((x.size,), 0xA5, dtype=torch.uint8, device=DEV)
+        say("no status word", "good" if ok else "corrupt header")
+        k3huf.decode_layer(d_blob, d_lut, d_out, None)
+        torch.cuda.synchronize()
+        got = d_out.cpu().numpy()
+        assert (got == x).all() if ok else (got == 0xA5).all()
+
+
 def test_wrong_out_size_is_flagged():
     x = synth.small_random(10, 65536 * 2)
     blob = O.encode_layer(x)
