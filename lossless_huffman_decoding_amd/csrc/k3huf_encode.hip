@@ -478,6 +478,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
         }
     };
     if (!tail) {
+        uint2 evp[8];   // an even phase's even bytes, stored with the next phase's
         // phase 0's raw bytes are in rv from A; unrolled, so the raw
         // registers need no copies between phases (a copy waits for every
         // outstanding load and store)
@@ -499,9 +500,18 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
                                    __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
             }
             if (ph + 1 < kPackPhases) load_raw(ph + 1);
+            if (ph & 1) {
+                // both halves of each 128-byte even-plane line, back to back
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<uint2*>(ueven + (i * 8 + sub) * K3HUF_LANE_SYMS + ph * kPhSyms + q * 8) = ev[i];
+                for (int i = 0; i < 8; ++i) {
+                    uint8_t* e = ueven + (i * 8 + sub) * K3HUF_LANE_SYMS + (ph - 1) * kPhSyms + q * 8;
+                    *reinterpret_cast<uint2*>(e) = evp[i];
+                    *reinterpret_cast<uint2*>(e + kPhSyms) = ev[i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) evp[i] = ev[i];
+            }
             wave_sync();
             pack_phase(ph);
             wave_sync();
