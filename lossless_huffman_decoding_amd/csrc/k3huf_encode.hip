@@ -243,6 +243,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     // its phase (8 lanes per chunk phase of 128 raw bytes)
     const int q = lane & 7, sub = lane >> 3;
     uint4 rv[8];
+    uint4 ra[8];   // after A: phase 1's raw bytes (rv holds phase 0's)
     auto load_into = [&](uint4* r, int ph) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -252,12 +253,12 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
 
     // A. the lane chunks' code bits: every lane adds up the code lengths of
     // the odd bytes it loads (phases 3, 2, 1, 0, two in flight at a time;
-    // phase 0's bytes stay in registers for C), then the 8 lanes of each
-    // chunk are summed and lane t takes chunk t's sum
+    // the bytes of phases 0 and 1 stay in registers for C, so only phases 2
+    // and 3 are read again), then the 8 lanes of each chunk are summed and
+    // lane t takes chunk t's sum
     uint32_t bits = 0;
     if (!tail) {
         uint32_t part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        uint4 ra[8];
         auto count = [&](const uint4* r) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -479,9 +480,9 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     };
     if (!tail) {
         uint2 evp[8];   // an even phase's even bytes, stored with the next phase's
-        // phase 0's raw bytes are in rv from A; unrolled, so the raw
-        // registers need no copies between phases (a copy waits for every
-        // outstanding load and store)
+        // phases 0 and 1's raw bytes are in rv and ra from A; unrolled, so
+        // the raw registers need no copies between phases (a copy waits for
+        // every outstanding load and store)
 #pragma unroll
         for (int ph = 0; ph < kPackPhases; ++ph) {
             // stage this phase's odd bytes and keep its even bytes; the next
@@ -492,14 +493,14 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int ch = i * 8 + sub;
-                const uint4 v = rv[i];
+                const uint4 v = ph == 1 ? ra[i] : rv[i];
                 uint32_t* r = reinterpret_cast<uint32_t*>(row + ch * kRowBytes + q * 8);
                 r[0] = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
                 r[1] = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
                 ev[i] = make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
                                    __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
             }
-            if (ph + 1 < kPackPhases) load_raw(ph + 1);
+            if (ph + 1 < kPackPhases && ph != 0) load_raw(ph + 1);
             if (ph & 1) {
                 // both halves of each 128-byte even-plane line, back to back
 #pragma unroll
