@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     // its phase (8 lanes per chunk phase of 128 raw bytes)
     const int q = lane & 7, sub = lane >> 3;
     uint4 rv[8];
-    uint4 ra[8];   // after A: phase 1's raw bytes (rv holds phase 0's)
+    uint4 ra[8], rb[8];   // after A: phases 1 and 2's raw bytes (rv holds phase 0's)
     auto load_into = [&](uint4* r, int ph) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -252,10 +252,10 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     auto load_raw = [&](int ph) { load_into(rv, ph); };
 
     // A. the lane chunks' code bits: every lane adds up the code lengths of
-    // the odd bytes it loads (phases 3, 2, 1, 0, two in flight at a time;
-    // the bytes of phases 0 and 1 stay in registers for C, so only phases 2
-    // and 3 are read again), then the 8 lanes of each chunk are summed and
-    // lane t takes chunk t's sum
+    // the odd bytes it loads (phases 3 and 2, then 1 and 0, two in flight at
+    // a time; the bytes of phases 0-2 stay in registers for C, so only phase
+    // 3 is read again: all four would take 180 VGPRs, two waves per SIMD),
+    // then the 8 lanes of each chunk are summed and lane t takes chunk t's sum
     uint32_t bits = 0;
     if (!tail) {
         uint32_t part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -269,11 +269,11 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
             }
         };
         load_into(ra, 3);
-        load_into(rv, 2);
+        load_into(rb, 2);
         count(ra);
         load_into(ra, 1);
-        count(rv);
         load_into(rv, 0);
+        count(rb);
         count(ra);
         count(rv);
 #pragma unroll
@@ -480,9 +480,10 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     };
     if (!tail) {
         uint2 evp[8];   // an even phase's even bytes, stored with the next phase's
-        // phases 0 and 1's raw bytes are in rv and ra from A; unrolled, so
-        // the raw registers need no copies between phases (a copy waits for
-        // every outstanding load and store)
+        // phases 0-2's raw bytes are in rv, ra and rb from A, phase 3's are
+        // read into rv during phase 2; unrolled, so the raw registers need no
+        // copies between phases (a copy waits for every outstanding load and
+        // store)
 #pragma unroll
         for (int ph = 0; ph < kPackPhases; ++ph) {
             // stage this phase's odd bytes and keep its even bytes; the next
@@ -493,14 +494,14 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int ch = i * 8 + sub;
-                const uint4 v = ph == 1 ? ra[i] : rv[i];
+                const uint4 v = ph == 1 ? ra[i] : ph == 2 ? rb[i] : rv[i];
                 uint32_t* r = reinterpret_cast<uint32_t*>(row + ch * kRowBytes + q * 8);
                 r[0] = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
                 r[1] = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
                 ev[i] = make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
                                    __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
             }
-            if (ph + 1 < kPackPhases && ph != 0) load_raw(ph + 1);
+            if (ph == 2) load_raw(3);
             if (ph & 1) {
                 // both halves of each 128-byte even-plane line, back to back
 #pragma unroll
