@@ -36,11 +36,12 @@
  * per 65,536-byte subblock, code bits per 256-symbol lane chunk) is an addition
  * for parallel decoding, counted in the container size.
  *
- * Parity unpinned: the exact code lengths the length limit and the repay pass
- * give. They are a heuristic, so the tests pin only their invariants (no
- * length above 12, an exactly full table for two or more symbols, a cost at
- * least the optimal limited cost) and every decode reads the lengths from the
- * container, so decoding does not depend on them.
+ * The length limit and the repay pass are a procedure, fixed up to their
+ * tie rules: the tests pin their exact output on hand-derived cases (clamp
+ * only, lengthen then repay, a tie in each loop, a repay that shortens one
+ * code twice), besides invariants (no length above 12, an exactly full table
+ * for two or more symbols, a cost at least the optimal limited cost). Every
+ * decode reads the lengths from the container.
  *
  * The decoder here ignores the index entirely: it reads the stripe bitstream
  * one bit at a time and matches the growing code against the canonical ranges.

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle as O
+from goldens import limiter_goldens
 from lossless_huffman_decoding_amd import k3huf, synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -110,6 +111,33 @@ def test_packer_mixed_spans_matches_oracle():
     a = O.encode_layer(x)
     b = k3huf.encode_layer(x)
     assert a.size == b.size and (a == b).all()
+
+
+def _layer_with_counts(counts, seed):
+    """bf16 layer bytes whose odd (high) bytes hold symbol v exactly counts[v]
+    times, in a seeded order; even bytes seeded at random."""
+    rng = np.random.default_rng(seed)
+    odd = rng.permutation(np.repeat(np.arange(len(counts), dtype=np.uint8), counts))
+    x = np.empty(2 * odd.size, np.uint8)
+    x[1::2] = odd
+    x[0::2] = rng.integers(0, 256, odd.size, dtype=np.uint8)
+    return x
+
+
+def test_packer_code_lengths_match_limiter_goldens():
+    """The native packer's codelen[256] (as written into its container header)
+    equals the hand-derived length-limit cases of tests/golden/limiter_cases.txt,
+    and so does the oracle's (K3 page, section "canonical code assignment and
+    Kraft check")."""
+    for i, (name, counts, want) in enumerate(limiter_goldens()):
+        x = _layer_with_counts(counts, 500 + i)
+        b = k3huf.encode_layer(x)
+        got = k3huf.layer_info(b)["codelen"]
+        assert list(got[: len(counts)]) == want, name
+        assert (got[len(counts):] == 0).all(), name
+        a = O.encode_layer(x)
+        assert a.size == b.size and (a == b).all(), name
+        assert (O.decode_layer(b) == x).all(), name
 
 
 def test_packer_bad_args():

@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 
 import oracle as O
+from goldens import limiter_goldens
 from lossless_huffman_decoding_amd import synth
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -178,6 +179,19 @@ def test_limiter_random_sweep():
         if trial % 10 == 0:
             assert c >= _package_merge(counts, 12)
     assert forced > 50  # the sweep really exercises the limiter
+
+
+@pytest.mark.parametrize("name,counts,want", limiter_goldens(), ids=lambda v: v if isinstance(v, str) else "")
+def test_limiter_and_repay_golden(name, counts, want):
+    """Exact code lengths of the limiter and the repay, against hand-derived
+    cases: clamp only (fib14), lengthen then repay (fib15), a tie in the
+    lengthen step (ltie15), a tie in the repay step (rtie15), and a repay that
+    shortens a code twice, from 12 to 10 (mixed16)."""
+    got = O.code_lengths(counts)
+    assert list(got[: len(counts)]) == want, name
+    assert (got[len(counts):] == 0).all()
+    assert O.kraft(got) == 4096
+    assert O.huffman_depths(counts).max() > 12      # every case needs the limit
 
 
 def test_package_merge_matches_huffman_when_unconstrained():
