@@ -118,9 +118,16 @@ typedef struct k3huf_info {
 
 /*
  * k3huf_layer_info -- parse and check a layer header held in host memory.
- * h_blob/h_bytes: at least the first K3HUF_HDR_BYTES bytes of a blob.
- * Checks magic, version, geometry constants, raw size and stripe count.
- * Errors: K3HUF_E_ARG, K3HUF_E_FORMAT.
+ * K3 page, "what was implemented": a layer starts with a header that holds
+ * its codelen[256] (one code table per layer), followed by its stripes; this
+ * reads that header (plus the geometry fields the container adds) so the
+ * caller can build the layer's table and size its output.
+ * h_blob/h_bytes: at least the first K3HUF_HDR_BYTES bytes of a blob (host
+ *   memory, caller-owned, only read). out: caller-owned, filled on success.
+ * Checks magic, version, geometry constants, raw size and stripe count; the
+ * stripe records are not read.
+ * Errors: K3HUF_E_ARG (null pointer, h_bytes < K3HUF_HDR_BYTES),
+ * K3HUF_E_FORMAT (a field off the format; *out is left unchanged).
  */
 int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out);
 
@@ -154,8 +161,12 @@ int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out);
  * waves from a counter in the workgroup's own LDS, which shares nothing: for
  * smaller layers it is as fast or faster, for larger ones slower (about
  * 1.05 times the time on the trunk layer). That covers launches on later
- * streams and launches made while the stream is being captured into a graph
- * (and so all of a graph's replays).
+ * streams, launches on hipStreamPerThread (one handle for a different stream
+ * in each host thread) and launches made while the stream is being captured
+ * into a graph (and so all of a graph's replays). A slot belongs to a stream
+ * handle's value: a stream must not be destroyed while a decode on it is
+ * still pending if a new stream could then be created at the same address
+ * and decode at the same time.
  */
 int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut,
                        void* d_out, size_t out_bytes, void* stream, uint32_t* d_status);

@@ -23,6 +23,7 @@
 #include <vector>
 
 #include "k3huf.h"
+#include "k3huf_bounds.h"
 
 namespace {
 
@@ -224,7 +225,7 @@ struct Unit {
     const uint8_t* bits;   // stripe bitstream
     const uint8_t* even;   // this unit's even-plane bytes
     uint8_t* out;          // this unit's output bytes
-    int dmax;              // last readable 16-byte unit (dwords from `bits`)
+    int dmax;              // last readable 16-byte unit (dwords from `bits`, within the stripe)
     uint32_t nsyms;        // symbols in this unit (16384 unless last in stripe)
 };
 
@@ -314,7 +315,7 @@ __device__ __forceinline__ void decode_super(const uint32_t* tab, uint32_t* buf,
             uint2 g[kSlotDw / 2];
 #pragma unroll
             for (int i = 0; i < kSlotDw / 2; ++i)
-                g[i] = *reinterpret_cast<const uint2*>(un.bits + 4 * min(d0 + 2 * i, un.dmax));
+                g[i] = *reinterpret_cast<const uint2*>(un.bits + k3huf_bounds::clamped_read_off(d0 + 2 * i, un.dmax));
 #pragma unroll
             for (int i = 0; i < kSlotDw / 2; ++i)
                 *reinterpret_cast<uint2*>(slot + 2 * i) = make_uint2(bswap32(g[i].x), bswap32(g[i].y));
@@ -446,7 +447,7 @@ __device__ __forceinline__ void fill_buffer(uint32_t* buf, const Unit& un, int j
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int u = min(lane + 64 * i, units - 1);
-        v[i] = *reinterpret_cast<const uint4*>(un.bits + 4 * min(j0 + 4 * u, un.dmax));
+        v[i] = *reinterpret_cast<const uint4*>(un.bits + k3huf_bounds::clamped_read_off(j0 + 4 * u, un.dmax));
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
@@ -499,13 +500,10 @@ __device__ __forceinline__ StripeLane load_stripes(const DecodeArgs& a, uint32_t
     const uint4 r1 = *reinterpret_cast<const uint4*>(a.blob + so + 16);
     const uint32_t n_bits = r0.z, bit_bytes = r0.w, bits_off = r1.z, even_off = r1.w;
     const uint32_t ok = bit(has) & in & bit(r0.x == uint32_t(raw_s)) & bit(r0.y == n) &
-                        bit(r1.x == sc * kSubPerStripe) & bit(r1.y == nsb) & bit((bits_off & 15) == 0) &
-                        bit((even_off & 15) == 0) &
-                        bit(bits_off >= K3HUF_STRIPE_HDR_BYTES + K3HUF_SUBBLOCK_REC_BYTES * nsb) &
-                        bit(uint64_t(n_bits) <= 8ull * bit_bytes) &
+                        bit(r1.x == sc * kSubPerStripe) & bit(r1.y == nsb) &
                         bit(uint64_t(n_bits) <= uint64_t(K3HUF_MAXLEN) * n) &
-                        bit(uint64_t(even_off) >= uint64_t(bits_off) + bit_bytes) &
-                        bit(so + even_off + ((uint64_t(n) + 15) & ~15ull) <= a.blob_bytes);
+                        bit(k3huf_bounds::stripe_planes_ok(a.blob_bytes, so, n, nsb, n_bits, bit_bytes,
+                                                           bits_off, even_off));
     StripeLane t;
     t.off16 = ok ? uint32_t(so >> 4) : 0u;
     t.bits_off = ok ? bits_off : 0u;
@@ -687,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         if (un.nsyms == 0) continue;
         const uint32_t unit_start = start_bit + (half ? other_bits : 0u);
         un.bits = st + bits_off;
-        un.dmax = int(((a.blob_bytes - (soff + bits_off) - 16) / 4) & ~3ull);
+        un.dmax = k3huf_bounds::stripe_read_dmax(bits_off, even_off, n);
         un.even = st + even_off + uint64_t(jsb) * K3HUF_SUBBLOCK_SYMS + uint64_t(half) * kUnitSyms;
         un.out = a.out + uint64_t(k) * K3HUF_SUBBLOCK_BYTES + 2ull * half * kUnitSyms;
         const uint32_t lane_start = unit_start + incl - lb;
@@ -755,9 +753,13 @@ int device_info(void* stream, DevInfo* out, uint32_t* slot) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (int(g_next_slot.size()) <= dev) g_next_slot.resize(dev + 1, 0u);
     // streams past the slots are not recorded, so the map stays bounded
-    // however many streams a process creates
+    // however many streams a process creates. hipStreamPerThread names a
+    // different stream in each host thread, so launches through that one
+    // handle can overlap: it never gets a slot.
     auto it = g_stream_slot.find({dev, stream});
-    if (it != g_stream_slot.end())
+    if (stream == static_cast<void*>(hipStreamPerThread))
+        *slot = kNoSlot;
+    else if (it != g_stream_slot.end())
         *slot = it->second;
     else if (g_next_slot[dev] < kSchedSlots)
         *slot = g_stream_slot.emplace(std::make_pair(dev, stream), g_next_slot[dev]++).first->second;
