@@ -277,6 +277,31 @@ def test_bad_arguments_raise_before_launch():
         k3huf.decode_layer(d_blob[:1024], d_lut, d_out[:4096])  # output above twice the blob
 
 
+def test_layer_at_the_start_of_a_buffer_over_8_gib():
+    """A two-stripe container at the start of a 9 GiB device buffer, decoded
+    with blob_bytes set to the whole buffer: every stripe's bitstream starts
+    more than 8 GiB before the blob's end. The kernel bounds its bitstream
+    reads by each stripe's own planes, in 64-bit offsets (the read bounds are
+    checked on the CPU up to 2^36 bytes by tests/test_read_bounds.py), so the
+    layer decodes exactly."""
+    x = synth.small_random(655, (1 << 26) + 3 * 65536 + 514)
+    blob = O.encode_layer(x)
+    lut = k3huf.build_table(k3huf.layer_info(blob)["codelen"])
+    big = (9 << 30) + 4096
+    say("layer in a buffer of", big, "bytes")
+    d_buf = torch.zeros(big, dtype=torch.uint8, device=DEV)
+    d_buf[: blob.size].copy_(torch.from_numpy(blob))
+    d_lut = torch.from_numpy(lut.view(np.int16)).to(DEV)
+    d_out = torch.full((x.size,), 0xA5, dtype=torch.uint8, device=DEV)
+    d_status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    k3huf.decode_layer(d_buf, d_lut, d_out, d_status)
+    torch.cuda.synchronize()
+    assert int(d_status.item()) == 0
+    assert (d_out.cpu().numpy() == x).all()
+    del d_buf
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # layer ring (K3 TUNING page, section 2: a two-slot trunk ring)
 
@@ -306,6 +331,42 @@ def test_ring_decodes_layers_in_order(n_slots, n_streams):
     assert int(status.item()) == 0
     for k in range(len(xs)):
         assert (results[k].cpu().numpy() == xs[k]).all(), k
+
+
+def test_ring_streamed_trunk_layers_full_size():
+    """The streamed-trunk ring at its real shape: six 1.17 GB trunk layers
+    (per-layer seeds, as layers 0..5 of the 93-layer pass) decoded in fixed
+    order into two slots on two streams (K3 page, "background": layers are
+    visited in order 0..92; K3 TUNING page, section 2: a two-slot ring). Each
+    layer is copied out of its slot on the slot's stream before the slot is
+    released, and every layer is compared byte for byte with its generated
+    bytes."""
+    n = 6
+    xs = [synth.streamed_layer(k) for k in range(n)]
+    blobs = [k3huf.encode_layer(x) for x in xs]
+    luts = [k3huf.build_table(k3huf.layer_info(b)["codelen"]) for b in blobs]
+    dev = [to_dev(b, l) for b, l in zip(blobs, luts)]
+    del blobs
+    layers = [(db, dl, x.size) for (db, dl), x in zip(dev, xs)]
+    slots = [torch.empty(max(x.size for x in xs), dtype=torch.uint8, device=DEV) for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    by_handle = {s.cuda_stream: s for s in streams}
+    results = [torch.full((x.size,), 0xA5, dtype=torch.uint8, device=DEV) for x in xs]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+
+    def consume(k, slot, handle):
+        with torch.cuda.stream(by_handle[handle]):
+            results[k].copy_(slots[slot][: xs[k].size])
+
+    torch.cuda.synchronize()   # buffers prepared on the current stream
+    say("streamed ring, full-size trunk layers", n)
+    k3huf.decode_ring(layers, slots, streams, consume, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for k, x in enumerate(xs):
+        assert torch.equal(results[k], torch.from_numpy(x).to(DEV)), k
+    del results, slots, dev, layers
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
@@ -401,26 +462,53 @@ def test_concurrent_decodes_on_many_streams():
         assert (outs[k].cpu().numpy() == x).all(), k
 
 
+def _hip_runtime():
+    """The HIP runtime torch has loaded (same soname, so dlopen returns it)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipStreamCreate.restype = ctypes.c_int
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipStreamDestroy.restype = ctypes.c_int
+    return hip
+
+
 @pytest.fixture(scope="module")
 def many_streams():
-    """300 new streams, each registered by a decode (a stream takes one of
-    the device's 256 work-counter slots at its first decode), so that the
-    last ones are past the slot limit whatever streams earlier tests used."""
+    """300 raw HIP streams (hipStreamCreate; torch's own Stream() objects
+    come from a pool of 32 and repeat), all alive at once, each registered by
+    a decode. The library gives work-counter slots to the first 256 distinct
+    streams of a device it sees and none to later ones, so at least the last
+    44 of these 300 distinct handles have no slot, whatever streams earlier
+    tests registered: decodes on them hand out units from workgroup
+    counters."""
+    import ctypes
+    torch.cuda.init()
+    hip = _hip_runtime()
+    handles = []
+    for _ in range(300):
+        h = ctypes.c_void_p()
+        assert hip.hipStreamCreate(ctypes.byref(h)) == 0
+        handles.append(h.value)
+    assert len(set(handles)) == 300 > 256
+    streams = [torch.cuda.ExternalStream(h, device=DEV) for h in handles]
     x = synth.small_random(611, 3 * 65536 + 514)
     blob = O.encode_layer(x)
     db, dl = to_dev(blob, k3huf.build_table(k3huf.layer_info(blob)["codelen"]))
-    streams = [torch.cuda.Stream() for _ in range(300)]
     outs = [torch.full((x.size,), 0xA5, dtype=torch.uint8, device=DEV) for _ in streams]
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     torch.cuda.synchronize()   # poison and status prepared on the current stream
-    say("register 300 streams")
+    say("register 300 raw streams")
     for s, o in zip(streams, outs):
         k3huf.decode_layer(db, dl, o, status, s)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     for k, o in enumerate(outs):
         assert (o.cpu().numpy() == x).all(), k
-    return streams
+    yield streams
+    torch.cuda.synchronize()
+    for h in handles:
+        assert hip.hipStreamDestroy(h) == 0
 
 
 def test_concurrent_decodes_past_the_counter_slots(many_streams):
@@ -463,7 +551,9 @@ def test_ticketed_schedule_parity(kind):
 @pytest.mark.parametrize("layer", ["tiny", "edge_fib40", "edge_single", "edge_uniform", "heavy", "trunk"])
 def test_unslotted_stream_parity(many_streams, layer):
     """Every config decodes right on a stream past the counter slots (each
-    workgroup's share of units handed to its waves from its own counter)."""
+    workgroup's share of units handed to its waves from its own counter);
+    the trunk layer is the case of more than five rounds of units without
+    device counters."""
     gen = {"tiny": synth.tiny, "heavy": synth.heavy, "trunk": synth.trunk_layer,
            **dict(synth.CONFIGS["edge"])}[layer]
     x, blob = oracle_container(layer, gen)
