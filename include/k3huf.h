@@ -285,6 +285,28 @@ int64_t k3huf_encode_work_bytes(uint64_t raw_bytes);
 int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
                                void* d_work, uint64_t work_bytes, void* stream);
 
+/*
+ * k3huf_encode_layer_dev_static -- k3huf_encode_layer_dev without any
+ * allocation, for callers that cannot allocate device or pinned memory (code
+ * that must not call hipMalloc or hipHostMalloc, harnesses that forbid it).
+ * Same result, byte for byte, as k3huf_encode_layer_dev on the same layer.
+ * Its work buffer is a library-owned device array of about 3.3 MB (one copy
+ * per GPU, held until the process ends) and its host staging is a
+ * library-owned host array (about 132 KB); so layers are limited to
+ * raw_bytes <= K3HUF_STATIC_MAX_RAW (4 GiB), and the host round trips are
+ * copies from pageable memory. The arrays keep the last call's contents; each
+ * call clears what must start at zero with a kernel. Calls are serialized
+ * inside the library (a second caller waits for the first to return), and
+ * each call is synchronous, so calls never overlap on a GPU.
+ * d_raw, raw_bytes, d_out, cap, stream: as for k3huf_encode_layer_dev.
+ * Returns the container size, K3HUF_E_ARG (as for k3huf_encode_layer_dev,
+ * and for raw_bytes above K3HUF_STATIC_MAX_RAW), K3HUF_E_HIP, or
+ * K3HUF_E_CORRUPT (d_raw changed during the call).
+ */
+#define K3HUF_STATIC_MAX_RAW (1ull << 32)
+int64_t k3huf_encode_layer_dev_static(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
+                                      void* stream);
+
 /* Static text for a return code. */
 const char* k3huf_strerror(int code);
 

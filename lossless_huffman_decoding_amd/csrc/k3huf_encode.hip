@@ -602,8 +602,6 @@ std::vector<std::pair<void*, size_t>> g_pin_pool;
 struct PinnedLease {
     void* p = nullptr;
     size_t n = 0;
-    hipStream_t pending = nullptr;   // stream with copies queued from p, if any
-    bool queued = false;
     explicit PinnedLease(size_t want) {
         std::lock_guard<std::mutex> lk(g_pin_mu);
         for (size_t i = 0; i < g_pin_pool.size(); ++i)
@@ -625,13 +623,39 @@ struct PinnedLease {
     }
     ~PinnedLease() {
         if (!p) return;
-        if (queued) (void)hipStreamSynchronize(pending);
         std::lock_guard<std::mutex> lk(g_pin_mu);
         g_pin_pool.emplace_back(p, n);
     }
     PinnedLease(const PinnedLease&) = delete;
     PinnedLease& operator=(const PinnedLease&) = delete;
 };
+
+// Waits for `st` on scope exit while work of the call may still be queued on
+// it (an error path returns early), so that neither the host staging nor the
+// work buffer is reused under a pending copy or kernel.
+struct QueueGuard {
+    hipStream_t st;
+    bool queued = false;
+    explicit QueueGuard(hipStream_t s) : st(s) {}
+    ~QueueGuard() {
+        if (queued) (void)hipStreamSynchronize(st);
+    }
+};
+
+// Bytes of host staging a call needs for ns stripes: the histograms, the
+// layer header with its stripe offsets, the stripe geometry, a status word.
+struct HostStageLayout {
+    size_t hist, hdr, geom, status, total;
+};
+HostStageLayout host_stage_layout(uint32_t ns) {
+    HostStageLayout h;
+    h.hist = 0;
+    h.hdr = size_t(ns) * 256 * 8;
+    h.geom = h.hdr + pad256(K3HUF_HDR_BYTES + 8ull * ns);
+    h.status = h.geom + ((size_t(ns) * sizeof(StripeDev) + 15) & ~size_t(15));
+    h.total = h.status + 16;
+    return h;
+}
 
 // blocks of `kernel` (block size `threads`, no dynamic LDS) resident on the
 // current device at once, or 0 when the runtime cannot tell
@@ -645,29 +669,13 @@ int resident_blocks(K kernel, int threads) {
     return cus * per;
 }
 
-}  // namespace
-
-extern "C" {
-
-int64_t k3huf_encode_work_bytes(uint64_t raw_bytes) {
-    if (!raw_bytes || (raw_bytes & 1)) return K3HUF_E_ARG;
-    return int64_t(work_layout(raw_bytes).total);
-}
-
-int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
-                               void* d_work, uint64_t work_bytes, void* stream) {
-    if (!d_raw || !d_out || !d_work || !raw_bytes || (raw_bytes & 1)) return K3HUF_E_ARG;
-    if ((reinterpret_cast<uintptr_t>(d_raw) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15) ||
-        (reinterpret_cast<uintptr_t>(d_work) & 15))
-        return K3HUF_E_ARG;
-    const int64_t bound = k3huf_encode_bound(raw_bytes);
-    if (bound < 0 || uint64_t(bound) > cap) return K3HUF_E_ARG;
+// One encode: device layer raw -> container out, with the device work buffer
+// `work` (work_layout(raw_bytes).total bytes), host staging `host`
+// (host_stage_layout(ns).total bytes) and stripe geometry storage g (ns
+// entries). Allocates nothing; synchronous.
+int64_t encode_dev(const uint8_t* raw, uint64_t raw_bytes, uint8_t* out, uint64_t cap, uint8_t* work,
+                   hipStream_t st, uint8_t* host, StripeGeom* g) {
     const WorkLayout wl = work_layout(raw_bytes);
-    if (work_bytes < wl.total) return K3HUF_E_ARG;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const uint8_t* raw = static_cast<const uint8_t*>(d_raw);
-    uint8_t* out = static_cast<uint8_t*>(d_out);
-    uint8_t* work = static_cast<uint8_t*>(d_work);
     const uint32_t ns = k3huf_detail::stripes_for(raw_bytes);
     const uint64_t n_chunks = (raw_bytes / 2 + K3HUF_LANE_SYMS - 1) / K3HUF_LANE_SYMS;
     auto* hist = reinterpret_cast<unsigned long long*>(work + wl.hist);
@@ -675,9 +683,16 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     auto* look = reinterpret_cast<uint64_t*>(work + wl.look);
     auto* status = reinterpret_cast<uint32_t*>(work + wl.status);   // [0] status, [1] block ticket
     auto* edges = reinterpret_cast<UnitEdges*>(work + wl.edges);
+    const HostStageLayout hl = host_stage_layout(ns);
+    const uint64_t* h = reinterpret_cast<const uint64_t*>(host + hl.hist);
+    uint8_t* host_hdr = host + hl.hdr;
+    StripeDev* gd = reinterpret_cast<StripeDev*>(host + hl.geom);
+    uint32_t* host_status = reinterpret_cast<uint32_t*>(host + hl.status);
+    QueueGuard guard(st);
 
     // 1. per-stripe histograms (the look-back words, the status word and the
-    // block ticket are cleared with them)
+    // block ticket are cleared with them, by a kernel)
+    guard.queued = true;
     hipLaunchKernelGGL(enc_fill_zero, dim3(64), dim3(256), 0, st, reinterpret_cast<uint4*>(work),
                        wl.total / 16);
     const int hist_res = resident_blocks(enc_hist, kHistThreads);
@@ -685,22 +700,9 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     hipLaunchKernelGGL(enc_hist, dim3(hist_per_stripe, ns), dim3(kHistThreads), 0, st, raw,
                        raw_bytes, hist);
     if (launched()) return K3HUF_E_HIP;
-    // pinned staging: histograms, layer header, stripe geometry, status word
-    const size_t hist_b = size_t(ns) * 256 * 8, hdr_b = pad256(K3HUF_HDR_BYTES + 8ull * ns);
-    const size_t geom_b = (size_t(ns) * sizeof(StripeDev) + 15) & ~size_t(15);
-    PinnedLease pin(hist_b + hdr_b + geom_b + 16);
-    if (!pin.p) return K3HUF_E_HIP;
-    uint8_t* pin_b = static_cast<uint8_t*>(pin.p);
-    const uint64_t* h = reinterpret_cast<const uint64_t*>(pin_b);
-    uint8_t* pin_hdr = pin_b + hist_b;
-    StripeDev* gd = reinterpret_cast<StripeDev*>(pin_hdr + hdr_b);
-    uint32_t* pin_status = reinterpret_cast<uint32_t*>(pin_hdr + hdr_b + geom_b);
-    pin.pending = st;
-    pin.queued = true;
-    if (hipMemcpyAsync(pin_b, hist, hist_b, hipMemcpyDeviceToHost, st) != hipSuccess ||
+    if (hipMemcpyAsync(host + hl.hist, hist, hl.hdr - hl.hist, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
         return K3HUF_E_HIP;
-    pin.queued = false;
 
     // 2. code lengths, canonical codes and the layout, on the host
     uint64_t count[256] = {};
@@ -712,18 +714,16 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     k3huf_detail::canonical_codes(len, code);
     CodeTable ct;
     for (int v = 0; v < 256; ++v) ct.e[v] = (uint32_t(len[v]) << 16) | code[v];
-    std::vector<StripeGeom> g;
     uint32_t nsb_total = 0;
     const uint64_t total = k3huf_detail::layout(raw_bytes, h, len, g, &nsb_total);
     if (total > cap) return K3HUF_E_ARG;
-    k3huf_detail::write_layer_header(pin_hdr, raw_bytes, len, g, nsb_total, total);
+    k3huf_detail::write_layer_header(host_hdr, raw_bytes, len, g, nsb_total, total);
     for (uint32_t s = 0; s < ns; ++s)
         gd[s] = StripeDev{g[s].raw0, g[s].off, g[s].raw, g[s].n, g[s].nsb, g[s].nbits,
                           g[s].bit_bytes, g[s].bits_off, g[s].even_off, 0u};
 
     // 3. headers, then the byte work
-    pin.queued = true;
-    if (hipMemcpyAsync(out, pin_hdr, hdr_b, hipMemcpyHostToDevice, st) != hipSuccess ||
+    if (hipMemcpyAsync(out, host_hdr, hl.geom - hl.hdr, hipMemcpyHostToDevice, st) != hipSuccess ||
         hipMemcpyAsync(geom, gd, size_t(ns) * sizeof(StripeDev), hipMemcpyHostToDevice, st) != hipSuccess)
         return K3HUF_E_HIP;
     const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
@@ -733,12 +733,81 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
     hipLaunchKernelGGL(enc_edges, dim3(unsigned((n_units + 255) / 256)), dim3(256), 0, st, edges,
                        n_units, geom, out);
     if (launched()) return K3HUF_E_HIP;
-    if (hipMemcpyAsync(pin_status, status, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+    if (hipMemcpyAsync(host_status, status, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
         return K3HUF_E_HIP;
-    pin.queued = false;
-    const uint32_t bad = *pin_status;
+    guard.queued = false;
+    const uint32_t bad = *host_status;
     return (bad & 2u) ? K3HUF_E_HIP : bad ? K3HUF_E_CORRUPT : int64_t(total);
+}
+
+// Argument checks shared by the two entry points (sizes, alignment, capacity).
+bool encode_args_ok(const void* d_raw, uint64_t raw_bytes, const void* d_out, uint64_t cap) {
+    if (!d_raw || !d_out || !raw_bytes || (raw_bytes & 1)) return false;
+    if ((reinterpret_cast<uintptr_t>(d_raw) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15)) return false;
+    const int64_t bound = k3huf_encode_bound(raw_bytes);
+    return bound >= 0 && uint64_t(bound) <= cap;
+}
+
+// The entry point without allocation: its work buffer is this file-scope
+// device array (one per GPU, kept until the process ends), its host staging
+// and stripe geometry are file-scope host arrays. Layers up to
+// K3HUF_STATIC_MAX_RAW bytes: 64 stripes and 131,072 packing units.
+constexpr uint32_t kStaticStripes = uint32_t(K3HUF_STATIC_MAX_RAW / K3HUF_STRIPE_BYTES);
+constexpr uint64_t kStaticUnits = K3HUF_STATIC_MAX_RAW / 2 / K3HUF_LANE_SYMS / kUnitChunks;
+constexpr uint64_t kStaticWorkBytes = 256 * 8 * kStaticStripes + 256 + sizeof(StripeDev) * kStaticStripes +
+                                      256 + sizeof(UnitEdges) * kStaticUnits + 256 + 8 * kStaticUnits + 256 +
+                                      256;
+static __device__ __align__(256) uint8_t scratch[kStaticWorkBytes];
+alignas(64) uint8_t g_static_host[size_t(256) * 8 * kStaticStripes +
+                                  256 * ((K3HUF_HDR_BYTES + 8 * kStaticStripes + 255) / 256) +
+                                  sizeof(StripeDev) * kStaticStripes + 16 + 16];
+StripeGeom g_static_geom[kStaticStripes];
+std::mutex g_static_mu;                  // one call at a time uses the arrays
+constexpr int kMaxDevices = 64;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};  // per device: the address of `scratch` there
+
+}  // namespace
+
+extern "C" {
+
+int64_t k3huf_encode_work_bytes(uint64_t raw_bytes) {
+    if (!raw_bytes || (raw_bytes & 1)) return K3HUF_E_ARG;
+    return int64_t(work_layout(raw_bytes).total);
+}
+
+int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
+                               void* d_work, uint64_t work_bytes, void* stream) {
+    if (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 15) || !encode_args_ok(d_raw, raw_bytes, d_out, cap))
+        return K3HUF_E_ARG;
+    if (work_bytes < work_layout(raw_bytes).total) return K3HUF_E_ARG;
+    const uint32_t ns = k3huf_detail::stripes_for(raw_bytes);
+    PinnedLease pin(host_stage_layout(ns).total);
+    if (!pin.p) return K3HUF_E_HIP;
+    std::vector<StripeGeom> g(ns);
+    return encode_dev(static_cast<const uint8_t*>(d_raw), raw_bytes, static_cast<uint8_t*>(d_out), cap,
+                      static_cast<uint8_t*>(d_work), static_cast<hipStream_t>(stream),
+                      static_cast<uint8_t*>(pin.p), g.data());
+}
+
+int64_t k3huf_encode_layer_dev_static(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
+                                      void* stream) {
+    if (!encode_args_ok(d_raw, raw_bytes, d_out, cap) || raw_bytes > K3HUF_STATIC_MAX_RAW ||
+        work_layout(raw_bytes).total > sizeof(scratch) ||
+        host_stage_layout(k3huf_detail::stripes_for(raw_bytes)).total > sizeof(g_static_host))
+        return K3HUF_E_ARG;
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return K3HUF_E_HIP;
+    if (!g_scratch_ptr[dev]) {
+        // first call on this device (current here): the device address of
+        // its copy of the array; host code uses only this address
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return K3HUF_E_HIP;
+        g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+    }
+    return encode_dev(static_cast<const uint8_t*>(d_raw), raw_bytes, static_cast<uint8_t*>(d_out), cap,
+                      g_scratch_ptr[dev], static_cast<hipStream_t>(stream), g_static_host, g_static_geom);
 }
 
 }  // extern "C"

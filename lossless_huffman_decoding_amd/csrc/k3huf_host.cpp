@@ -5,7 +5,6 @@
 
 #include <algorithm>
 #include <cstring>
-#include <queue>
 #include <thread>
 #include <vector>
 
@@ -33,30 +32,55 @@ int kraft_units(const uint8_t* len) {
 
 // Huffman leaf depths with a binary heap keyed (weight, node id); leaves get
 // ids 0.. in ascending symbol order and merged nodes the following ids, so the
-// tree -- and the container -- is reproducible.
+// tree -- and the container -- is reproducible. Fixed-size arrays: at most 256
+// leaves and 255 merged nodes, no heap allocation.
 void huffman_depths(const uint64_t* count, uint8_t* depth) {
     struct Node { uint64_t w; int id; };
-    auto cmp = [](const Node& a, const Node& b) { return a.w != b.w ? a.w > b.w : a.id > b.id; };
-    std::priority_queue<Node, std::vector<Node>, decltype(cmp)> heap(cmp);
-    std::vector<int> parent;
+    auto before = [](const Node& a, const Node& b) { return a.w != b.w ? a.w < b.w : a.id < b.id; };
+    Node heap[256];
+    int size = 0, nodes = 0;
+    int parent[511];
     int leaf[256];
+    auto push = [&](Node x) {
+        int i = size++;
+        while (i > 0 && before(x, heap[(i - 1) / 2])) {
+            heap[i] = heap[(i - 1) / 2];
+            i = (i - 1) / 2;
+        }
+        heap[i] = x;
+    };
+    auto pop = [&]() {
+        const Node top = heap[0];
+        const Node x = heap[--size];
+        int i = 0;
+        for (;;) {
+            int c = 2 * i + 1;
+            if (c >= size) break;
+            if (c + 1 < size && before(heap[c + 1], heap[c])) ++c;
+            if (!before(heap[c], x)) break;
+            heap[i] = heap[c];
+            i = c;
+        }
+        if (size > 0) heap[i] = x;
+        return top;
+    };
     for (int s = 0; s < 256; ++s) {
         depth[s] = 0;
         leaf[s] = -1;
         if (count[s]) {
-            leaf[s] = int(parent.size());
-            heap.push({count[s], leaf[s]});
-            parent.push_back(-1);
+            leaf[s] = nodes;
+            parent[nodes] = -1;
+            push({count[s], nodes++});
         }
     }
-    while (heap.size() > 1) {
-        Node a = heap.top(); heap.pop();
-        Node b = heap.top(); heap.pop();
-        int p = int(parent.size());
-        parent.push_back(-1);
+    while (size > 1) {
+        const Node a = pop();
+        const Node b = pop();
+        const int p = nodes++;
+        parent[p] = -1;
         parent[a.id] = p;
         parent[b.id] = p;
-        heap.push({a.w + b.w, p});
+        push({a.w + b.w, p});
     }
     for (int s = 0; s < 256; ++s) {
         if (leaf[s] < 0) continue;
@@ -138,10 +162,10 @@ void canonical_codes(const uint8_t* len, uint32_t* code) {
     for (int s = 0; s < 256; ++s) code[s] = len[s] ? next[len[s]]++ : 0;
 }
 
-uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len,
-                std::vector<StripeGeom>& g, uint32_t* nsb_total) {
+uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len, StripeGeom* g,
+                uint32_t* nsb_total) {
     const uint32_t ns = stripes_for(raw_bytes);
-    g.assign(ns, StripeGeom{});
+    for (uint32_t s = 0; s < ns; ++s) g[s] = StripeGeom{};
     uint64_t o = pad256(K3HUF_HDR_BYTES + 8ull * ns);
     uint32_t nsb = 0;
     for (uint32_t s = 0; s < ns; ++s) {
@@ -164,9 +188,9 @@ uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len,
     return o;
 }
 
-void write_layer_header(uint8_t* out, uint64_t raw_bytes, const uint8_t* len,
-                        const std::vector<StripeGeom>& g, uint32_t nsb_total, uint64_t total) {
-    const uint32_t ns = uint32_t(g.size());
+void write_layer_header(uint8_t* out, uint64_t raw_bytes, const uint8_t* len, const StripeGeom* g,
+                        uint32_t nsb_total, uint64_t total) {
+    const uint32_t ns = stripes_for(raw_bytes);
     std::memset(out, 0, pad256(K3HUF_HDR_BYTES + 8ull * ns));
     std::memcpy(out, "K3HF", 4);
     wr(out + 4, 1, 2);
@@ -309,8 +333,8 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
 
     // layout: every stripe's size is known from its histogram
     uint32_t nsb_total = 0;
-    const uint64_t total = k3huf_detail::layout(raw_bytes, hist.data(), len, g, &nsb_total);
-    k3huf_detail::write_layer_header(out, raw_bytes, len, g, nsb_total, total);
+    const uint64_t total = k3huf_detail::layout(raw_bytes, hist.data(), len, g.data(), &nsb_total);
+    k3huf_detail::write_layer_header(out, raw_bytes, len, g.data(), nsb_total, total);
 
     // stripes are independent (K3 page, "key design points"): pack in parallel
     parallel_for(int(ns), threads, [&](int s) {

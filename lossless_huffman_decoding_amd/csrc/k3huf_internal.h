@@ -6,8 +6,6 @@
 
 #include <stdint.h>
 
-#include <vector>
-
 #include "k3huf.h"
 
 namespace k3huf_detail {
@@ -20,6 +18,7 @@ inline uint32_t stripes_for(uint64_t raw) {
 }
 
 // Code lengths from the layer's odd-byte histogram (false if it is empty).
+// No allocation.
 bool limited_lengths(const uint64_t* count, uint8_t* len);
 // Longest-first canonical codes for the lengths.
 void canonical_codes(const uint8_t* len, uint32_t* code);
@@ -30,15 +29,15 @@ struct StripeGeom {
 };
 
 // Geometry of every stripe from the per-stripe histograms (hist[s * 256 + v])
-// and the code lengths; returns the container size. Fills g (one entry per
-// stripe) and the subblock total.
-uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len,
-                std::vector<StripeGeom>& g, uint32_t* nsb_total);
+// and the code lengths; returns the container size. Fills g (caller storage
+// of stripes_for(raw_bytes) entries) and the subblock total. No allocation.
+uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len, StripeGeom* g,
+                uint32_t* nsb_total);
 
 // The layer header and stripe offset table (pad256(K3HUF_HDR_BYTES + 8 ns)
-// bytes, zero padded) into out.
-void write_layer_header(uint8_t* out, uint64_t raw_bytes, const uint8_t* len,
-                        const std::vector<StripeGeom>& g, uint32_t nsb_total, uint64_t total);
+// bytes, zero padded) into out, from the stripes_for(raw_bytes) entries of g.
+void write_layer_header(uint8_t* out, uint64_t raw_bytes, const uint8_t* len, const StripeGeom* g,
+                        uint32_t nsb_total, uint64_t total);
 
 }  // namespace k3huf_detail
 

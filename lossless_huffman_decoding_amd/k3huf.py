@@ -24,7 +24,9 @@ DEV_HEADER, DEV_STRIPE, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 2, 4, 8, 16
 # names the C header declares, checked by the ABI test
 EXPORTS = ("k3huf_build_table", "k3huf_layer_info", "k3huf_decode_layer", "k3huf_decode_ring",
            "k3huf_decode_ring_host", "k3huf_encode_bound", "k3huf_encode_layer",
-           "k3huf_encode_work_bytes", "k3huf_encode_layer_dev", "k3huf_strerror")
+           "k3huf_encode_work_bytes", "k3huf_encode_layer_dev", "k3huf_encode_layer_dev_static",
+           "k3huf_strerror")
+STATIC_MAX_RAW = 1 << 32   # K3HUF_STATIC_MAX_RAW
 
 
 class K3HufError(RuntimeError):
@@ -87,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.k3huf_encode_layer_dev.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp,
                                              ctypes.c_uint64, vp]
         L.k3huf_encode_layer_dev.restype = ctypes.c_int64
+        L.k3huf_encode_layer_dev_static.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp]
+        L.k3huf_encode_layer_dev_static.restype = ctypes.c_int64
         L.k3huf_strerror.argtypes = [ctypes.c_int]
         L.k3huf_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -169,6 +173,21 @@ def encode_layer_dev(d_raw, d_out=None, d_work=None, stream=None):
     size = _check(lib().k3huf_encode_layer_dev(d_raw.data_ptr(), n, d_out.data_ptr(), _nbytes(d_out),
                                                d_work.data_ptr(), _nbytes(d_work),
                                                _stream_handle(stream)), "k3huf_encode_layer_dev")
+    return d_out[:size]
+
+
+def encode_layer_dev_static(d_raw, d_out=None, stream=None):
+    """The GPU packer without allocation inside the library (its work buffer
+    and host staging are library-owned arrays; layers up to STATIC_MAX_RAW
+    bytes). ``d_out`` is allocated here when None. Returns the container as a
+    view of d_out (synchronous call)."""
+    import torch
+    n = _nbytes(d_raw)
+    if d_out is None:
+        d_out = torch.empty(encode_bound(n), dtype=torch.uint8, device=d_raw.device)
+    size = _check(lib().k3huf_encode_layer_dev_static(d_raw.data_ptr(), n, d_out.data_ptr(),
+                                                      _nbytes(d_out), _stream_handle(stream)),
+                  "k3huf_encode_layer_dev_static")
     return d_out[:size]
 
 

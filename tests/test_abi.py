@@ -224,6 +224,26 @@ def test_gpu_encoder_rejects_bad_arguments_before_any_device_call():
     assert f(raw, n, out, cap, work, wb - 1, None) == k3huf.E_ARG       # work too small
 
 
+def test_static_gpu_encoder_rejects_bad_arguments_before_any_device_call():
+    """k3huf_encode_layer_dev_static checks sizes (including its
+    K3HUF_STATIC_MAX_RAW limit), alignment and capacity on the host before
+    any HIP call (so this runs without a GPU)."""
+    L = k3huf.lib()
+    raw, out = 1 << 20, 1 << 24
+    f = L.k3huf_encode_layer_dev_static
+    n = k3huf.STATIC_MAX_RAW + 2
+    assert f(raw, n, out, k3huf.encode_bound(n), None) == k3huf.E_ARG     # above the limit
+    n = 3 * 65536 + 514
+    cap = k3huf.encode_bound(n)
+    assert f(None, n, out, cap, None) == k3huf.E_ARG
+    assert f(raw, n, None, cap, None) == k3huf.E_ARG
+    assert f(raw, n + 1, out, cap, None) == k3huf.E_ARG                   # odd size
+    assert f(raw, 0, out, cap, None) == k3huf.E_ARG
+    assert f(raw + 8, n, out, cap, None) == k3huf.E_ARG                   # misaligned input
+    assert f(raw, n, out + 4, cap, None) == k3huf.E_ARG                   # misaligned output
+    assert f(raw, n, out, cap - 1, None) == k3huf.E_ARG                   # output too small
+
+
 def test_packer_fuzz_matches_oracle():
     """The native packer against the oracle's encoder on the seeded random
     sweep of the GPU tests (random sizes and high-byte laws)."""
