@@ -251,3 +251,120 @@ def small_trunk_matrix(seed: int, rows: int, cols: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     s = math.exp(rng.uniform(math.log(0.005), math.log(0.05)))
     return f64_to_bf16_bytes(rng.standard_normal(rows * cols) * s)
+
+
+# ---------------------------------------------------------------------------
+# FP8 tensors for the exponent codec (ECF8 page, sections 1.2 and 2.1: FP8
+# weights, E4M3 or E5M2, whose exponent field is entropy coded). Values are
+# drawn as above, scaled per tensor so that the largest magnitude lands on the
+# format's largest finite value (a per-tensor amax scale), and rounded to the
+# format (round to nearest even) by torch's float8 conversion.
+
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+FP8_EXP_BITS = {"e4m3": 4, "e5m2": 5}
+
+# values of the FP8 trunk layer: the bf16 trunk layer's 585,000,000 values
+FP8_TRUNK_VALUES = TRUNK_LAYER_BYTES // 2
+
+
+def fp8_bytes(x: np.ndarray, fmt: str = "e4m3", amax: float | None = None) -> np.ndarray:
+    """Scale x so that max |x| (or ``amax``) maps to the format's largest
+    finite value, round to FP8 and return the bytes (uint8)."""
+    import torch
+    x = np.asarray(x, dtype=np.float64)
+    m = float(np.abs(x).max()) if amax is None else float(amax)
+    scale = FP8_MAX[fmt] / m if m > 0 else 1.0
+    t = torch.from_numpy((x * scale).astype(np.float32))
+    dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    return t.to(dt).view(torch.uint8).numpy().copy()
+
+
+def e8_tiny(seed: int = SEED_BASE + 101, fmt: str = "e4m3") -> np.ndarray:
+    """4,194,304 FP8 values: iid N(0, 1), per-tensor amax scale."""
+    rng = np.random.default_rng(seed)
+    return fp8_bytes(rng.standard_normal(4_194_304), fmt)
+
+
+def e8_small(seed: int, n: int, fmt: str = "e4m3", sigma: float = 1.0) -> np.ndarray:
+    """n FP8 values: iid N(0, sigma), per-tensor amax scale (quick tests)."""
+    rng = np.random.default_rng((SEED_BASE, 8100, seed))
+    if n == 1:
+        return fp8_bytes(np.array([sigma * float(rng.standard_normal())]), fmt)
+    return fp8_bytes(rng.standard_normal(n) * sigma, fmt)
+
+
+def e8_trunk(seed: int = SEED_BASE + 102, n_values: int = FP8_TRUNK_VALUES, fmt: str = "e4m3") -> np.ndarray:
+    """The trunk layer's tensor cycle as FP8: tensor t is N(0, s_t) (s_t
+    log-uniform in [0.005, 0.05]) or N(1, 0.05) gains, each tensor scaled to
+    the format by its own amax; truncated to n_values."""
+    out = np.empty(n_values, dtype=np.uint8)
+    pos, t = 0, 0
+    lo, hi = math.log(0.005), math.log(0.05)
+    while pos < n_values:
+        spec = TRUNK_CYCLE[t % len(TRUNK_CYCLE)]
+        cnt = spec[1] * spec[2] if spec[0] == "W" else spec[1]
+        take = min(cnt, n_values - pos)
+        vals = np.empty(take, dtype=np.float64)
+
+        def job(c, t=t, spec=spec, vals=vals, take=take):
+            p = c * CHUNK
+            m = min(CHUNK, take - p)
+            rng = np.random.default_rng((seed, t, 1, c))
+            if spec[0] == "W":
+                s = math.exp(np.random.default_rng((seed, t)).uniform(lo, hi))
+                vals[p:p + m] = rng.standard_normal(m) * s
+            else:
+                vals[p:p + m] = 1.0 + 0.05 * rng.standard_normal(m)
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(job, range(-(-take // CHUNK))))
+        out[pos:pos + take] = fp8_bytes(vals, fmt)
+        pos += take
+        t += 1
+    return out
+
+
+def e8_heavy(seed: int = SEED_BASE + 103, n_values: int = 256 << 20, fmt: str = "e4m3") -> np.ndarray:
+    """Symmetric alpha-stable (alpha = 1.7, scale 0.01) values clipped to
+    +-64, scaled so that 64 maps to the format's largest value (the clip
+    bound as amax), as FP8."""
+    vals = np.empty(n_values, dtype=np.float64)
+
+    def job(c):
+        p = c * CHUNK
+        m = min(CHUNK, n_values - p)
+        rng = np.random.default_rng((seed, c))
+        vals[p:p + m] = np.clip(_alpha_stable_sym(rng, m, 1.7) * 0.01, -64.0, 64.0)
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(job, range(-(-n_values // CHUNK))))
+    return fp8_bytes(vals, fmt, amax=64.0)
+
+
+def e8_one_exponent(seed: int, n: int, fmt: str = "e4m3") -> np.ndarray:
+    """n FP8 values that all share one exponent field (+-[1, 2) scaled to the
+    format), random signs and mantissas: a one-symbol exponent plane."""
+    rng = np.random.default_rng((SEED_BASE, 8200, seed))
+    m = 3 if fmt == "e4m3" else 2
+    e = 7 if fmt == "e4m3" else 15
+    sign = rng.integers(0, 2, n, dtype=np.uint8) << 7
+    mant = rng.integers(0, 1 << m, n, dtype=np.uint8)
+    return (sign | np.uint8(e << m) | mant).astype(np.uint8)
+
+
+def e8_uniform_bytes(seed: int, n: int) -> np.ndarray:
+    """n uniformly random bytes (every exponent field equally likely; in E4M3
+    this includes the NaN patterns, which the codec keeps like any byte)."""
+    return np.random.default_rng((SEED_BASE, 8300, seed)).integers(0, 256, n, dtype=np.uint8)
+
+
+def e8_fib_exponents(seed: int, n: int, k: int = 18) -> np.ndarray:
+    """n E5M2 bytes whose exponent fields 0..k-1 occur with Fibonacci-like
+    counts (as in edge_fib40), random signs and mantissas: the unsmoothed
+    Huffman tree is deeper than 16 bits."""
+    rng = np.random.default_rng((SEED_BASE, 8400, seed))
+    f = np.array(_fibonacci(k), dtype=np.float64)
+    c = np.maximum(1, np.floor(f * n / f.sum())).astype(np.int64)
+    c[-1] += n - c.sum()
+    exps = rng.permutation(np.repeat(np.arange(k, dtype=np.uint8), c))
+    sign = rng.integers(0, 2, n, dtype=np.uint8) << 7
+    mant = rng.integers(0, 4, n, dtype=np.uint8)
+    return (sign | (exps << 2) | mant).astype(np.uint8)

@@ -1,4 +1,5 @@
-"""ctypes wrapper around the plain C oracle (k3huf_oracle.c).
+"""ctypes wrapper around the plain C oracles (k3huf_oracle.c: the bf16
+high-byte codec; e8huf_oracle.c: the FP8 exponent codec).
 
 TEST INFRASTRUCTURE ONLY: the product path must never import this module.
 Every function here calls straight into the C oracle; see that file's header
@@ -14,7 +15,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "k3huf_oracle.c")
+_SRCS = [os.path.join(_HERE, "k3huf_oracle.c"), os.path.join(_HERE, "e8huf_oracle.c")]
 _LIB = os.path.join(_HERE, "_build", "liboracle.so")
 
 OK, E_ARG, E_EMPTY, E_OVERSUB, E_BADLEN, E_OVERLAP, E_FORMAT, E_CORRUPT, E_INDEX = (
@@ -25,11 +26,11 @@ MAXLEN = 12
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc into oracle/_build/liboracle.so."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(map(os.path.getmtime, _SRCS)):
         os.makedirs(os.path.dirname(_LIB), exist_ok=True)
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC",
-                               "-o", tmp, _SRC])
+                               "-o", tmp, *_SRCS])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -71,6 +72,28 @@ def lib():
         L.oh_check_index.restype = ctypes.c_int
         L.oh_raw_bytes.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
         L.oh_raw_bytes.restype = ctypes.c_int64
+        L.e8_kraft.argtypes = [u8p]
+        L.e8_kraft.restype = ctypes.c_int64
+        L.e8_code_lengths.argtypes = [u64p, u8p]
+        L.e8_code_lengths.restype = ctypes.c_int
+        L.e8_canonical.argtypes = [u8p, ctypes.POINTER(ctypes.c_uint32)]
+        L.e8_canonical.restype = None
+        L.e8_check_table.argtypes = [u8p]
+        L.e8_check_table.restype = ctypes.c_int
+        L.e8_decode_prefix.argtypes = [u8p, ctypes.c_uint32, ctypes.POINTER(ctypes.c_int),
+                                       ctypes.POINTER(ctypes.c_int)]
+        L.e8_decode_prefix.restype = ctypes.c_int
+        L.e8_encode_bound.argtypes = [ctypes.c_uint64]
+        L.e8_encode_bound.restype = ctypes.c_int64
+        L.e8_encode.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_uint64]
+        L.e8_encode.restype = ctypes.c_int64
+        L.e8_decode.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64]
+        L.e8_decode.restype = ctypes.c_int
+        L.e8_check_index.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
+        L.e8_check_index.restype = ctypes.c_int
+        L.e8_n_values.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
+        L.e8_n_values.restype = ctypes.c_int64
         _lib = L
     return _lib
 
@@ -181,3 +204,85 @@ def decode_stripes(blob, first: int, count: int, out_cap: int) -> np.ndarray:
 def check_index(blob) -> int:
     b = _u8(blob)
     return lib().oh_check_index(b.ctypes.data, b.size)
+
+
+# ---------------------------------------------------------------------------
+# FP8 exponent codec (e8huf_oracle.c)
+
+E8_MAXLEN = 16
+
+
+def _len32(lengths) -> np.ndarray:
+    ln = np.zeros(32, np.uint8)
+    ln[: len(lengths)] = lengths
+    return ln
+
+
+def e8_code_lengths(counts):
+    """(code lengths[32], smoothing rounds) for up to 32 exponent counts."""
+    c = np.zeros(32, np.uint64)
+    c[: len(counts)] = counts
+    d = np.zeros(32, np.uint8)
+    rounds = lib().e8_code_lengths(_p(c, ctypes.c_uint64), _p(d))
+    return d, rounds
+
+
+def e8_kraft(lengths) -> int:
+    return lib().e8_kraft(_p(_len32(lengths)))
+
+
+def e8_canonical(lengths) -> np.ndarray:
+    c = np.zeros(32, np.uint32)
+    lib().e8_canonical(_p(_len32(lengths)), _p(c, ctypes.c_uint32))
+    return c
+
+
+def e8_check_table(lengths) -> int:
+    return lib().e8_check_table(_p(_len32(lengths)))
+
+
+def e8_decode_prefix(lengths, bits16: int):
+    """(symbol, code length) of the code that prefixes the 16-bit string, or None."""
+    s, l = ctypes.c_int(), ctypes.c_int()
+    if lib().e8_decode_prefix(_p(_len32(lengths)), bits16, ctypes.byref(s), ctypes.byref(l)) < 0:
+        return None
+    return s.value, l.value
+
+
+def e8_encode(x, exp_bits: int = 4) -> np.ndarray:
+    """Container bytes for FP8 bytes x (E4M3: exp_bits 4, E5M2: 5)."""
+    r = _u8(x)
+    cap = lib().e8_encode_bound(r.size)
+    if cap < 0:
+        raise ValueError("oracle e8 encode: bad size")
+    out = np.empty(cap, np.uint8)
+    n = lib().e8_encode(r.ctypes.data, r.size, exp_bits, out.ctypes.data, cap)
+    if n < 0:
+        raise ValueError("oracle e8 encode failed: %d" % n)
+    return out[:n]
+
+
+def e8_decode(blob) -> np.ndarray:
+    b = _u8(blob)
+    n = lib().e8_n_values(b.ctypes.data, b.size)
+    if n < 0:
+        raise ValueError("oracle e8: bad container header: %d" % n)
+    out = np.empty(n, np.uint8)
+    rc = lib().e8_decode(b.ctypes.data, b.size, out.ctypes.data, n)
+    if rc:
+        raise ValueError("oracle e8 decode failed: %d" % rc)
+    return out
+
+
+def e8_decode_rc(blob) -> int:
+    b = _u8(blob)
+    n = lib().e8_n_values(b.ctypes.data, b.size)
+    if n < 0:
+        return int(n)
+    out = np.empty(n, np.uint8)
+    return lib().e8_decode(b.ctypes.data, b.size, out.ctypes.data, n)
+
+
+def e8_check_index(blob) -> int:
+    b = _u8(blob)
+    return lib().e8_check_index(b.ctypes.data, b.size)
