@@ -1,8 +1,8 @@
 """Compile the k3huf HIP library for gfx950, in-tree.
 
 Produces lossless_huffman_decoding_amd/_lib/libk3huf.so from csrc/ with hipcc
-(decode kernels and ring drivers, GPU encoder) and g++ (host table build,
-header parsing, packer).
+(decode kernels and ring drivers, GPU encoder, FP8 exponent decoder) and g++
+(host table builds, header parsing, packers).
 Always recompiles when called (the build check wants a real compile).
 """
 
@@ -40,13 +40,14 @@ def build(verbose: bool = False) -> str:
     bdir = os.path.join(OUT_DIR, "_obj")
     os.makedirs(bdir, exist_ok=True)
     objs = []
-    for name in ("k3huf_decode", "k3huf_encode"):
+    for name in ("k3huf_decode", "k3huf_encode", "e8huf_decode"):
         o = os.path.join(bdir, name + ".o")
         _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
         objs.append(o)
-    o = os.path.join(bdir, "k3huf_host.o")
-    _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "k3huf_host.cpp"), "-o", o])
-    objs.append(o)
+    for name in ("k3huf_host", "e8huf_host"):
+        o = os.path.join(bdir, name + ".o")
+        _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, name + ".cpp"), "-o", o])
+        objs.append(o)
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-pthread", *objs, "-o", tmp])
     os.replace(tmp, LIB)

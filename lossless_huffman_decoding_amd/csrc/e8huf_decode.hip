@@ -1,0 +1,462 @@
+// gfx950 decoder of the FP8 exponent codec (include/e8huf.h).
+//
+// What is computed (ECF8 page, "指数集中现象：GenAI模型权重压缩的理论基础",
+// pwwt.cn/news/2030120): FP8 values (section 1.2) whose exponent fields were
+// Huffman coded (codes of at most 16 bits, section 2.1) are rebuilt from the
+// codes and the raw sign/mantissa nibbles. Section 2.2's decoder gives each
+// thread its start bit from per-block metadata, decodes into on-chip memory
+// and writes the output out coalesced; section 2.1's two-level table (8-bit
+// first level, 8-bit second level) resolves the codes.
+//
+// How it is laid out on the GPU (not from the page): one wave decodes one
+// block of 16,384 values; lane t decodes its lane chunk t (256 values) from
+// the start bit the block record's prefix sum gives it. The block's codes are
+// copied into the wave's LDS buffer first. The workgroup derives, from the
+// two-level table, an LDS table on 12-bit prefixes whose entries hold up to
+// three whole codes (the codes of frequent exponents are 2-4 bits long);
+// codes longer than 12 bits go through the second level of the two-level
+// table, kept in LDS too. Decoded exponents are staged in LDS rows, so that
+// each output store instruction writes whole 128-byte lines, combined with
+// the sign/mantissa nibbles on the way out.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "e8huf.h"
+
+namespace {
+
+constexpr int kWaves = 7;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLanes = 64;
+constexpr int kChunk = int(E8HUF_LANE_VALUES);        // values per lane chunk
+constexpr int kPhase = 128;                           // values per lane per phase
+constexpr int kPhases = kChunk / kPhase;              // 2
+constexpr int kRounds = kLanes / 8;                   // store rounds per phase (8 chunks each)
+constexpr int kBufBytes = 8192;                       // per-wave bitstream buffer
+constexpr int kBufUnits = kBufBytes / 16;
+constexpr int kStageStride = kPhase + 4;              // odd dword count: no bank conflicts on row writes
+constexpr int kWaveLds = kBufBytes + kLanes * kStageStride;
+constexpr int kTabEntries = 4096;                     // 12-bit decode table
+constexpr int kLookups = 4;                           // lookups per 64-bit window (an escape takes 16 bits)
+constexpr int kMaxWindows = (kPhase + kLookups - 1) / kLookups;
+constexpr int kLdsBytes = kTabEntries * 4 + E8HUF_LUT_MAX * 2 + 64 + kWaves * kWaveLds;
+static_assert(kLdsBytes <= 163840, "LDS budget");
+
+// 12-bit table entry:
+//   [23:0]  up to three exponent symbols, one per byte, first code lowest
+//   [25:24] symbols in the entry (0 for an escape)
+//   [29:26] bits the entry's codes take (0..12)
+//   [30]    no code covers the prefix (decoded as one bad 12-bit code)
+//   [31]    escape: the first code is longer than 12 bits; [7:0] holds its
+//           level-2 table
+constexpr uint32_t kEsc = 1u << 31;
+constexpr uint32_t kBadE = 1u << 30;
+__device__ __forceinline__ uint32_t e_count(uint32_t e) { return (e >> 24) & 3u; }
+__device__ __forceinline__ uint32_t e_bits(uint32_t e) { return (e >> 26) & 15u; }
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+struct Args {
+    const uint8_t* blob;
+    uint64_t blob_bytes;
+    const uint16_t* lut;
+    uint32_t lut_entries;
+    uint8_t* out;
+    uint64_t n;
+    uint32_t* status;
+};
+
+__device__ __forceinline__ uint32_t ld32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ uint64_t ld64(const uint8_t* p) { return *reinterpret_cast<const uint64_t*>(p); }
+__device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_amdgcn_perm(0u, x, 0x00010203u); }
+__device__ __forceinline__ void flag(uint32_t* status, uint32_t bit) {
+    if (status) atomicOr(status, bit);
+}
+__device__ __forceinline__ uint32_t bit(bool c) { return c ? 1u : 0u; }
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+// inclusive prefix sum over the 64 lanes (DPP row shifts, then row broadcasts)
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);
+    return x;
+}
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) { return __builtin_amdgcn_readlane(v, l); }
+
+// The code at the start of the 16-bit string s16 (first bit = bit 15; bits
+// the caller does not know are zeros) from the two-level table in LDS:
+// (symbol << 8) | length, or 0 when no code covers it. A code longer than the
+// known bits comes back too; the caller compares lengths.
+__device__ __forceinline__ uint32_t two_level(const uint16_t* l2, uint32_t s16) {
+    uint32_t e = l2[s16 >> 8];
+    if (e & 0x20u) e = l2[min(256u * (1u + (e >> 8)) + (s16 & 0xFFu), uint32_t(E8HUF_LUT_MAX - 1))];
+    return e;
+}
+
+// 12-bit table entry for prefix i: up to three whole codes of the 12 bits.
+__device__ uint32_t make_entry(const uint16_t* l2, uint32_t i) {
+    uint32_t syms = 0, k = 0, pos = 0;
+    const uint32_t first = two_level(l2, i << 4);
+    if ((first & 31u) == 0u) return kBadE | (1u << 24) | (12u << 26);   // no code: one bad 12-bit code
+    if ((first & 31u) > 12u) {
+        const uint32_t t = l2[i >> 4] >> 8;   // the level-1 link of the first 8 bits
+        return kEsc | t;
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const uint32_t e = two_level(l2, ((i << pos) & 0xFFFu) << 4);
+        const uint32_t l = e & 31u;
+        if (l == 0u || pos + l > 12u) break;
+        syms |= (e >> 8) << (8 * k);
+        ++k;
+        pos += l;
+    }
+    return syms | (k << 24) | (pos << 26);
+}
+
+// 64-bit window whose top bit is the bit after buffer bit pm1 (buffer dwords
+// held byte-swapped, bit 31 first).
+__device__ __forceinline__ uint64_t window(const uint32_t* buf, uint32_t pm1) {
+    const uint32_t* p = buf + (pm1 >> 5);
+    const uint32_t d0 = p[0], d1 = p[1], d2 = p[2];
+    const uint32_t r = ~pm1;
+    return (uint64_t(__builtin_amdgcn_alignbit(d0, d1, r)) << 32) | __builtin_amdgcn_alignbit(d1, d2, r);
+}
+
+// per-lane decode state across a block's phases
+struct Lane {
+    uint32_t pm1;      // buffer bit index of the next code, minus one
+    uint32_t cnt;      // symbols decoded so far (may pass the lane's count by two)
+    uint64_t pend;     // decoded symbols not yet written, first in the low byte
+    uint32_t np;       // how many
+    uint32_t last;     // the symbols of the last lookup and their count (count << 24)
+    uint32_t bad;      // an entry with no code or an escape with no code was taken
+};
+
+// One phase of a lane: symbols [kPhase ph, min(kPhase (ph + 1), target)) into
+// its stage row, four bytes at a time. Lanes that have their symbols take no
+// entries until the wave's slowest lane is done; at most 64 lookups finish a
+// phase, since every lookup yields a symbol.
+__device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint16_t* l2, const uint32_t* buf,
+                                             uint32_t* row, uint32_t target, uint32_t base, Lane& ls) {
+    uint32_t w = 0;   // dwords of the row written
+#pragma unroll 1
+    for (int win = 0; win < kMaxWindows; ++win) {
+        if (!__any(ls.cnt < target)) break;
+        uint64_t acc = window(buf, ls.pm1);
+#pragma unroll
+        for (int q = 0; q < kLookups; ++q) {
+            const bool live = ls.cnt < target;
+            uint32_t e = live ? tab[uint32_t(acc >> 52)] : 0u;
+            uint32_t syms = e & 0xFFFFFFu, k = e_count(e), t = e_bits(e);
+            if (__any(e & kEsc)) {
+                if (e & kEsc) {
+                    const uint32_t e2 = l2[min(256u * (1u + (e & 0xFFu)) + uint32_t((acc >> 48) & 0xFFu),
+                                               uint32_t(E8HUF_LUT_MAX - 1))];
+                    const uint32_t l = e2 & 31u;
+                    syms = e2 >> 8;
+                    k = 1u;
+                    t = l ? l : 16u;
+                    if (!l) e |= kBadE;
+                }
+            }
+            ls.bad |= e & kBadE;
+            ls.last = k ? (syms | (k << 24)) : ls.last;
+            ls.pend |= uint64_t(syms) << (8 * ls.np);
+            ls.np += k;
+            ls.cnt += k;
+            ls.pm1 += t;
+            acc <<= t;
+            if (ls.np >= 4) {
+                row[w++] = uint32_t(ls.pend);
+                ls.pend >>= 32;
+                ls.np -= 4;
+            }
+        }
+    }
+    // a lane whose count ends inside this phase writes its last bytes
+    if (target < base + kPhase && ls.np) {
+        row[w] = uint32_t(ls.pend);
+        ls.pend = 0;
+        ls.np = 0;
+    }
+}
+
+// the 16 staged exponents of chunk c at phase offset 16 part (rows are 4-byte
+// aligned, so four dword reads)
+__device__ __forceinline__ v4u staged16(const uint8_t* stage, int c, int part) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(stage + c * kStageStride + part * 16);
+    v4u r;
+    r.x = p[0];
+    r.y = p[1];
+    r.z = p[2];
+    r.w = p[3];
+    return r;
+}
+
+// FP8 bytes from 16 staged exponents (four dwords) and their 16 nibbles
+// (eight bytes: value 2i low nibble, 2i + 1 high nibble).
+__device__ __forceinline__ v4u combine(v4u ex, uint2 nib, uint32_t m, uint32_t smask, uint32_t mmask) {
+    const uint32_t lo0 = nib.x & 0x0F0F0F0Fu, hi0 = (nib.x >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lo1 = nib.y & 0x0F0F0F0Fu, hi1 = (nib.y >> 4) & 0x0F0F0F0Fu;
+    const uint32_t nb[4] = {__builtin_amdgcn_perm(hi0, lo0, 0x05010400u), __builtin_amdgcn_perm(hi0, lo0, 0x07030602u),
+                            __builtin_amdgcn_perm(hi1, lo1, 0x05010400u), __builtin_amdgcn_perm(hi1, lo1, 0x07030602u)};
+    v4u o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t e = i == 0 ? ex.x : i == 1 ? ex.y : i == 2 ? ex.z : ex.w;
+        const uint32_t v = ((nb[i] << (7u - m)) & smask) | (e << m) | (nb[i] & mmask);
+        if (i == 0) o.x = v;
+        else if (i == 1) o.y = v;
+        else if (i == 2) o.z = v;
+        else o.w = v;
+    }
+    return o;
+}
+
+__global__ __launch_bounds__(kThreads) void e8huf_decode_kernel(Args a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    __shared__ uint32_t local_ticket;
+    uint32_t* tab = reinterpret_cast<uint32_t*>(lds);
+    uint16_t* l2 = reinterpret_cast<uint16_t*>(lds + kTabEntries * 4);
+    uint8_t* lenof = lds + kTabEntries * 4 + E8HUF_LUT_MAX * 2;   // code length per exponent value
+
+    // header: must describe this call, and its planes must lie in the blob
+    const uint8_t* b = a.blob;
+    const uint32_t w1 = ld32(b + 4);
+    const uint32_t exp_bits = (w1 >> 16) & 0xFFu;
+    const uint64_t n_bits = ld64(b + 32), bits_off = ld64(b + 40), nib_off = ld64(b + 48);
+    const uint32_t n_blocks = ld32(b + 24);
+    const uint64_t nib_end = nib_off + (((a.n + 1) / 2 + 15) & ~15ull);
+    const uint32_t hdr_ok =
+        bit(ld32(b) == 0x46483845u /* "E8HF" */) & bit((w1 & 0xFFFFu) == 1u) & bit(exp_bits == 4u || exp_bits == 5u) &
+        bit((w1 >> 24) == uint32_t(E8HUF_MAXLEN)) & bit(ld64(b + 8) == a.n) & bit(ld32(b + 16) == E8HUF_BLOCK_VALUES) &
+        bit(ld32(b + 20) == E8HUF_LANE_VALUES) & bit(uint64_t(n_blocks) == (a.n + E8HUF_BLOCK_VALUES - 1) / E8HUF_BLOCK_VALUES) &
+        bit(n_bits <= uint64_t(E8HUF_MAXLEN) * a.n) & bit((bits_off & 15) == 0) & bit((nib_off & 15) == 0) &
+        bit(bits_off >= E8HUF_HDR_BYTES + uint64_t(E8HUF_BLOCK_REC_BYTES) * n_blocks) &
+        bit(nib_off >= bits_off + (n_bits + 7) / 8) & bit(nib_off < a.blob_bytes) & bit(nib_end <= a.blob_bytes);
+    if (!hdr_ok) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, E8HUF_DEV_HEADER);
+        return;
+    }
+    const uint32_t m = 7u - exp_bits;
+    const uint32_t smask = 0x80808080u, mmask = ((1u << m) - 1u) * 0x01010101u;
+
+    // the two-level table and the code lengths into LDS, then the 12-bit table
+    for (uint32_t i = threadIdx.x; i < a.lut_entries; i += kThreads) l2[i] = a.lut[i];
+    if (threadIdx.x < 32) lenof[threadIdx.x] = b[64 + threadIdx.x];
+    if (threadIdx.x == 0) local_ticket = 0u;
+    __syncthreads();
+    constexpr int kPer = (kTabEntries + kThreads - 1) / kThreads;
+    uint32_t ent[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const uint32_t i = threadIdx.x + uint32_t(q) * kThreads;
+        ent[q] = i < uint32_t(kTabEntries) ? make_entry(l2, i) : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const uint32_t i = threadIdx.x + uint32_t(q) * kThreads;
+        if (i < uint32_t(kTabEntries)) tab[i] = ent[q];
+    }
+    __syncthreads();
+
+    const int lane = int(threadIdx.x & 63);
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+    uint8_t* wl = lds + kTabEntries * 4 + E8HUF_LUT_MAX * 2 + 64 + wave * kWaveLds;
+    uint32_t* buf = reinterpret_cast<uint32_t*>(wl);
+    uint8_t* stage = wl + kBufBytes;
+    const uint8_t* bits = b + bits_off;
+    const uint8_t* nib = b + nib_off;
+    // last readable 16-byte unit (dword index from `bits`): reads stop inside
+    // the padded nibble plane, which the header check keeps in the blob
+    const int64_t dmax = int64_t(((nib_end - bits_off - 16) >> 2) & ~3ull);
+    const uint32_t G = gridDim.x;
+    uint32_t h = wave * G + blockIdx.x;   // position; block n_blocks - 1 - h
+
+    while (h < n_blocks) {
+        const uint32_t blk = n_blocks - 1u - h;
+        const uint8_t* rec = b + E8HUF_HDR_BYTES + uint64_t(E8HUF_BLOCK_REC_BYTES) * blk;
+        const uint64_t start = ld64(rec);
+        const uint64_t next = blk + 1u < n_blocks ? ld64(rec + E8HUF_BLOCK_REC_BYTES) : n_bits;
+        const uint32_t lb = reinterpret_cast<const uint16_t*>(rec + 8)[lane];
+        const uint64_t v0 = uint64_t(blk) * E8HUF_BLOCK_VALUES;
+        const uint32_t nvals = uint32_t(min(uint64_t(E8HUF_BLOCK_VALUES), a.n - v0));
+        const int lane_cnt = min(max(int(nvals) - lane * kChunk, 0), kChunk);
+        const uint32_t incl = wave_incl_scan(lb);
+        const uint32_t total = lane_value(incl, 63);
+        const bool lane_ok = lb >= uint32_t(lane_cnt) && lb <= uint32_t(lane_cnt) * E8HUF_MAXLEN;
+        const bool blk_ok = start <= n_bits && start + total == next && next <= n_bits;
+        if (!blk_ok || __any(!lane_ok)) {
+            if (lane == 0) flag(a.status, E8HUF_DEV_INDEX);
+        } else {
+            const uint64_t lane_start = start + incl - lb, lane_end = start + incl;
+            const bool full = nvals == E8HUF_BLOCK_VALUES;
+            uint32_t bad = 0, end_bad = 0;
+            // passes over consecutive lane ranges whose codes fit the buffer
+            // (one pass unless the block's codes exceed it)
+            for (int l0 = 0; l0 < kLanes;) {
+                const int64_t j0 = ((int64_t(__builtin_amdgcn_readlane(uint32_t(lane_start), l0)) |
+                                     (int64_t(__builtin_amdgcn_readlane(uint32_t(lane_start >> 32), l0)) << 32)) - 1) >> 5 & ~3ll;
+                const int64_t my_end = ((int64_t(lane_end) - 1) >> 5) + 6 & ~3ll;
+                const bool over = lane >= l0 && (my_end - j0) * 4 > kBufBytes;
+                const uint64_t ovm = __ballot(over);
+                const int l1 = ovm ? int(__builtin_ctzll(ovm)) : kLanes;   // > l0: one chunk always fits
+                const uint32_t lhi = uint32_t(lane_value(uint32_t(my_end), uint32_t(l1 - 1)));
+                const uint32_t hhi = uint32_t(lane_value(uint32_t(uint64_t(my_end) >> 32), uint32_t(l1 - 1)));
+                const int64_t end_all = int64_t((uint64_t(hhi) << 32) | lhi);
+                const int units = int((end_all - j0) / 4);
+                const bool mine = lane >= l0 && lane < l1;
+                // copy dwords [j0, j0 + 4 units) into the buffer, byte-swapped
+                {
+                    constexpr int kPerL = kBufUnits / kLanes;
+                    uint4 v[kPerL];
+#pragma unroll
+                    for (int i = 0; i < kPerL; ++i) {
+                        const int u = min(lane + kLanes * i, units - 1);
+                        const int64_t j = min(j0 + 4 * int64_t(u), dmax);
+                        v[i] = *reinterpret_cast<const uint4*>(bits + 4 * j);
+                    }
+#pragma unroll
+                    for (int i = 0; i < kPerL; ++i)
+                        reinterpret_cast<uint4*>(buf)[lane + kLanes * i] =
+                            make_uint4(bswap32(v[i].x), bswap32(v[i].y), bswap32(v[i].z), bswap32(v[i].w));
+                    wave_sync();
+                }
+                const uint32_t my_cnt = mine ? uint32_t(lane_cnt) : 0u;
+                // lanes outside the pass keep their windows at the buffer start
+                Lane ls = {mine ? uint32_t(lane_start - uint64_t(32 * j0) - 1) : 0u, 0u, 0ull, 0u, 0u, 0u};
+                const uint32_t pm1_0 = ls.pm1;
+                uint32_t* row = reinterpret_cast<uint32_t*>(stage + lane * kStageStride);
+#pragma unroll 1
+                for (int ph = 0; ph < kPhases; ++ph) {
+                    const uint32_t base = uint32_t(ph * kPhase);
+                    // the phase's nibbles, requested before its decode so that
+                    // the loads overlap it
+                    uint2 nb[kRounds];
+#pragma unroll
+                    for (int rr = 0; rr < kRounds; ++rr) {
+                        const uint32_t v = uint32_t((rr * 8 + (lane >> 3)) * kChunk + ph * kPhase + (lane & 7) * 16);
+                        const uint64_t at = v < nvals ? (v0 + v) / 2 : 0ull;
+                        nb[rr] = *reinterpret_cast<const uint2*>(nib + at);
+                    }
+                    decode_phase(tab, l2, buf, row, min(base + kPhase, my_cnt), base, ls);
+                    wave_sync();
+                    if (full && l0 == 0 && l1 == kLanes) {
+#pragma unroll
+                        for (int rr = 0; rr < kRounds; ++rr) {
+                            const int c = rr * 8 + (lane >> 3), part = lane & 7;
+                            const v4u o = combine(staged16(stage, c, part), nb[rr], m, smask, mmask);
+                            __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(a.out + v0 + uint64_t(c) * kChunk +
+                                                                                   uint64_t(ph * kPhase + part * 16)));
+                        }
+                    } else {
+#pragma unroll
+                        for (int rr = 0; rr < kRounds; ++rr) {
+                            const int c = rr * 8 + (lane >> 3), part = lane & 7;
+                            const uint32_t v = uint32_t(c * kChunk + ph * kPhase + part * 16);
+                            if (c < l0 || c >= l1 || v >= nvals) continue;
+                            const v4u o = combine(staged16(stage, c, part), nb[rr], m, smask, mmask);
+                            uint8_t* dst = a.out + v0 + v;
+                            if (v + 16 <= nvals) {
+                                *reinterpret_cast<v4u*>(dst) = o;
+                            } else {
+                                for (uint32_t i = 0; i < nvals - v; ++i) {
+                                    const uint32_t wd = i < 4 ? o.x : i < 8 ? o.y : i < 12 ? o.z : o.w;
+                                    dst[i] = uint8_t(wd >> (8 * (i & 3)));
+                                }
+                            }
+                        }
+                    }
+                    wave_sync();
+                }
+                // the last lookup may have taken symbols past the lane's
+                // count; their bits are not the lane's
+                uint32_t used = ls.pm1 - pm1_0;
+                const uint32_t k = (ls.last >> 24) & 3u;
+                for (uint32_t j = 0; j < ls.cnt - min(ls.cnt, my_cnt) && j < k; ++j)
+                    used -= lenof[(ls.last >> (8 * (k - 1 - j))) & 31u];
+                bad |= mine ? ls.bad : 0u;
+                end_bad |= bit(mine && used != lb);
+                l0 = l1;
+            }
+            // one status update per wave (every lane takes part in the votes)
+            const bool any_bad = __any(bad != 0), any_end = __any(end_bad != 0);
+            if (lane == 0 && any_bad) flag(a.status, E8HUF_DEV_CODE);
+            if (lane == 0 && any_end) flag(a.status, E8HUF_DEV_LANE_END);
+        }
+        uint32_t ticket = 0;
+        if (lane == 0) ticket = atomicAdd(&local_ticket, 1u);
+        h = uniform(blockIdx.x + G * (kWaves + lane_value(ticket, 0)));
+    }
+}
+
+struct DevGeom {
+    int cus = 0;
+    int per = 0;
+};
+std::mutex g_mu;
+std::vector<DevGeom> g_geom;
+
+int device_geom(DevGeom* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return K3HUF_E_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (int(g_geom.size()) <= dev) g_geom.resize(dev + 1);
+    DevGeom& g = g_geom[dev];
+    if (!g.cus) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, e8huf_decode_kernel, kThreads, 0) != hipSuccess)
+            return K3HUF_E_HIP;
+        g.cus = cus;
+        g.per = per > 0 ? per : 1;
+    }
+    *out = g;
+    return K3HUF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int e8huf_decode(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut, int lut_entries, void* d_out,
+                 uint64_t n_values, void* stream, uint32_t* d_status) {
+    if (!d_blob || !d_lut || !d_out) return K3HUF_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(d_blob) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15) ||
+        (reinterpret_cast<uintptr_t>(d_lut) & 1) || (reinterpret_cast<uintptr_t>(d_status) & 3))
+        return K3HUF_E_ARG;
+    if (n_values == 0 || n_values > (1ull << 40) || blob_bytes < E8HUF_HDR_BYTES + E8HUF_BLOCK_REC_BYTES ||
+        uint64_t(blob_bytes) >= (1ull << 44))
+        return K3HUF_E_ARG;
+    if (lut_entries < 256 || lut_entries > E8HUF_LUT_MAX || lut_entries % 256) return K3HUF_E_ARG;
+    DevGeom g;
+    int rc = device_geom(&g);
+    if (rc) return rc;
+    const uint64_t blocks = (n_values + E8HUF_BLOCK_VALUES - 1) / E8HUF_BLOCK_VALUES;
+    // one workgroup per block up to a full chip: a tensor of fewer blocks
+    // than CUs gets a CU per block
+    const uint64_t resident = uint64_t(g.cus) * uint64_t(g.per);
+    const unsigned grid = unsigned(blocks < resident ? blocks : resident);
+    Args a;
+    a.blob = static_cast<const uint8_t*>(d_blob);
+    a.blob_bytes = blob_bytes;
+    a.lut = d_lut;
+    a.lut_entries = uint32_t(lut_entries);
+    a.out = static_cast<uint8_t*>(d_out);
+    a.n = n_values;
+    a.status = d_status;
+    hipLaunchKernelGGL(e8huf_decode_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+    return hipGetLastError() == hipSuccess ? K3HUF_OK : K3HUF_E_HIP;
+}
+
+}  // extern "C"

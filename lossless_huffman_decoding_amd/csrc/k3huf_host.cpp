@@ -30,6 +30,27 @@ int kraft_units(const uint8_t* len) {
     return k;
 }
 
+int pick_threads(int n) {
+    if (n > 0) return n;
+    unsigned h = std::thread::hardware_concurrency();
+    return int(std::max(1u, std::min(h, 64u)));
+}
+
+template <class F>
+void parallel_for(int n, int threads, F f) {
+    threads = std::max(1, std::min(threads, n));
+    std::vector<std::thread> pool;
+    for (int t = 0; t < threads; ++t)
+        pool.emplace_back([=] {
+            for (int i = t; i < n; i += threads) f(i);
+        });
+    for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+namespace k3huf_detail {
+
 // Huffman leaf depths with a binary heap keyed (weight, node id); leaves get
 // ids 0.. in ascending symbol order and merged nodes the following ids, so the
 // tree -- and the container -- is reproducible. Fixed-size arrays: at most 256
@@ -89,27 +110,6 @@ void huffman_depths(const uint64_t* count, uint8_t* depth) {
         depth[s] = uint8_t(std::min(d, 255));
     }
 }
-
-int pick_threads(int n) {
-    if (n > 0) return n;
-    unsigned h = std::thread::hardware_concurrency();
-    return int(std::max(1u, std::min(h, 64u)));
-}
-
-template <class F>
-void parallel_for(int n, int threads, F f) {
-    threads = std::max(1, std::min(threads, n));
-    std::vector<std::thread> pool;
-    for (int t = 0; t < threads; ++t)
-        pool.emplace_back([=] {
-            for (int i = t; i < n; i += threads) f(i);
-        });
-    for (auto& th : pool) th.join();
-}
-
-}  // namespace
-
-namespace k3huf_detail {
 
 // Code lengths for the layer: Huffman depths, then the 12-bit limit (K3
 // page, "canonical code assignment and Kraft check": while the Kraft sum is

@@ -17,6 +17,11 @@ inline uint32_t stripes_for(uint64_t raw) {
     return uint32_t((raw + K3HUF_STRIPE_BYTES - 1) / K3HUF_STRIPE_BYTES);
 }
 
+// Huffman leaf depths over 256 counts (0 for absent symbols); ties in weight
+// go to the lower node id (leaves 0.. by symbol, merged nodes the following
+// ids). No allocation.
+void huffman_depths(const uint64_t* count, uint8_t* depth);
+
 // Code lengths from the layer's odd-byte histogram (false if it is empty).
 // No allocation.
 bool limited_lengths(const uint64_t* count, uint8_t* len);

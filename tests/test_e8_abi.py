@@ -1,0 +1,157 @@
+"""CPU-side checks of the FP8 exponent codec's C ABI (include/e8huf.h): the
+two-level table against the oracle's bit-by-bit decode, the header parse, and
+the native packer against the oracle's encoder, byte for byte. No GPU compute
+is called here."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from lossless_huffman_decoding_amd import e8huf, k3huf, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_e8_symbol():
+    txt = open(os.path.join(ROOT, "include", "e8huf.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = set(re.findall(r"\b(e8huf_[a-z_]+)\s*\(", txt))
+    assert names == set(e8huf.EXPORTS)
+    L = e8huf.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _lookup(lut, bits16):
+    """Two-level lookup as the header describes it: (symbol, length) or None."""
+    e = int(lut[bits16 >> 8])
+    if e & 0x20:
+        e = int(lut[256 * (1 + (e >> 8)) + (bits16 & 0xFF)])
+    if e & 0x1F == 0:
+        return None
+    return e >> 8, e & 0x1F
+
+
+def _tables():
+    rng = np.random.default_rng(21)
+    yield [1], 4
+    yield [1, 1], 4
+    yield [2, 2, 2], 4                     # under-full, prefix-free
+    yield [4] * 16, 4
+    yield [5] * 32, 5
+    yield [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 10], 4          # the golden chain code
+    yield list(O.e8_code_lengths(synth._fibonacci(16))[0]), 4    # codes up to 15 bits
+    yield list(O.e8_code_lengths(synth._fibonacci(32))[0]), 5    # smoothed, up to 16 bits
+    for _ in range(30):
+        eb = int(rng.choice([4, 5]))
+        k = int(rng.integers(2, (1 << eb) + 1))
+        counts = np.zeros(1 << eb, np.int64)
+        counts[rng.permutation(1 << eb)[:k]] = np.maximum(1, rng.geometric(rng.uniform(0.02, 0.6), k) ** 3)
+        yield list(O.e8_code_lengths(counts)[0]), eb
+
+
+def test_build_table_matches_oracle_bit_by_bit_decode():
+    """For every 16-bit string, the two-level table gives the code the oracle
+    decodes bit by bit (or none, for strings no code prefixes)."""
+    for lens, eb in _tables():
+        lut = e8huf.build_table(lens, eb)
+        assert lut.size % 256 == 0 and 256 <= lut.size <= e8huf.LUT_MAX
+        for b in range(1 << 16):
+            assert _lookup(lut, b) == O.e8_decode_prefix(lens, b), (lens, b)
+
+
+def test_build_table_golden_chain():
+    """The hand-derived table of tests/golden/e8_canonical_and_table.txt."""
+    lut = e8huf.build_table([1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 10], 4)
+    assert lut.size == 512
+    for line in open(os.path.join(ROOT, "tests", "golden", "e8_canonical_and_table.txt")):
+        r = line.split()
+        if not r or r[0].startswith("#"):
+            continue
+        if r[0] == "l1":
+            lo, hi, sym, l = map(int, r[1:])
+            assert all(int(lut[i]) == (sym << 8) | l for i in range(lo, hi + 1))
+        elif r[0] == "link":
+            assert int(lut[int(r[1])]) == (int(r[2]) << 8) | 0x20
+        elif r[0] == "l2":
+            t, lo, hi, sym, l = map(int, r[1:])
+            assert all(int(lut[256 * (1 + t) + j]) == (sym << 8) | l for j in range(lo, hi + 1))
+
+
+def test_build_table_rejections():
+    assert e8huf.build_table_rc([0] * 32, 4)[0] == k3huf.E_EMPTY
+    assert e8huf.build_table_rc([1, 1, 1], 4)[0] == k3huf.E_OVERSUB
+    assert e8huf.build_table_rc([17, 1], 5)[0] == k3huf.E_BADLEN
+    assert e8huf.build_table_rc([0] * 16 + [1, 1], 4)[0] == k3huf.E_ARG     # symbol past 2^exp_bits
+    assert e8huf.build_table_rc([1, 1], 6)[0] == k3huf.E_ARG                  # no such format
+
+
+def _same(x, eb):
+    a = O.e8_encode(x, eb)
+    b = e8huf.encode(x, eb)
+    assert a.size == b.size and (a == b).all()
+    return b
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 255, 256, 257, 16383, 16384, 16385, 3 * 16384 + 77, 1 << 20])
+def test_packer_matches_oracle(n):
+    _same(synth.e8_small(n, n), 4)
+    _same(synth.e8_small(n + 1, n, "e5m2"), 5)
+
+
+def test_packer_edge_tensors_match_oracle():
+    _same(synth.e8_one_exponent(1, 100_003), 4)
+    _same(synth.e8_uniform_bytes(3, 70_001), 4)
+    _same(synth.e8_uniform_bytes(3, 70_001), 5)
+    _same(synth.e8_fib_exponents(4, 300_007), 5)
+    x = synth.e8_tiny()
+    b = _same(x, 4)
+    info = e8huf.layer_info(b)
+    assert info["n_values"] == x.size and info["exp_bits"] == 4 and info["container_bytes"] == b.size
+    assert info["n_blocks"] == -(-x.size // 16384)
+
+
+def test_packer_code_lengths_match_smoothing_goldens():
+    """Tensors whose exponent counts are the hand-derived smoothing cases:
+    the packer's codelen equals them (ECF8 page, section 2.1)."""
+    for line in open(os.path.join(ROOT, "tests", "golden", "e8_smoothing.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        name, _, counts, want = (f.split() for f in line.split("|"))
+        counts = [int(c) for c in counts]
+        rng = np.random.default_rng(len(counts))
+        e = rng.permutation(np.repeat(np.arange(len(counts), dtype=np.uint8), counts))
+        x = ((rng.integers(0, 2, e.size, dtype=np.uint8) << 7) | (e << 2) |
+             rng.integers(0, 4, e.size, dtype=np.uint8)).astype(np.uint8)
+        b = _same(x, 5)
+        assert list(e8huf.layer_info(b)["codelen"][: len(counts)]) == [int(w) for w in want], name
+
+
+def test_layer_info_rejects_bad_headers():
+    b = e8huf.encode(synth.e8_small(5, 1000))
+    for off, val in ((0, 0x41), (6, 3), (7, 12), (16, 1)):
+        bad = b.copy()
+        bad[off] = val
+        with pytest.raises(k3huf.K3HufError):
+            e8huf.layer_info(bad)
+
+
+def test_decode_rejects_bad_arguments_before_any_device_call():
+    raw = e8huf.decode_raw
+    blob, lut, out = 1 << 20, 1 << 21, 1 << 22
+    good = 4096
+    assert raw(0, good, lut, 256, out, 100, None, None) == k3huf.E_ARG
+    assert raw(blob, good, 0, 256, out, 100, None, None) == k3huf.E_ARG
+    assert raw(blob, good, lut, 256, 0, 100, None, None) == k3huf.E_ARG
+    assert raw(blob + 8, good, lut, 256, out, 100, None, None) == k3huf.E_ARG   # misaligned blob
+    assert raw(blob, good, lut, 256, out + 4, 100, None, None) == k3huf.E_ARG   # misaligned output
+    assert raw(blob, good, lut + 1, 256, out, 100, None, None) == k3huf.E_ARG   # misaligned table
+    assert raw(blob, good, lut, 256, out, 0, None, None) == k3huf.E_ARG         # no values
+    assert raw(blob, 127, lut, 256, out, 100, None, None) == k3huf.E_ARG        # shorter than a header
+    assert raw(blob, good, lut, 300, out, 100, None, None) == k3huf.E_ARG       # table size
+    assert raw(blob, good, lut, 256 * 34, out, 100, None, None) == k3huf.E_ARG
+    assert raw(blob, 1 << 44, lut, 256, out, 100, None, None) == k3huf.E_ARG    # blob too large
+    assert raw(blob, good, lut, 256, out, (1 << 40) + 1, None, None) == k3huf.E_ARG
