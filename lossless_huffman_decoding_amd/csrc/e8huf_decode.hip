@@ -36,11 +36,14 @@ constexpr int kPhases = kChunk / kPhase;              // 2
 constexpr int kRounds = kLanes / 8;                   // store rounds per phase (8 chunks each)
 constexpr int kBufBytes = 8192;                       // per-wave bitstream buffer
 constexpr int kBufUnits = kBufBytes / 16;
-constexpr int kStageStride = kPhase + 4;              // odd dword count: no bank conflicts on row writes
+// stage row: the phase's 128 symbols, up to two carried past it plus the
+// unused third byte of the last lookup, and a spare spot where lanes outside
+// the phase write; 35 dwords (odd, so rows start in different banks)
+constexpr int kStageStride = kPhase + 12;
+constexpr uint32_t kSpare = kPhase + 5;
 constexpr int kWaveLds = kBufBytes + kLanes * kStageStride;
 constexpr int kTabEntries = 4096;                     // 12-bit decode table
-constexpr int kLookups = 4;                           // lookups per 64-bit window (an escape takes 16 bits)
-constexpr int kMaxWindows = (kPhase + kLookups - 1) / kLookups;
+constexpr int kLookups = 5;                           // lookups per 64-bit window: five 12-bit codes fit
 constexpr int kLdsBytes = kTabEntries * 4 + E8HUF_LUT_MAX * 2 + 64 + kWaves * kWaveLds;
 static_assert(kLdsBytes <= 163840, "LDS budget");
 
@@ -136,58 +139,65 @@ __device__ __forceinline__ uint64_t window(const uint32_t* buf, uint32_t pm1) {
 struct Lane {
     uint32_t pm1;      // buffer bit index of the next code, minus one
     uint32_t cnt;      // symbols decoded so far (may pass the lane's count by two)
-    uint64_t pend;     // decoded symbols not yet written, first in the low byte
-    uint32_t np;       // how many
-    uint32_t last;     // the symbols of the last lookup and their count (count << 24)
-    uint32_t bad;      // an entry with no code or an escape with no code was taken
+    uint32_t last;     // the last entry that yielded symbols
+    uint32_t bad;      // OR of the entries taken (bit 30: a prefix no code covers)
 };
 
-// One phase of a lane: symbols [kPhase ph, min(kPhase (ph + 1), target)) into
-// its stage row, four bytes at a time. Lanes that have their symbols take no
-// entries until the wave's slowest lane is done; at most 64 lookups finish a
-// phase, since every lookup yields a symbol.
+// Decode of a lane's symbols [base, target) into its stage row (byte i of the
+// row is symbol base + i). Each 64-bit window feeds kLookups lookups of the
+// 12-bit table; an entry's symbols are written as three bytes at the lane's
+// count (bytes past the entry's symbols are overwritten by the next lookup or
+// lie past the phase). A lane that has its symbols takes zero entries until
+// the wave's slowest lane is done. An escape entry (the first code is longer
+// than 12 bits) yields nothing, so the lane stays on that code for the rest
+// of the window; after the window, lanes on an escape take that one code
+// through the second-level table. Every window either yields a symbol on each
+// live lane or resolves an escape, so 2 * 64 windows always finish a phase.
+// A lookup that ends past the phase leaves up to two symbols in the row's
+// spare bytes; they move to the start of the next phase's row.
 __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint16_t* l2, const uint32_t* buf,
-                                             uint32_t* row, uint32_t target, uint32_t base, Lane& ls) {
-    uint32_t w = 0;   // dwords of the row written
+                                             uint8_t* row, uint32_t target, uint32_t base, Lane& ls) {
+    if (ls.cnt > base) {   // symbols the previous phase's last lookup carried over
+        const uint32_t k = e_count(ls.last), j = ls.cnt - base;
+        row[0] = uint8_t(ls.last >> (8 * (k - j)));
+        row[1] = uint8_t(ls.last >> (8 * (k - j + 1)));
+    }
 #pragma unroll 1
-    for (int win = 0; win < kMaxWindows; ++win) {
+    for (int win = 0; win < 2 * kPhase; ++win) {
         if (!__any(ls.cnt < target)) break;
         uint64_t acc = window(buf, ls.pm1);
+        uint32_t fl = 0;
 #pragma unroll
         for (int q = 0; q < kLookups; ++q) {
-            const bool live = ls.cnt < target;
-            uint32_t e = live ? tab[uint32_t(acc >> 52)] : 0u;
-            uint32_t syms = e & 0xFFFFFFu, k = e_count(e), t = e_bits(e);
-            if (__any(e & kEsc)) {
-                if (e & kEsc) {
-                    const uint32_t e2 = l2[min(256u * (1u + (e & 0xFFu)) + uint32_t((acc >> 48) & 0xFFu),
-                                               uint32_t(E8HUF_LUT_MAX - 1))];
-                    const uint32_t l = e2 & 31u;
-                    syms = e2 >> 8;
-                    k = 1u;
-                    t = l ? l : 16u;
-                    if (!l) e |= kBadE;
-                }
-            }
-            ls.bad |= e & kBadE;
-            ls.last = k ? (syms | (k << 24)) : ls.last;
-            ls.pend |= uint64_t(syms) << (8 * ls.np);
-            ls.np += k;
+            uint32_t e = tab[uint32_t(acc >> 52)];
+            e = ls.cnt < target ? e : 0u;
+            fl |= e;
+            // lanes past the phase (or before it) write to the row's spare bytes
+            uint8_t* p = row + min(ls.cnt - base, kSpare);
+            p[0] = uint8_t(e);
+            p[1] = uint8_t(e >> 8);
+            p[2] = uint8_t(e >> 16);
+            const uint32_t k = e_count(e), t = e_bits(e);
+            ls.last = k ? e : ls.last;
             ls.cnt += k;
             ls.pm1 += t;
             acc <<= t;
-            if (ls.np >= 4) {
-                row[w++] = uint32_t(ls.pend);
-                ls.pend >>= 32;
-                ls.np -= 4;
+        }
+        ls.bad |= fl;
+        if (__any(fl & kEsc)) {
+            const uint64_t w = window(buf, ls.pm1);
+            const uint32_t e = tab[uint32_t(w >> 52)];
+            if ((e & kEsc) && ls.cnt < target) {
+                const uint32_t e2 = l2[min(256u * (1u + (e & 0xFFu)) + uint32_t((w >> 48) & 0xFFu),
+                                           uint32_t(E8HUF_LUT_MAX - 1))];
+                const uint32_t l = e2 & 31u;
+                row[ls.cnt - base] = uint8_t(e2 >> 8);
+                ls.last = (e2 >> 8) | (1u << 24);
+                ls.bad |= l ? 0u : kBadE;
+                ls.cnt += 1;
+                ls.pm1 += l ? l : 16u;
             }
         }
-    }
-    // a lane whose count ends inside this phase writes its last bytes
-    if (target < base + kPhase && ls.np) {
-        row[w] = uint32_t(ls.pend);
-        ls.pend = 0;
-        ls.np = 0;
     }
 }
 
@@ -334,9 +344,9 @@ __global__ __launch_bounds__(kThreads) void e8huf_decode_kernel(Args a) {
                 }
                 const uint32_t my_cnt = mine ? uint32_t(lane_cnt) : 0u;
                 // lanes outside the pass keep their windows at the buffer start
-                Lane ls = {mine ? uint32_t(lane_start - uint64_t(32 * j0) - 1) : 0u, 0u, 0ull, 0u, 0u, 0u};
+                Lane ls = {mine ? uint32_t(lane_start - uint64_t(32 * j0) - 1) : 0u, 0u, 0u, 0u};
                 const uint32_t pm1_0 = ls.pm1;
-                uint32_t* row = reinterpret_cast<uint32_t*>(stage + lane * kStageStride);
+                uint8_t* row = stage + lane * kStageStride;
 #pragma unroll 1
                 for (int ph = 0; ph < kPhases; ++ph) {
                     const uint32_t base = uint32_t(ph * kPhase);
@@ -382,10 +392,10 @@ __global__ __launch_bounds__(kThreads) void e8huf_decode_kernel(Args a) {
                 // the last lookup may have taken symbols past the lane's
                 // count; their bits are not the lane's
                 uint32_t used = ls.pm1 - pm1_0;
-                const uint32_t k = (ls.last >> 24) & 3u;
+                const uint32_t k = e_count(ls.last);
                 for (uint32_t j = 0; j < ls.cnt - min(ls.cnt, my_cnt) && j < k; ++j)
                     used -= lenof[(ls.last >> (8 * (k - 1 - j))) & 31u];
-                bad |= mine ? ls.bad : 0u;
+                bad |= mine ? (ls.bad & kBadE) : 0u;
                 end_bad |= bit(mine && used != lb);
                 l0 = l1;
             }

@@ -269,14 +269,24 @@ FP8_TRUNK_VALUES = TRUNK_LAYER_BYTES // 2
 
 def fp8_bytes(x: np.ndarray, fmt: str = "e4m3", amax: float | None = None) -> np.ndarray:
     """Scale x so that max |x| (or ``amax``) maps to the format's largest
-    finite value, round to FP8 and return the bytes (uint8)."""
+    finite value, round to FP8 and return the bytes (uint8). Large arrays are
+    handled in CHUNK-value pieces on several threads (the result does not
+    depend on the split)."""
     import torch
     x = np.asarray(x, dtype=np.float64)
-    m = float(np.abs(x).max()) if amax is None else float(amax)
-    scale = FP8_MAX[fmt] / m if m > 0 else 1.0
-    t = torch.from_numpy((x * scale).astype(np.float32))
     dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
-    return t.to(dt).view(torch.uint8).numpy().copy()
+    spans = [(p, min(p + CHUNK, x.size)) for p in range(0, x.size, CHUNK)]
+    with ThreadPoolExecutor(_workers()) as ex:
+        if amax is None:
+            amax = max(ex.map(lambda sp: float(np.abs(x[sp[0]:sp[1]]).max()), spans))
+        scale = FP8_MAX[fmt] / amax if amax > 0 else 1.0
+        out = np.empty(x.size, dtype=np.uint8)
+
+        def conv(sp):
+            t = torch.from_numpy((x[sp[0]:sp[1]] * scale).astype(np.float32))
+            out[sp[0]:sp[1]] = t.to(dt).view(torch.uint8).numpy()
+        list(ex.map(conv, spans))
+    return out
 
 
 def e8_tiny(seed: int = SEED_BASE + 101, fmt: str = "e4m3") -> np.ndarray:
