@@ -63,8 +63,12 @@ extern "C" {
 #define E8HUF_LANES (E8HUF_BLOCK_VALUES / E8HUF_LANE_VALUES)
 #define E8HUF_HDR_BYTES 128u
 #define E8HUF_BLOCK_REC_BYTES (8u + 2u * E8HUF_LANES)
-/* two-level table: level 1 (256 entries), then up to 32 level-2 tables */
-#define E8HUF_LUT_MAX (256 * 33)
+/* two-level table: level 1 (256 entries), then at most 17 level-2 tables:
+ * with codes assigned shortest first, the codes longer than 8 bits are the
+ * numerically last ones, so they cover one contiguous range of the 16-bit
+ * code space of at most 32 * 2^7 values, which spans at most 17 8-bit
+ * prefixes */
+#define E8HUF_LUT_MAX (256 * 18)
 
 /* device status bits, OR-ed into *d_status by the decode kernel */
 #define E8HUF_DEV_HEADER 1u    /* header does not match the call or the blob */
@@ -141,7 +145,7 @@ int64_t e8huf_encode(const void* h_x, uint64_t n, int exp_bits, void* h_out, uin
  * state between launches).
  * Returns K3HUF_OK once queued, K3HUF_E_ARG (null or misaligned pointers,
  * n_values 0 or above 2^40, blob_bytes below a header or at least 2^44,
- * lut_entries not 256 * (1 + t) for t in 0..32), K3HUF_E_HIP (launch failed).
+ * lut_entries not 256 * (1 + t) for t in 0..17), K3HUF_E_HIP (launch failed).
  */
 int e8huf_decode(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut, int lut_entries,
                  void* d_out, uint64_t n_values, void* stream, uint32_t* d_status);

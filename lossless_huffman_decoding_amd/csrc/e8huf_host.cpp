@@ -155,6 +155,9 @@ int e8huf_build_table(const uint8_t codelen[32], int exp_bits, uint16_t* lut, in
                 table_of[p] = tables++;
                 break;
             }
+    // at most 17 for any table accepted above (include/e8huf.h); kept as a
+    // check so that no table can write past E8HUF_LUT_MAX entries
+    if (256 * (1 + tables) > E8HUF_LUT_MAX) return K3HUF_E_ARG;
     for (int s = 0; s < kMaxSyms; ++s) {
         const int l = codelen[s];
         if (!l) continue;

@@ -10,7 +10,7 @@ import numpy as np
 
 from . import k3huf
 
-LUT_MAX = 256 * 33        # E8HUF_LUT_MAX
+LUT_MAX = 256 * 18        # E8HUF_LUT_MAX
 HDR_BYTES = 128
 DEV_HEADER, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 4, 8, 16
 EXPORTS = ("e8huf_build_table", "e8huf_layer_info", "e8huf_encode_bound", "e8huf_encode",

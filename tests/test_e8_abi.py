@@ -81,6 +81,23 @@ def test_build_table_golden_chain():
             assert all(int(lut[256 * (1 + t) + j]) == (sym << 8) | l for j in range(lo, hi + 1))
 
 
+def test_second_level_tables_stay_within_the_bound():
+    """Codes longer than 8 bits are the numerically last canonical codes, so
+    they span at most 17 8-bit prefixes (include/e8huf.h): over every
+    Kraft-valid mix of 32 codes of lengths 9, 10 and one longer length the
+    table never needs more than 17 second-level tables."""
+    most = 0
+    for c9 in range(33):
+        for c10 in range(33 - c9):
+            for L in range(11, 17):
+                lens = [9] * c9 + [10] * c10 + [L] * (32 - c9 - c10)
+                if sum(2.0 ** -l for l in lens) <= 1:
+                    rc, _, n = e8huf.build_table_rc(lens, 5)
+                    assert rc == 0
+                    most = max(most, n // 256 - 1)
+    assert 0 < most <= 17
+
+
 def test_build_table_rejections():
     assert e8huf.build_table_rc([0] * 32, 4)[0] == k3huf.E_EMPTY
     assert e8huf.build_table_rc([1, 1, 1], 4)[0] == k3huf.E_OVERSUB
@@ -152,6 +169,6 @@ def test_decode_rejects_bad_arguments_before_any_device_call():
     assert raw(blob, good, lut, 256, out, 0, None, None) == k3huf.E_ARG         # no values
     assert raw(blob, 127, lut, 256, out, 100, None, None) == k3huf.E_ARG        # shorter than a header
     assert raw(blob, good, lut, 300, out, 100, None, None) == k3huf.E_ARG       # table size
-    assert raw(blob, good, lut, 256 * 34, out, 100, None, None) == k3huf.E_ARG
+    assert raw(blob, good, lut, 256 * 19, out, 100, None, None) == k3huf.E_ARG
     assert raw(blob, 1 << 44, lut, 256, out, 100, None, None) == k3huf.E_ARG    # blob too large
     assert raw(blob, good, lut, 256, out, (1 << 40) + 1, None, None) == k3huf.E_ARG
