@@ -111,8 +111,9 @@ def test_layer_of_more_than_64_stripes():
     when a unit falls in the next block; the GPU encoder's look-back restarts
     in every stripe. The GPU encoder's container must equal the native
     packer's (which equals the oracle's byte for byte on every other layer
-    here; the oracle needs about two minutes for this size), and decoding it
-    must give the layer back."""
+    here; the oracle's encoder needs about two minutes for this size), its
+    code lengths, stripe bit counts and three of its stripes are checked
+    against the oracle, and decoding it must give the layer back."""
     n = (65 << 26) + 3 * 65536 + 1234
     x = synth.trunk_layer(synth.SEED_BASE + 77, n_bytes=n)
     want = k3huf.encode_layer(x)
@@ -126,6 +127,23 @@ def test_layer_of_more_than_64_stripes():
     d_dec, st = gpu_decode_dev(d_blob, x.size)
     assert st == 0
     assert torch.equal(d_dec, d_x)
+    # oracle checks of the GPU's container that stay within seconds: its
+    # code lengths are the oracle's for the layer's histogram, every stripe's
+    # bit count is the closed form sum(count * length), and the oracle's
+    # bit-by-bit decode of stripes 0, 64 and 65 gives the layer's bytes
+    blob = d_blob.cpu().numpy()
+    info = k3huf.layer_info(blob)
+    hist = np.bincount(x[1::2], minlength=256)
+    assert (info["codelen"] == O.code_lengths(hist)).all()
+    lens = info["codelen"].astype(np.int64)
+    for s in range(66):
+        off = int(np.frombuffer(bytes(blob[304 + 8 * s: 312 + 8 * s]), "<u8")[0])
+        n_bits = int(np.frombuffer(bytes(blob[off + 8: off + 12]), "<u4")[0])
+        hs = np.bincount(x[(s << 26) + 1: min(x.size, (s + 1) << 26): 2], minlength=256)
+        assert n_bits == int((hs * lens).sum()), s
+    for s in (0, 64, 65):
+        size = min(1 << 26, x.size - (s << 26))
+        assert (O.decode_stripes(blob, s, 1, size) == x[s << 26: (s << 26) + size]).all(), s
 
 
 def test_encode_reuses_buffers_across_calls():
