@@ -34,6 +34,20 @@ __host__ __device__ inline bool stripe_planes_ok(uint64_t blob_bytes, uint64_t s
            soff + even_off + ((uint64_t(n_syms) + 15) & ~15ull) <= blob_bytes;
 }
 
+// Whether subblock record j of the stripe record at soff lies inside the
+// blob, together with the next record's start_bit when has_next (the bytes a
+// decoder reads for the record: [rec, rec + 264), or [rec, rec + 268)). For a
+// stripe that stripe_planes_ok accepts, every record j < nsb passes: the
+// records end at or before bits_off, inside the blob. So a decoder may read
+// a record before it has the stripe's other values, sending a read this
+// test fails to the blob's first bytes instead.
+__host__ __device__ inline bool subblock_rec_in_blob(uint64_t blob_bytes, uint64_t soff, uint32_t j,
+                                                     bool has_next) {
+    return soff + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * j + K3HUF_SUBBLOCK_REC_BYTES +
+               (has_next ? 4u : 0u) <=
+           blob_bytes;
+}
+
 // Largest dword index, counted from the stripe's bitstream start and a
 // multiple of 4, at which a 16-byte read still ends inside the stripe's
 // padded even plane. For an accepted record with n_syms >= 1 it lies in

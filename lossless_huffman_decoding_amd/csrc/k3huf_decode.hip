@@ -393,9 +393,13 @@ __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uin
     uint32_t* row = reinterpret_cast<uint32_t*>(stage + lane * kStageStride);
 #pragma unroll 1
     for (int ph = 0; ph < kPhases; ++ph) {
+        // phases and groups past every lane's symbols are skipped (the
+        // wave's lanes agree on each test)
+        if (!__any(mine && ph * kPhase < lane_cnt)) break;
         if (mine) {
 #pragma unroll 1
             for (int g = 0; g < kGroups; ++g) {
+                if (!__any(ph * kPhase + g * 4 < lane_cnt)) break;
                 uint64_t acc = window(buf, pm1);
                 uint32_t ww = 0;
 #pragma unroll
@@ -485,21 +489,32 @@ __device__ __forceinline__ uint32_t stripe_subblocks(uint32_t n_syms) {
 // Branch-free: every lane issues its loads (a stripe that does not exist,
 // or whose offset fails the checks, reads the blob's first 32 bytes instead
 // and is then rejected), and every check is evaluated, so the loads of all
-// lanes go out together instead of one dependent round trip per check.
-__device__ __forceinline__ StripeLane load_stripes(const DecodeArgs& a, uint32_t blk, int lane) {
+// lanes go out together instead of one dependent round trip per check. In
+// two halves: the record offsets, then the records (a caller can issue
+// other loads that need only the offsets in between).
+struct StripeOff {
+    uint64_t so;   // the lane's stripe record offset, or 0 where it fails the checks
+    uint32_t in;   // 1 where it passes
+};
+__device__ __forceinline__ StripeOff stripe_offsets(const DecodeArgs& a, uint32_t blk, int lane) {
+    const uint32_t s = blk * 64u + uint32_t(lane);
+    const uint32_t sc = s < a.n_stripes ? s : 0u;
+    const uint64_t soff = ld64(a.blob + K3HUF_HDR_BYTES + 8ull * sc);
+    const uint32_t in = bit((soff & 15) == 0) & bit(soff + K3HUF_STRIPE_HDR_BYTES <= a.blob_bytes);
+    return {in ? soff : 0ull, in};
+}
+__device__ __forceinline__ StripeLane stripe_values(const DecodeArgs& a, uint32_t blk, int lane, StripeOff o) {
     const uint32_t s = blk * 64u + uint32_t(lane);
     const bool has = s < a.n_stripes;
     const uint32_t sc = has ? s : 0u;
-    const uint64_t soff = ld64(a.blob + K3HUF_HDR_BYTES + 8ull * sc);
     const uint64_t raw_s = stripe_raw(a, sc);
     const uint32_t n = uint32_t(raw_s / 2);
     const uint32_t nsb = stripe_subblocks(n);
-    const uint32_t in = bit((soff & 15) == 0) & bit(soff + K3HUF_STRIPE_HDR_BYTES <= a.blob_bytes);
-    const uint64_t so = in ? soff : 0ull;
+    const uint64_t so = o.so;
     const uint4 r0 = *reinterpret_cast<const uint4*>(a.blob + so);
     const uint4 r1 = *reinterpret_cast<const uint4*>(a.blob + so + 16);
     const uint32_t n_bits = r0.z, bit_bytes = r0.w, bits_off = r1.z, even_off = r1.w;
-    const uint32_t ok = bit(has) & in & bit(r0.x == uint32_t(raw_s)) & bit(r0.y == n) &
+    const uint32_t ok = bit(has) & o.in & bit(r0.x == uint32_t(raw_s)) & bit(r0.y == n) &
                         bit(r1.x == sc * kSubPerStripe) & bit(r1.y == nsb) &
                         bit(uint64_t(n_bits) <= uint64_t(K3HUF_MAXLEN) * n) &
                         bit(k3huf_bounds::stripe_planes_ok(a.blob_bytes, so, n, nsb, n_bits, bit_bytes,
@@ -510,6 +525,9 @@ __device__ __forceinline__ StripeLane load_stripes(const DecodeArgs& a, uint32_t
     t.even_off = ok ? even_off : 0u;
     t.n_bits = ok ? n_bits : kNoStripe;
     return t;
+}
+__device__ __forceinline__ StripeLane load_stripes(const DecodeArgs& a, uint32_t blk, int lane) {
+    return stripe_values(a, blk, lane, stripe_offsets(a, blk, lane));
 }
 
 // A subblock record as vector registers: lanes 0 and 1 hold start_bit and
@@ -536,17 +554,15 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     uint32_t* tab = reinterpret_cast<uint32_t*>(lds);  // at LDS address 0
 
     // layer header must describe exactly this call (uniform over the grid;
-    // every field is tested, so the loads go out together)
+    // every field is tested, so the loads go out together). The set-up below
+    // reads nothing whose place the header decides, so the test is taken
+    // after it and the header's loads travel with its first round trip.
     const uint8_t* b = a.blob;
     const uint32_t hdr_ok = bit(ld32(b) == 0x4648334Bu /* "K3HF" */) & bit(ld32(b + 4) == (1u | (12u << 16))) &
                             bit(ld32(b + 8) == K3HUF_STRIPE_BYTES) & bit(ld32(b + 12) == K3HUF_SUBBLOCK_BYTES) &
                             bit(ld32(b + 16) == K3HUF_LANE_SYMS) & bit(ld32(b + 20) == a.n_stripes) &
                             bit(ld64(b + 24) == a.out_bytes) & bit(ld32(b + 32) == a.n_sub) &
                             bit(ld64(b + 40) <= a.blob_bytes);
-    if (!hdr_ok) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, K3HUF_DEV_HEADER);
-        return;
-    }
 
     const int lane = threadIdx.x & 63;
     const uint32_t wave = uniform(threadIdx.x >> 6);
@@ -558,9 +574,10 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     auto unit_of = [&](uint32_t p) { return n_units - 1u - p; };   // p < n_units
     uint32_t h = wave * gridDim.x + blockIdx.x;                    // position of this wave's unit
 
-    // The set-up's loads go out in three round trips: the table's first
-    // words with the stripe offsets, then the stripe records, then the first
-    // unit's record with the table's second words.
+    // The set-up's loads go out in two round trips: the header, the table's
+    // first words and the stripe offsets; then the stripe records, the
+    // table's second words and the first unit's record (its address needs
+    // only its stripe's offset).
     constexpr int kPerThread = (K3HUF_LUT_ENTRIES + kThreads - 1) / kThreads;
     uint32_t ta[kPerThread], tb[kPerThread];
 #pragma unroll
@@ -570,9 +587,24 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     }
     // stripe values of the block holding this wave's first unit
     uint32_t blk = h < n_units ? unit_of(h) / (kUnitsPerSub * kSubPerStripe * 64u) : 0u;
-    StripeLane sl = load_stripes(a, blk, lane);
+    const StripeOff so0 = stripe_offsets(a, blk, lane);
     uint32_t pf_h = 0xFFFFFFFFu;   // position whose unit's record `pf` holds
     RecLanes pf = {0u, 0u, 0u};
+    if (h < n_units) {
+        // a record outside the blob is read from the blob's start instead;
+        // the records of a stripe that passes its checks lie inside, so the
+        // record is the right one whenever the unit is decoded
+        const uint32_t kn = unit_of(h) / kUnitsPerSub;
+        const uint32_t sn = kn / kSubPerStripe, jn = kn % kSubPerStripe;
+        const uint64_t son = uint64_t(lane_value(uint32_t(so0.so >> 4), sn & 63u)) << 4;
+        const bool nx = jn + 1 < stripe_subblocks(uint32_t(stripe_raw(a, sn) / 2));
+        const uint64_t ro = k3huf_bounds::subblock_rec_in_blob(a.blob_bytes, son, jn, nx)
+                                ? son + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jn
+                                : 0ull;
+        pf = load_rec(b + ro, nx, lane);
+        pf_h = h;
+    }
+    StripeLane sl = stripe_values(a, blk, lane, so0);
     // request the record of position p's unit (when its stripe is in `sl`)
     auto request_rec = [&](uint32_t p) {
         pf_h = 0xFFFFFFFFu;
@@ -587,7 +619,6 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
             }
         }
     };
-    request_rec(h);
     if (threadIdx.x == 0) local_ticket = 0u;
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
@@ -601,6 +632,10 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         if (i < K3HUF_LUT_ENTRIES) tab[i] = make_entry(ta[q], tb[q]);
     }
     __syncthreads();
+    if (!hdr_ok) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, K3HUF_DEV_HEADER);
+        return;
+    }
 
     uint8_t* wl = lds + kTabBytes + wave * kWaveLds;
     uint32_t* buf = reinterpret_cast<uint32_t*>(wl);

@@ -9,7 +9,12 @@
 //      and planes, so inside [0, blob_bytes);
 //   2. every dword that holds one of the stripe's n_bits code bits is read
 //      unclamped, so a valid stripe decodes from its true bytes;
-//   3. dmax is in [0, 2^31).
+//   3. dmax is in [0, 2^31);
+//   4. every subblock record j < nsb, read with or without the next record's
+//      start_bit (as the kernel does when j + 1 < nsb), passes
+//      subblock_rec_in_blob, so a record read before the stripe's values are
+//      known is the right one whenever the stripe is accepted; and a record
+//      that passes ends inside the blob.
 // Prints "ok <records checked>" or the first failing record and exits 1.
 #define __host__
 #define __device__
@@ -67,6 +72,15 @@ static int check(uint64_t blob, uint64_t soff, uint32_t n, uint32_t n_bits, uint
                 return fail("8-byte read", blob, soff, n, n_bits, bit_bytes, bits_off, even_off, j);
         }
     }
+    // 4: the stripe's subblock records (first, last and a few between)
+    const uint32_t jr[] = {0u, nsb - 1, nsb / 2, uint32_t(below(nsb))};
+    for (uint32_t j : jr) {
+        const bool nx = j + 1 < nsb;
+        if (!subblock_rec_in_blob(blob, soff, j, nx))
+            return fail("record outside", blob, soff, n, n_bits, bit_bytes, bits_off, even_off, j);
+        if (soff + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * (j + 1) + (nx ? 4 : 0) > blob)
+            return fail("record end", blob, soff, n, n_bits, bit_bytes, bits_off, even_off, j);
+    }
     // 2: the dwords holding code bits are read where they are
     if (n_bits) {
         const int32_t last = int32_t((uint64_t(n_bits) - 1) >> 5);
@@ -119,6 +133,19 @@ int main() {
                                                    : below(1ull << 32) & ~15ull);
         const uint64_t soff = (t & 4) ? below(blob) & ~15ull : (blob - (blob >> (1 + t % 30))) & ~15ull;
         if (check(blob, soff, n, n_bits, bit_bytes, bits_off, even_off, &accepted)) return 1;
+    }
+    // a record that passes subblock_rec_in_blob ends inside the blob, for
+    // any offset and index the kernel can form (offsets below 2^36, j < 1024)
+    for (long t = 0; t < 4000000; ++t) {
+        const uint64_t blob = 304 + below(kMaxBlob - 303);
+        const uint64_t back = below(blob < (1ull << 20) ? blob : (1ull << 20));
+        const uint64_t soff = (t & 1) ? below(blob) & ~15ull : (blob - back) & ~15ull;
+        const uint32_t j = uint32_t(below(1024));
+        const bool nx = (t & 2) != 0;
+        const uint64_t end = soff + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * j +
+                             K3HUF_SUBBLOCK_REC_BYTES + (nx ? 4 : 0);
+        if (subblock_rec_in_blob(blob, soff, j, nx) != (end <= blob))
+            return fail("record test", blob, soff, 0, 0, 0, 0, 0, j);
     }
     std::printf("ok %ld\n", accepted);
     return accepted > 100000 ? 0 : 1;
