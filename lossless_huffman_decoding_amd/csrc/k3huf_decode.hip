@@ -255,30 +255,44 @@ static_assert(64 * kSlotDw * 4 <= kBufBytes, "gather slots fit the buffer");
 // or lands past the phase). A lane that has its 64 symbols takes zero entries
 // (no bits, no symbols) until the wave's slowest lane is done. A lookup that
 // ends one symbol past the phase leaves that symbol at row offset 64; it is
-// moved to offset 0 when the next phase starts.
+// moved to offset 0 when the next phase starts. A wave's LDS operations run
+// in order, so each lookup's writes are issued after the next lookup's table
+// read, which then waits for no write; the lane mask enters through the
+// field width of the length extraction (zero for a finished lane), so the
+// dependent chain from one table read to the next is four ALU operations
+// (measured on one wave per CU: 4% less time per unit).
 __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint32_t* buf, uint8_t* row,
                                              int ph, LaneState& ls) {
     const uint32_t base = uint32_t(ph * kPhase), target = base + kPhase;
     if (ls.cnt > base) row[0] = uint8_t(ls.last >> 16);   // carried symbol
+    // each lookup's two bytes are written after the next table read has been
+    // issued, so that read does not queue behind them; the first pending
+    // write is a dummy past the phase
+    uint8_t* wp = row + kPhase + 2;
+    uint32_t we = 0;
 #pragma unroll 1
     for (int w = 0; w < kMaxWindows; ++w) {
         if (!__any(ls.cnt < target)) break;
         uint64_t acc = window(buf, ls.pm1);
 #pragma unroll
         for (int i = 0; i < kLookups; ++i) {
-            uint32_t e = peek(tab, acc);
-            e = ls.cnt < target ? e : 0u;
-            const uint32_t t = ent_bits(e);
-            uint8_t* p = row + (ls.cnt - base);
-            p[0] = uint8_t(e);
-            p[1] = uint8_t(e >> 16);
-            ls.last = e ? e : ls.last;
-            ls.bad |= e;
-            ls.cnt += ent_syms(e);
+            const uint32_t e = peek(tab, acc);
+            wp[0] = uint8_t(we);
+            wp[1] = uint8_t(we >> 16);
+            const bool live = ls.cnt < target;
+            const uint32_t t = __builtin_amdgcn_ubfe(e, 8u, live ? 4u : 0u);
+            const uint32_t ez = live ? e : 0u;
+            wp = row + (ls.cnt - base);
+            we = ez;
+            ls.last = ez ? ez : ls.last;
+            ls.bad |= ez;
+            ls.cnt += ent_syms(ez);
             ls.pm1 += t;
             acc <<= t;
         }
     }
+    wp[0] = uint8_t(we);
+    wp[1] = uint8_t(we >> 16);
 }
 
 // One super-phase (kSuper phases from sp) of a full unit (64 chunks of 256
