@@ -307,6 +307,22 @@ int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_ou
 int64_t k3huf_encode_layer_dev_static(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
                                       void* stream);
 
+/*
+ * k3huf_stream_ref -- measurement reference, not a decode step: a plain
+ * streaming kernel that reads in_bytes from d_in and writes out_bytes to
+ * d_out in 16-byte units (output unit u = input unit u while the input
+ * lasts, then {u mod 2^32, 0, 0, 0}; input units past the output are only
+ * read). Given a decode launch's container and output sizes it moves the same
+ * HBM bytes with nothing in between, so a benchmark can report the rate a
+ * simple kernel reaches for that traffic beside the decode's own.
+ * d_in (nullable when in_bytes is 0), d_out: device, 16-byte aligned; both
+ * sizes multiples of 16, out_bytes > 0. grid: workgroups of 256 threads,
+ * 1..2^20. nontemporal != 0 streams the stores past the caches. Queued on
+ * `stream`; returns K3HUF_OK, K3HUF_E_ARG or K3HUF_E_HIP.
+ */
+int k3huf_stream_ref(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_bytes, int grid,
+                     int nontemporal, void* stream);
+
 /* Static text for a return code. */
 const char* k3huf_strerror(int code);
 

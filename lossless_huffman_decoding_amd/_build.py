@@ -40,7 +40,7 @@ def build(verbose: bool = False) -> str:
     bdir = os.path.join(OUT_DIR, "_obj")
     os.makedirs(bdir, exist_ok=True)
     objs = []
-    for name in ("k3huf_decode", "k3huf_encode", "e8huf_decode"):
+    for name in ("k3huf_decode", "k3huf_encode", "e8huf_decode", "k3huf_stream"):
         o = os.path.join(bdir, name + ".o")
         _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
         objs.append(o)

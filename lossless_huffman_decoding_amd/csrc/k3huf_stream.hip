@@ -1,0 +1,50 @@
+// A plain streaming kernel, kept as the measured bandwidth reference of the
+// decode kernels: it reads and writes the byte counts a decode launch moves
+// (its container and its output) with nothing in between, so the HBM rate it
+// reaches is what a simple kernel gets for that traffic on the device at
+// hand. Not part of any decode path. Declared in include/k3huf.h.
+#include <hip/hip_runtime.h>
+
+#include "k3huf.h"
+
+namespace {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte unit u of the output is unit u of the input while the input lasts,
+// then {u mod 2^32, 0, 0, 0}; input units past the output are read and
+// folded into one word, written to output unit 0 only when it equals a
+// value the caller never sees in practice, so the reads are kept.
+__global__ __launch_bounds__(256) void stream_kernel(const v4u* __restrict__ in, uint64_t n_in,
+                                                     v4u* __restrict__ out, uint64_t n_out, int nontemporal) {
+    const uint64_t stride = uint64_t(gridDim.x) * blockDim.x;
+    const uint64_t n = n_in > n_out ? n_in : n_out;
+    uint32_t fold = 0;
+    for (uint64_t u = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < n; u += stride) {
+        v4u v = {uint32_t(u), 0u, 0u, 0u};
+        if (u < n_in) v = in[u];
+        if (u < n_out) {
+            if (nontemporal)
+                __builtin_nontemporal_store(v, out + u);
+            else
+                out[u] = v;
+        } else {
+            fold ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+    }
+    if (n_out != 0 && fold == 0x6B334846u && n_in > n_out) out[0] = v4u{fold, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+extern "C" int k3huf_stream_ref(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_bytes, int grid,
+                                int nontemporal, void* stream) {
+    if ((in_bytes && !d_in) || !d_out || out_bytes == 0 || (in_bytes & 15) || (out_bytes & 15) ||
+        (reinterpret_cast<uintptr_t>(d_in) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15) || grid < 1 ||
+        grid > (1 << 20))
+        return K3HUF_E_ARG;
+    hipLaunchKernelGGL(stream_kernel, dim3(unsigned(grid)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const v4u*>(d_in), in_bytes / 16, static_cast<v4u*>(d_out), out_bytes / 16,
+                       nontemporal);
+    return hipGetLastError() == hipSuccess ? K3HUF_OK : K3HUF_E_HIP;
+}

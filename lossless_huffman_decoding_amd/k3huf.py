@@ -25,7 +25,7 @@ DEV_HEADER, DEV_STRIPE, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 2, 4, 8, 16
 EXPORTS = ("k3huf_build_table", "k3huf_layer_info", "k3huf_decode_layer", "k3huf_decode_ring",
            "k3huf_decode_ring_host", "k3huf_encode_bound", "k3huf_encode_layer",
            "k3huf_encode_work_bytes", "k3huf_encode_layer_dev", "k3huf_encode_layer_dev_static",
-           "k3huf_strerror")
+           "k3huf_stream_ref", "k3huf_strerror")
 STATIC_MAX_RAW = 1 << 32   # K3HUF_STATIC_MAX_RAW
 
 
@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.k3huf_encode_layer_dev.restype = ctypes.c_int64
         L.k3huf_encode_layer_dev_static.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp]
         L.k3huf_encode_layer_dev_static.restype = ctypes.c_int64
+        L.k3huf_stream_ref.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                       vp]
+        L.k3huf_stream_ref.restype = ctypes.c_int
         L.k3huf_strerror.argtypes = [ctypes.c_int]
         L.k3huf_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -219,6 +222,15 @@ def decode_layer_raw(blob_ptr: int, blob_bytes: int, lut_ptr: int, out_ptr: int,
     """Unchecked pointer-level call; returns the C return code."""
     return lib().k3huf_decode_layer(blob_ptr, blob_bytes, lut_ptr, out_ptr, out_bytes, stream,
                                     status_ptr)
+
+
+def stream_ref(d_in, d_out, grid: int, nontemporal: bool = False, stream=None) -> None:
+    """Queue the streaming reference kernel (k3huf_stream_ref): read all of
+    ``d_in`` (uint8 tensor, or None), write all of ``d_out``."""
+    _check(lib().k3huf_stream_ref(d_in.data_ptr() if d_in is not None else None,
+                                  _nbytes(d_in) if d_in is not None else 0, d_out.data_ptr(), _nbytes(d_out),
+                                  int(grid), int(bool(nontemporal)), _stream_handle(stream)),
+           "k3huf_stream_ref")
 
 
 def decode_ring(layers, slots, streams, cb=None, d_status=None) -> None:

@@ -253,3 +253,19 @@ def test_packer_fuzz_matches_oracle():
         b = k3huf.encode_layer(x)
         assert a.size == b.size and (a == b).all(), (seed, what)
         assert O.check_index(b) == O.OK, (seed, what)
+
+
+def test_stream_ref_rejects_bad_arguments_before_any_device_call():
+    """The bandwidth reference kernel's launcher checks its arguments first:
+    these calls return K3HUF_E_ARG without touching a device."""
+    L = k3huf.lib()
+    good = 1 << 12   # a 4 KiB-aligned fake address; never dereferenced here
+    assert L.k3huf_stream_ref(good, 16, None, 16, 1, 0, None) == k3huf.E_ARG        # no output
+    assert L.k3huf_stream_ref(None, 16, good, 16, 1, 0, None) == k3huf.E_ARG        # input bytes, no input
+    assert L.k3huf_stream_ref(good, 16, good, 0, 1, 0, None) == k3huf.E_ARG         # empty output
+    assert L.k3huf_stream_ref(good, 24, good, 16, 1, 0, None) == k3huf.E_ARG        # not whole units
+    assert L.k3huf_stream_ref(good, 16, good, 40, 1, 0, None) == k3huf.E_ARG
+    assert L.k3huf_stream_ref(good + 8, 16, good, 16, 1, 0, None) == k3huf.E_ARG    # misaligned
+    assert L.k3huf_stream_ref(good, 16, good + 4, 16, 1, 0, None) == k3huf.E_ARG
+    assert L.k3huf_stream_ref(good, 16, good, 16, 0, 0, None) == k3huf.E_ARG        # grid
+    assert L.k3huf_stream_ref(good, 16, good, 16, (1 << 20) + 1, 0, None) == k3huf.E_ARG
