@@ -68,7 +68,6 @@ static_assert(kLdsStatic + 16 + E8HUF_LUT_MAX * 2 <= 163840, "LDS budget, with t
 constexpr uint32_t kEsc = 1u << 31;
 constexpr uint32_t kBadE = 1u << 30;
 __device__ __forceinline__ uint32_t e_count(uint32_t e) { return (e >> 24) & 3u; }
-__device__ __forceinline__ uint32_t e_bits(uint32_t e) { return (e >> 26) & 15u; }
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -174,6 +173,12 @@ __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint16_t
         row[0] = uint8_t(ls.last >> (8 * (k - j)));
         row[1] = uint8_t(ls.last >> (8 * (k - j + 1)));
     }
+    // each lookup's three bytes are written after the next table read has
+    // been issued (a wave's LDS operations complete in order, so that read
+    // waits for no write); the first pending write is a dummy in the spare
+    // bytes, and the pending write goes out before an escape's own byte
+    uint8_t* wp = row + kSpare;
+    uint32_t we = 0;
 #pragma unroll 1
     for (int win = 0; win < 2 * kPhase; ++win) {
         if (!__any(ls.cnt < target)) break;
@@ -181,22 +186,32 @@ __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint16_t
         uint32_t fl = 0;
 #pragma unroll
         for (int q = 0; q < kLookups; ++q) {
-            uint32_t e = tab[uint32_t(acc >> 52)];
-            e = ls.cnt < target ? e : 0u;
-            fl |= e;
+            const uint32_t e = tab[uint32_t(acc >> 52)];
+            wp[0] = uint8_t(we);
+            wp[1] = uint8_t(we >> 8);
+            wp[2] = uint8_t(we >> 16);
+            // a lane that has its symbols takes a zero entry: its field
+            // widths are zero, so the mask stays off the chain of reads
+            const bool live = ls.cnt < target;
+            const uint32_t t = __builtin_amdgcn_ubfe(e, 26u, live ? 4u : 0u);
+            const uint32_t ez = live ? e : 0u;
+            fl |= ez;
             // lanes past the phase (or before it) write to the row's spare bytes
-            uint8_t* p = row + min(ls.cnt - base, kSpare);
-            p[0] = uint8_t(e);
-            p[1] = uint8_t(e >> 8);
-            p[2] = uint8_t(e >> 16);
-            const uint32_t k = e_count(e), t = e_bits(e);
-            ls.last = k ? e : ls.last;
+            wp = row + min(ls.cnt - base, kSpare);
+            we = ez;
+            const uint32_t k = e_count(ez);
+            ls.last = k ? ez : ls.last;
             ls.cnt += k;
             ls.pm1 += t;
             acc <<= t;
         }
         ls.bad |= fl;
         if (__any(fl & kEsc)) {
+            wp[0] = uint8_t(we);
+            wp[1] = uint8_t(we >> 8);
+            wp[2] = uint8_t(we >> 16);
+            wp = row + kSpare;
+            we = 0;
             const uint64_t w = window(buf, ls.pm1);
             const uint32_t e = tab[uint32_t(w >> 52)];
             if ((e & kEsc) && ls.cnt < target) {
@@ -210,6 +225,9 @@ __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint16_t
             }
         }
     }
+    wp[0] = uint8_t(we);
+    wp[1] = uint8_t(we >> 8);
+    wp[2] = uint8_t(we >> 16);
 }
 
 // the 16 staged exponents of chunk c at phase offset 16 part (rows are 4-byte
