@@ -48,13 +48,15 @@
  *
  * Container layout (all little-endian), restated from the format description:
  *   layer header, 304 bytes: magic "K3HF", u16 version 1, u16 maxlen 12,
- *     u32 stripe_bytes 2^26, u32 subblock_bytes 2^16, u32 lane_syms 256,
+ *     u32 stripe_bytes 2^26, u32 subblock_bytes = 256 * lane_syms,
+ *     u32 lane_syms (256, or 64 for the short-chunk layout of small layers),
  *     u32 n_stripes, u64 raw_bytes, u32 n_subblocks, u32 0, u64 container_bytes,
  *     u8 codelen[256]; then u64 stripe_off[n_stripes]; zero pad to 256.
  *   stripe record at stripe_off[s] (256-aligned): u32 raw_bytes, u32 n_syms,
  *     u32 n_bits, u32 bit_bytes, u32 first_subblock, u32 n_subblocks,
  *     u32 bits_off, u32 even_off; then n_subblocks records of 264 bytes
- *     {u32 start_bit, u32 n_syms, u16 lane_bits[128]}; zero pad to 256; the
+ *     {u32 start_bit, u32 n_syms, u16 lane_bits[128]} (a subblock holds 128
+ *     lane chunks of lane_syms symbols); zero pad to 256; the
  *     bitstream (bit_bytes = ceil(n_bits/8) rounded up to 16, zero padded) at
  *     bits_off; zero pad to 256; the even plane (n_syms bytes, zero padded to
  *     256) at even_off. bits_off and even_off count from the stripe record's
@@ -68,10 +70,7 @@
 
 #define OH_MAXLEN 12
 #define OH_STRIPE (1u << 26)
-#define OH_SUBBLOCK (1u << 16)
-#define OH_SB_SYMS (OH_SUBBLOCK / 2)
-#define OH_LANE_SYMS 256u
-#define OH_LANES (OH_SB_SYMS / OH_LANE_SYMS)
+#define OH_LANES 128u              /* lane chunks per subblock */
 #define OH_HDR 304u
 #define OH_STRIPE_HDR 32u
 #define OH_REC (8u + 2u * OH_LANES)
@@ -301,19 +300,25 @@ int oh_decode_prefix(const uint8_t len[256], uint32_t bits12, int *sym, int *cle
 
 static uint32_t n_stripes_of(uint64_t raw) { return (uint32_t)((raw + OH_STRIPE - 1) / OH_STRIPE); }
 
+/* the two lane-chunk lengths the format allows, and the subblock they make */
+static int lane_syms_ok(uint32_t lane) { return lane == 256u || lane == 64u; }
+static uint32_t sb_syms_of(uint32_t lane) { return OH_LANES * lane; }
+
 /* Upper bound on the container size for raw_bytes of layer data (worst case:
- * every code 12 bits long). */
-int64_t oh_encode_bound(uint64_t raw) {
+ * every code 12 bits long), for lane chunks of `lane` symbols. */
+int64_t oh_encode_bound_lanes(uint64_t raw, uint32_t lane) {
+    if (!lane_syms_ok(lane)) return OH_E_ARG;
     uint64_t ns = n_stripes_of(raw);
     uint64_t b = up256(OH_HDR + 8 * ns);
     for (uint64_t s = 0; s < ns; s++) {
         uint64_t rb = raw - s * OH_STRIPE;
         if (rb > OH_STRIPE) rb = OH_STRIPE;
-        uint64_t n = rb / 2, nsb = (n + OH_SB_SYMS - 1) / OH_SB_SYMS;
+        uint64_t n = rb / 2, nsb = (n + sb_syms_of(lane) - 1) / sb_syms_of(lane);
         b += up256(OH_STRIPE_HDR + OH_REC * nsb) + up256(up16((n * OH_MAXLEN + 7) / 8)) + up256(n);
     }
     return (int64_t)b;
 }
+int64_t oh_encode_bound(uint64_t raw) { return oh_encode_bound_lanes(raw, 256u); }
 
 static void put_bits(uint8_t *buf, uint64_t *pos, uint32_t code, int l) {
     for (int b = l - 1; b >= 0; b--) {
@@ -325,10 +330,12 @@ static void put_bits(uint8_t *buf, uint64_t *pos, uint32_t code, int l) {
 /* Encoder (K3 page, "what was implemented" and "key design points"): one
  * histogram and one codelen[256] over the whole layer's odd bytes; per 64 MiB
  * stripe the odd-byte codes MSB-first, then the even bytes raw; plus the
- * subblock/lane index. Returns the container size, or a negative error. */
-int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64_t cap) {
-    if (!raw || !out || n_raw == 0 || (n_raw & 1)) return OH_E_ARG;
-    if ((uint64_t)oh_encode_bound(n_raw) > cap) return OH_E_ARG;
+ * subblock/lane index with lane chunks of `lane` symbols (256, or 64).
+ * Returns the container size, or a negative error. */
+int64_t oh_encode_layer_lanes(const uint8_t *raw, uint64_t n_raw, uint32_t lane, uint8_t *out, uint64_t cap) {
+    if (!raw || !out || n_raw == 0 || (n_raw & 1) || !lane_syms_ok(lane)) return OH_E_ARG;
+    if ((uint64_t)oh_encode_bound_lanes(n_raw, lane) > cap) return OH_E_ARG;
+    const uint32_t sb_syms = sb_syms_of(lane);
     uint64_t count[256] = {0};
     for (uint64_t i = 1; i < n_raw; i += 2) count[raw[i]]++;
     uint8_t len[256];
@@ -346,7 +353,7 @@ int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64
         uint64_t rb = n_raw - base;
         if (rb > OH_STRIPE) rb = OH_STRIPE;
         uint32_t n = (uint32_t)(rb / 2);
-        uint32_t nsb = (n + OH_SB_SYMS - 1) / OH_SB_SYMS;
+        uint32_t nsb = (n + sb_syms - 1) / sb_syms;
         uint8_t *st = out + o;
         wr_le(out + OH_HDR + 8ull * s, o, 8);
         uint64_t bits_off = up256(OH_STRIPE_HDR + (uint64_t)OH_REC * nsb);
@@ -354,25 +361,25 @@ int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64
         uint64_t pos = 0;
         uint64_t lane_start = 0;
         for (uint32_t i = 0; i < n; i++) {
-            if (i % OH_LANE_SYMS == 0) {
+            if (i % lane == 0) {
                 if (i > 0) {
-                    uint32_t pl = (i - 1) / OH_LANE_SYMS; /* previous lane, global in stripe */
+                    uint32_t pl = (i - 1) / lane; /* previous lane, global in stripe */
                     uint8_t *rec = st + OH_STRIPE_HDR + (uint64_t)OH_REC * (pl / OH_LANES);
                     wr_le(rec + 8 + 2 * (pl % OH_LANES), pos - lane_start, 2);
                 }
                 lane_start = pos;
             }
-            if (i % OH_SB_SYMS == 0) {
-                uint8_t *rec = st + OH_STRIPE_HDR + (uint64_t)OH_REC * (i / OH_SB_SYMS);
+            if (i % sb_syms == 0) {
+                uint8_t *rec = st + OH_STRIPE_HDR + (uint64_t)OH_REC * (i / sb_syms);
                 uint32_t left = n - i;
                 wr_le(rec, pos, 4);
-                wr_le(rec + 4, left < OH_SB_SYMS ? left : OH_SB_SYMS, 4);
+                wr_le(rec + 4, left < sb_syms ? left : sb_syms, 4);
             }
             uint8_t sym = raw[base + 2ull * i + 1];
             put_bits(bits, &pos, code[sym], len[sym]);
         }
         {
-            uint32_t pl = (n - 1) / OH_LANE_SYMS;
+            uint32_t pl = (n - 1) / lane;
             uint8_t *rec = st + OH_STRIPE_HDR + (uint64_t)OH_REC * (pl / OH_LANES);
             wr_le(rec + 8 + 2 * (pl % OH_LANES), pos - lane_start, 2);
         }
@@ -394,8 +401,8 @@ int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64
     wr_le(out + 4, 1, 2);
     wr_le(out + 6, OH_MAXLEN, 2);
     wr_le(out + 8, OH_STRIPE, 4);
-    wr_le(out + 12, OH_SUBBLOCK, 4);
-    wr_le(out + 16, OH_LANE_SYMS, 4);
+    wr_le(out + 12, 2ull * sb_syms, 4);
+    wr_le(out + 16, lane, 4);
     wr_le(out + 20, ns, 4);
     wr_le(out + 24, n_raw, 8);
     wr_le(out + 32, sb_total, 4);
@@ -404,13 +411,16 @@ int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64
     memcpy(out + 48, len, 256);
     return (int64_t)o;
 }
+int64_t oh_encode_layer(const uint8_t *raw, uint64_t n_raw, uint8_t *out, uint64_t cap) {
+    return oh_encode_layer_lanes(raw, n_raw, 256u, out, cap);
+}
 
 /* ------------------------------------------------------------------------- */
 /* decoder                                                                     */
 
 typedef struct {
     uint64_t raw;
-    uint32_t ns, nsb;
+    uint32_t ns, nsb, lane;
     const uint8_t *len;
 } oh_layer_t;
 
@@ -418,8 +428,9 @@ static int parse_layer(const uint8_t *blob, uint64_t nb, oh_layer_t *L) {
     if (!blob || nb < OH_HDR) return OH_E_FORMAT;
     if (memcmp(blob, "K3HF", 4) != 0) return OH_E_FORMAT;
     if (rd_le(blob + 4, 2) != 1 || rd_le(blob + 6, 2) != OH_MAXLEN) return OH_E_FORMAT;
-    if (rd_le(blob + 8, 4) != OH_STRIPE || rd_le(blob + 12, 4) != OH_SUBBLOCK ||
-        rd_le(blob + 16, 4) != OH_LANE_SYMS) return OH_E_FORMAT;
+    L->lane = (uint32_t)rd_le(blob + 16, 4);
+    if (rd_le(blob + 8, 4) != OH_STRIPE || !lane_syms_ok(L->lane) ||
+        rd_le(blob + 12, 4) != 2ull * sb_syms_of(L->lane)) return OH_E_FORMAT;
     L->ns = (uint32_t)rd_le(blob + 20, 4);
     L->raw = rd_le(blob + 24, 8);
     L->nsb = (uint32_t)rd_le(blob + 32, 4);
@@ -449,7 +460,7 @@ static int parse_stripe(const uint8_t *blob, uint64_t nb, const oh_layer_t *L, u
     S->first_sb = (uint32_t)rd_le(st + 16, 4);
     S->nsb = (uint32_t)rd_le(st + 20, 4);
     uint64_t bits_off = rd_le(st + 24, 4), even_off = rd_le(st + 28, 4);
-    if (S->nsb != (S->n + OH_SB_SYMS - 1) / OH_SB_SYMS) return OH_E_FORMAT;
+    if (S->nsb != (S->n + sb_syms_of(L->lane) - 1) / sb_syms_of(L->lane)) return OH_E_FORMAT;
     if (bits_off < OH_STRIPE_HDR + (uint64_t)OH_REC * S->nsb) return OH_E_FORMAT;
     if ((uint64_t)S->n_bits > 8ull * S->bit_bytes) return OH_E_FORMAT;
     if (even_off < bits_off + S->bit_bytes) return OH_E_FORMAT;
@@ -521,12 +532,13 @@ int oh_check_index(const uint8_t *blob, uint64_t nb) {
         uint64_t pos = 0;
         for (uint32_t b = 0; b < S.nsb; b++) {
             const uint8_t *rec = S.recs + (uint64_t)OH_REC * b;
-            uint32_t i0 = b * OH_SB_SYMS;
-            uint32_t m = S.n - i0 < OH_SB_SYMS ? S.n - i0 : OH_SB_SYMS;
+            const uint32_t sb_syms = sb_syms_of(L.lane);
+            uint32_t i0 = b * sb_syms;
+            uint32_t m = S.n - i0 < sb_syms ? S.n - i0 : sb_syms;
             if (rd_le(rec, 4) != pos || rd_le(rec + 4, 4) != m) return OH_E_INDEX;
             for (uint32_t t = 0; t < OH_LANES; t++) {
                 uint64_t p0 = pos;
-                for (uint32_t k = 0; k < OH_LANE_SYMS && t * OH_LANE_SYMS + k < m; k++)
+                for (uint32_t k = 0; k < L.lane && t * L.lane + k < m; k++)
                     if (dec_one(&d, S.bits, S.n_bits, &pos) < 0) return OH_E_CORRUPT;
                 if (rd_le(rec + 8 + 2 * t, 2) != pos - p0) return OH_E_INDEX;
             }

@@ -59,6 +59,11 @@ def lib():
         L.oh_decode_prefix.restype = ctypes.c_int
         L.oh_encode_bound.argtypes = [ctypes.c_uint64]
         L.oh_encode_bound.restype = ctypes.c_int64
+        L.oh_encode_bound_lanes.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+        L.oh_encode_bound_lanes.restype = ctypes.c_int64
+        L.oh_encode_layer_lanes.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p,
+                                            ctypes.c_uint64]
+        L.oh_encode_layer_lanes.restype = ctypes.c_int64
         L.oh_encode_layer.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                       ctypes.c_uint64]
         L.oh_encode_layer.restype = ctypes.c_int64
@@ -155,16 +160,20 @@ def decode_prefix(lengths, bits12: int):
     return s.value, l.value
 
 
-def encode_bound(raw_bytes: int) -> int:
-    return lib().oh_encode_bound(raw_bytes)
+def encode_bound(raw_bytes: int, lane_syms: int = 256) -> int:
+    n = lib().oh_encode_bound_lanes(raw_bytes, lane_syms)
+    if n < 0:
+        raise ValueError("oracle encode bound: lane_syms %d" % lane_syms)
+    return n
 
 
-def encode_layer(raw) -> np.ndarray:
-    """Container bytes (uint8 array) for one layer of bf16 bytes."""
+def encode_layer(raw, lane_syms: int = 256) -> np.ndarray:
+    """Container bytes (uint8 array) for one layer of bf16 bytes, with lane
+    chunks of lane_syms symbols (256, or 64)."""
     r = _u8(raw)
-    cap = encode_bound(r.size)
+    cap = encode_bound(r.size, lane_syms)
     out = np.empty(cap, np.uint8)
-    n = lib().oh_encode_layer(r.ctypes.data, r.size, out.ctypes.data, cap)
+    n = lib().oh_encode_layer_lanes(r.ctypes.data, r.size, lane_syms, out.ctypes.data, cap)
     if n < 0:
         raise ValueError("oracle encode failed: %d" % n)
     return out[:n]

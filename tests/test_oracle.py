@@ -301,14 +301,46 @@ def test_four_value_layer_golden():
     assert (O.decode_layer(blob) == raw).all()
 
 
+def test_short_lane_chunk_layer_golden():
+    g = {}
+    for line in open(os.path.join(GOLD, "lane64_layer.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            g[k] = v
+    n = int(g["values"][0])
+    raw = np.empty(2 * n, np.uint8)
+    raw[0::2] = np.arange(n, dtype=np.uint8)
+    raw[1::2] = [int(v, 16) for v in g["high"]]
+    blob = O.encode_layer(raw, 64)
+    h = hdr(blob)
+    assert h["sub"] == int(g["subblock_bytes"][0]) and h["lane"] == int(g["lane_syms"][0])
+    assert h["nsb"] == int(g["n_subblocks"][0]) and h["raw"] == 2 * n
+    want_len = np.zeros(256, np.uint8)
+    for kv in g["codelen"]:
+        k, v = kv.split("=")
+        want_len[int(k, 16)] = int(v)
+    assert (h["codelen"] == want_len).all()
+    st = stripe(blob, 0)
+    assert st["n_bits"] == int(g["n_bits"][0])
+    bits = blob[st["off"] + st["bits_off"]: st["off"] + st["bits_off"] + len(g["bitstream"][0]) // 2]
+    assert bytes(bits) == bytes.fromhex(g["bitstream"][0])
+    start, m, lanes = sub_rec(blob, st, 0)
+    assert start == 0 and m == n
+    want_lanes = [int(v) for v in g["lane_bits"]]
+    assert lanes[: len(want_lanes)].tolist() == want_lanes and (lanes[len(want_lanes):] == 0).all()
+    assert (O.decode_layer(blob) == raw).all()
+
+
 # ---------------------------------------------------------------------------
 # P1/P5/P6: round trip, closed-form bit counts, index replay
 
-def _roundtrip_checks(x):
-    blob = O.encode_layer(x)
+def _roundtrip_checks(x, lane_syms=256):
+    blob = O.encode_layer(x, lane_syms)
     h = hdr(blob)
     assert h["raw"] == x.size and h["cbytes"] == blob.size
     assert h["ns"] == -(-x.size // (1 << 26))
+    assert h["lane"] == lane_syms and h["sub"] == 256 * lane_syms
+    assert h["nsb"] == -(-x.size // (256 * lane_syms))
     counts_layer = np.bincount(x[1::2], minlength=256)
     lens = h["codelen"]
     assert (lens[counts_layer == 0] == 0).all() and (lens[counts_layer > 0] > 0).all()
@@ -323,11 +355,22 @@ def _roundtrip_checks(x):
         assert st["n_bits"] == int((cs * lens.astype(np.int64)).sum())
         assert st["first_sb"] == nsb_total
         nsb_total += st["nsb"]
-        # the subblock records' lane counts add up to the stripe's bits
+        # every lane chunk's recorded bit count is the sum of its symbols'
+        # code lengths (closed form), and the records' start bits are the
+        # running sum of those counts
+        sub_syms = 128 * lane_syms
+        assert st["nsb"] == -(-sym.size // sub_syms)
+        bits_of = lens.astype(np.int64)[sym]
+        chunk = np.add.reduceat(bits_of, np.arange(0, sym.size, lane_syms)) if sym.size else bits_of
         tot = 0
         for j in range(st["nsb"]):
             start, n, lanes = sub_rec(blob, st, j)
             assert start == tot
+            assert n == min(sub_syms, sym.size - j * sub_syms)
+            want = np.zeros(128, np.int64)
+            part = chunk[j * 128: (j + 1) * 128]
+            want[: part.size] = part
+            assert (lanes.astype(np.int64) == want).all()
             tot += int(lanes.sum())
         assert tot == st["n_bits"]
     assert nsb_total == h["nsb"]
@@ -347,6 +390,34 @@ def test_roundtrip_tiny():
 @pytest.mark.parametrize("n_bytes", [2, 4, 1022, 1024, 1026, 65534, 65536, 65538, 3 * 65536 + 514])
 def test_roundtrip_small_sizes(n_bytes):
     _roundtrip_checks(synth.small_random(n_bytes, n_bytes))
+
+
+@pytest.mark.parametrize("n_bytes", [2, 126, 128, 130, 16382, 16384, 16386, 3 * 16384 + 514, 65536 + 130])
+def test_roundtrip_short_lane_chunks(n_bytes):
+    """The 64-symbol lane-chunk layout (16 KiB subblocks of 128 chunks):
+    the same code, bitstream and even plane as the 256-symbol layout, only
+    the index differs."""
+    x = synth.small_random(n_bytes + 3, n_bytes)
+    blob = _roundtrip_checks(x, 64)
+    wide = O.encode_layer(x)
+    s64, s256 = stripe(blob, 0), stripe(wide, 0)
+    assert s64["n_bits"] == s256["n_bits"]
+    bits64 = blob[s64["off"] + s64["bits_off"]: s64["off"] + s64["bits_off"] + s64["bit_bytes"]]
+    bits256 = wide[s256["off"] + s256["bits_off"]: s256["off"] + s256["bits_off"] + s256["bit_bytes"]]
+    assert (bits64 == bits256).all()
+
+
+def test_roundtrip_short_lane_chunks_two_stripes():
+    x = synth.small_random(91, (1 << 26) + 3 * 16384 + 66)
+    blob = _roundtrip_checks(x, 64)
+    assert stripe(blob, 1)["first_sb"] == 4096
+
+
+def test_lane_syms_other_than_64_or_256_rejected():
+    x = synth.small_random(3, 1024)
+    for bad in (0, 32, 128, 512):
+        with pytest.raises(ValueError):
+            O.encode_layer(x, bad)
 
 
 def test_roundtrip_edge_layers():
