@@ -25,7 +25,10 @@
  *   layer header (K3HUF_HDR_BYTES = 304):
  *     0   char[4] magic "K3HF"         4  u16 version = 1
  *     6   u16 maxlen = 12               8  u32 stripe_bytes = 2^26
- *     12  u32 subblock_bytes = 2^16     16 u32 lane_syms = 256
+ *     12  u32 subblock_bytes = 256 * lane_syms (2^16, or 2^14)
+ *     16  u32 lane_syms = 256, or 64 (K3HUF_LANE_SYMS_SHORT: the layout for
+ *         small layers, whose decode time is one lane chunk's chain of
+ *         dependent table lookups; a subblock always holds 128 lane chunks)
  *     20  u32 n_stripes = ceil(raw_bytes / 2^26)
  *     24  u64 raw_bytes (even, > 0)     32 u32 n_subblocks (total)
  *     36  u32 reserved = 0              40 u64 container_bytes
@@ -35,13 +38,15 @@
  *   stripe record (at stripe_off[s]):
  *     0 u32 raw_bytes   4 u32 n_syms = raw_bytes / 2   8 u32 n_bits
  *     12 u32 bit_bytes = ceil(n_bits / 8) rounded up to 16
- *     16 u32 first_subblock = s * 1024   20 u32 n_subblocks = ceil(n_syms / 32768)
+ *     16 u32 first_subblock = s * 2^26 / subblock_bytes
+ *     20 u32 n_subblocks = ceil(n_syms / (128 * lane_syms))
  *     24 u32 bits_off   28 u32 even_off  (both from the record start,
  *          multiples of 256; decoders require only 16-byte alignment)
  *     32 subblock records, K3HUF_SUBBLOCK_REC_BYTES = 264 each:
  *          u32 start_bit (stripe-relative bit index of the subblock's first code)
- *          u32 n_syms    (32768, or fewer in the stripe's last subblock)
- *          u16 lane_bits[128] (code bits of each 256-symbol lane chunk; 0 if empty)
+ *          u32 n_syms    (128 * lane_syms, or fewer in the stripe's last subblock)
+ *          u16 lane_bits[128] (code bits of each lane chunk of lane_syms
+ *                             symbols; 0 if empty)
  *        zero pad to 256
  *     bits_off: the stripe's codes, most-significant bit first (K3 page,
  *        "decode loop": the stream head sits at the top of the bit window),
@@ -50,7 +55,8 @@
  *   The 256-byte boundaries keep each plane on whole cache lines, so the
  *   GPU's line-sized reads of a lane chunk's even bytes touch one line each.
  *   Stripe s covers raw bytes [s * 2^26, min((s + 1) * 2^26, raw_bytes)).
- *   Global subblock k covers raw bytes [k * 2^16, min((k + 1) * 2^16, raw_bytes)).
+ *   Global subblock k covers raw bytes [k * subblock_bytes, min((k + 1) *
+ *   subblock_bytes, raw_bytes)).
  */
 #ifndef K3HUF_H
 #define K3HUF_H
@@ -68,6 +74,7 @@ extern "C" {
 #define K3HUF_SUBBLOCK_BYTES (1u << 16)
 #define K3HUF_SUBBLOCK_SYMS (K3HUF_SUBBLOCK_BYTES / 2)
 #define K3HUF_LANE_SYMS 256u
+#define K3HUF_LANE_SYMS_SHORT 64u
 #define K3HUF_LANES (K3HUF_SUBBLOCK_SYMS / K3HUF_LANE_SYMS)
 #define K3HUF_HDR_BYTES 304u
 #define K3HUF_STRIPE_HDR_BYTES 32u
@@ -114,6 +121,7 @@ typedef struct k3huf_info {
     uint32_t n_stripes;
     uint32_t n_subblocks;
     uint8_t codelen[256];
+    uint32_t lane_syms;       /* 256 or 64 */
 } k3huf_info;
 
 /*
@@ -145,6 +153,8 @@ int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out);
  *   or a lane whose codes end off its index; the caller clears it beforehand
  *   and reads it after the stream synchronizes. Subblocks with bad records
  *   are left unwritten; no read ever leaves [d_blob, d_blob + blob_bytes).
+ * Both lane-chunk layouts are decoded (the kernel reads lane_syms from the
+ * header).
  * Returns K3HUF_OK once queued, K3HUF_E_ARG for bad sizes or alignment (also
  * for blob_bytes >= 2^36: the kernel keeps stripe offsets in 16-byte units;
  * and for out_bytes > 2 * blob_bytes, which no blob of this format allows:
@@ -247,18 +257,34 @@ int k3huf_decode_ring_host(const k3huf_host_layer* layers, int n_layers, void* c
  * longest-first canonical codes, stripes and the subblock/lane index.
  * h_raw: host bf16 layer bytes (raw_bytes even, > 0). h_out: host buffer of
  * cap >= k3huf_encode_bound(raw_bytes). n_threads <= 0 picks the core count.
- * Returns the container size, or K3HUF_E_ARG.
+ * Returns the container size, or K3HUF_E_ARG. Lane chunks of 256 symbols.
+ * k3huf_encode_bound_lanes / k3huf_encode_layer_lanes -- the same for lane
+ * chunks of lane_syms symbols, 256 or K3HUF_LANE_SYMS_SHORT (64); any other
+ * value is K3HUF_E_ARG. The code, bitstream and even plane do not depend on
+ * it, only the index does (its records cover 128 * lane_syms symbols each).
  */
 int64_t k3huf_encode_bound(uint64_t raw_bytes);
 int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, uint64_t cap,
                            int n_threads);
+int64_t k3huf_encode_bound_lanes(uint64_t raw_bytes, uint32_t lane_syms);
+/* The lane-chunk length that decodes faster on MI355X for a layer of
+ * raw_bytes: 64 up to K3HUF_SHORT_LANES_MAX_RAW (16 MiB), where a decode is
+ * one round of work units and its time one lane's chain of dependent table
+ * lookups (measured on trunk-recipe layers: 8.0 against 14.5 us at 64 KiB,
+ * 8.9 against 15.3 us at 4 MiB, 13.6 against 16.1 us at 16 MiB), else 256
+ * (19.5 against 17.7 us at 32 MiB, 98 against 83 us at 256 MiB). */
+#define K3HUF_SHORT_LANES_MAX_RAW (16ull << 20)
+uint32_t k3huf_lane_syms_for(uint64_t raw_bytes);
+int64_t k3huf_encode_layer_lanes(const void* h_raw, uint64_t raw_bytes, uint32_t lane_syms, void* h_out,
+                                 uint64_t cap, int n_threads);
 
 /*
  * k3huf_encode_work_bytes -- device work-buffer size k3huf_encode_layer_dev
  *   needs for raw_bytes of layer data (or K3HUF_E_ARG for an odd or zero size).
  * k3huf_encode_layer_dev -- the packer on the GPU: the bf16 layer in device
  * memory becomes, in device memory, the container k3huf_encode_layer writes
- * for the same bytes (byte for byte). K3 page, "what was implemented": one
+ * for the same bytes (byte for byte; lane chunks of 256 symbols: the GPU
+ * packer writes only that layout). K3 page, "what was implemented": one
  * histogram and codelen[256] for the whole layer's odd bytes, MSB-first
  * Huffman bitstream per stripe, even plane raw; "canonical code assignment
  * and Kraft check": depths limited to 12 bits, longest-first canonical codes.

@@ -44,11 +44,8 @@ namespace {
 constexpr int kWaves = 7;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kUnitLanes = 64;                        // lane chunks per work unit
-constexpr int kUnitSyms = kUnitLanes * K3HUF_LANE_SYMS;  // 16384
 constexpr int kUnitsPerSub = K3HUF_LANES / kUnitLanes;   // 2
 constexpr int kPhase = 64;                            // symbols per lane per phase
-constexpr int kPhases = K3HUF_LANE_SYMS / kPhase;    // 4
-constexpr int kSuper = 4;                             // phases per even-plane prefetch
 constexpr int kGroups = kPhase / 4;                   // 4-symbol groups per phase (tail path)
 constexpr int kRounds = 64 / 8;                       // write-out rounds (8 chunks each)
 constexpr int kBufBytes = 7680;                       // per-wave bitstream buffer
@@ -64,8 +61,21 @@ constexpr int kLookups = 5;
 constexpr int kMaxWindows = (kPhase + kLookups - 1) / kLookups;
 constexpr int kTabBytes = K3HUF_LUT_ENTRIES * 4;
 constexpr int kLdsBytes = kTabBytes + kWaves * kWaveLds;
-constexpr uint32_t kSubPerStripe = K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES;
 static_assert(kLdsBytes <= 163840, "LDS budget");
+
+// Lane-chunk geometry of a layer: L symbols per lane chunk (K3HUF_LANE_SYMS,
+// or K3HUF_LANE_SYMS_SHORT in the layout for small layers); a subblock holds
+// K3HUF_LANES chunks, a work unit half of them, and a lane decodes its chunk
+// in L / 64 phases.
+template <uint32_t L>
+struct Geo {
+    static constexpr int kUnitSyms = kUnitLanes * int(L);                 // 16384 or 4096
+    static constexpr int kPhases = int(L) / kPhase;                       // 4 or 1
+    static constexpr int kSuper = kPhases < 4 ? kPhases : 4;              // phases per even-plane prefetch
+    static constexpr uint32_t kSubSyms = K3HUF_LANES * L;                 // 32768 or 8192
+    static constexpr uint32_t kSubBytes = 2 * kSubSyms;
+    static constexpr uint32_t kSubPerStripe = K3HUF_STRIPE_BYTES / kSubBytes;   // 1024 or 4096
+};
 
 // LDS decode table, derived per workgroup from the 4096-entry
 // (symbol << 4 | length) table: one lookup of the top 12 window bits yields
@@ -132,7 +142,6 @@ struct DecodeArgs {
     const uint16_t* lut;
     uint8_t* out;
     uint64_t out_bytes;
-    uint32_t n_sub;
     uint32_t n_stripes;
     uint32_t* status;
     uint32_t slot;        // work-counter slot of this launch (when dyn)
@@ -302,10 +311,11 @@ __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint32_t
 // store waits for the ones before it to complete (vmcnt counts stores too,
 // and a store behind a branch makes the compiler wait for everything
 // outstanding). `after(ph)` runs after each phase ph.
-template <bool kGather, class After>
+template <uint32_t L, bool kGather, class After>
 __device__ __forceinline__ void decode_super(const uint32_t* tab, uint32_t* buf, uint8_t* stage,
                                              const Unit& un, int sp, int lane, LaneState& ls,
                                              After&& after) {
+    constexpr int kSuper = Geo<L>::kSuper;
     const int sub_line = lane >> 3, part = lane & 7;
     uint2 ev[kRounds][kSuper];
     // the super-phase's even-plane bytes: whole lines per chunk
@@ -314,7 +324,7 @@ __device__ __forceinline__ void decode_super(const uint32_t* tab, uint32_t* buf,
         const int c = rr * 8 + sub_line;
 #pragma unroll
         for (int f = 0; f < kSuper; ++f) {
-            const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t((sp + f) * kPhase + part * 8);
+            const uint32_t u = uint32_t(c) * L + uint32_t((sp + f) * kPhase + part * 8);
             ev[rr][f] = *reinterpret_cast<const uint2*>(un.even + u);
         }
     }
@@ -346,7 +356,7 @@ __device__ __forceinline__ void decode_super(const uint32_t* tab, uint32_t* buf,
             const int c = rr * 8 + sub_line;
             const uint2 sy = staged8(stage, c, part);
             const uint2 e = ev[rr][q];
-            const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
+            const uint32_t u = uint32_t(c) * L + uint32_t(ph * kPhase + part * 8);
             // the output is written once and not read back here: stream it
             // past the caches (non-temporal store)
             const v4u o = {__builtin_amdgcn_perm(sy.x, e.x, 0x05010400u),
@@ -360,30 +370,36 @@ __device__ __forceinline__ void decode_super(const uint32_t* tab, uint32_t* buf,
     }
 }
 
-// Decode a full unit: its super-phases, then the lane checks. `mid` runs
-// after the second phase and `late` after the third (the caller asks for its
-// next unit, then learns it and requests its record). kGather false: the
-// caller has copied the unit's codes from stripe dword j0 on into `buf`.
-template <bool kGather, class Mid, class Late>
+// Decode a full unit: its super-phases, then the lane checks. With four
+// phases, `mid` runs after the second phase and `late` after the third (the
+// caller asks for its next unit, then learns it and requests its record);
+// with one phase both run before it. kGather false: the caller has copied
+// the unit's codes from stripe dword j0 on into `buf`.
+template <uint32_t L, bool kGather, class Mid, class Late>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const uint32_t* tab, uint32_t* buf,
                                             uint8_t* stage, const Unit& un, int j0,
                                             uint32_t lane_start, uint32_t lane_bits, int lane,
                                             Mid&& mid, Late&& late) {
+    constexpr int kPhases = Geo<L>::kPhases, kSuper = Geo<L>::kSuper;
     // the buffer starts at least one dword before the lane's first code, so
     // pm1 >= 0
     LaneState ls = {lane_start - 32u * uint32_t(j0) - 1u, 0u, 0u, 0u, lane_start};
     const uint32_t pm1_0 = ls.pm1;
+    if (kPhases == 1) {
+        mid();
+        late();
+    }
 #pragma unroll 1
     for (int sp = 0; sp < kPhases; sp += kSuper) {
-        decode_super<kGather>(tab, buf, stage, un, sp, lane, ls, [&](int ph) {
-            if (ph == 1) mid();
-            if (ph == 2) late();
+        decode_super<L, kGather>(tab, buf, stage, un, sp, lane, ls, [&](int ph) {
+            if (kPhases > 1 && ph == 1) mid();
+            if (kPhases > 1 && ph == 2) late();
         });
     }
     // a last lookup that ran one symbol past the chunk took that symbol's
     // bits too
     uint32_t used = kGather ? ls.abs - lane_start : ls.pm1 - pm1_0;
-    if (ls.cnt > K3HUF_LANE_SYMS) used -= ent_bits(ls.last) - ent_len1(ls.last);
+    if (ls.cnt > L) used -= ent_bits(ls.last) - ent_len1(ls.last);
     // one status update per wave (a corrupt layer would otherwise send an
     // atomic per lane to the one status word)
     const bool code_bad = __any((ls.bad & kBad) != 0u), end_bad = __any(used != lane_bits);
@@ -391,15 +407,17 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const uint32_t*
     if (lane == 0 && end_bad) flag(a.status, K3HUF_DEV_LANE_END);
 }
 
-// The same for the layer's last unit when it holds fewer than 16384 symbols:
-// lane t decodes clamp(nsyms - 256 t, 0, 256) symbols one code per table
-// step; kept plain (it runs at most once per layer).
+// The same for the layer's last unit when it holds fewer than 64 L symbols:
+// lane t decodes clamp(nsyms - L t, 0, L) symbols one code per table step;
+// kept plain (it runs at most once per layer).
+template <uint32_t L>
 __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uint32_t* tab,
                                                   const uint32_t* buf, uint8_t* stage, const Unit& un,
                                                   int j0, uint32_t lane_start, uint32_t lane_bits,
                                                   int l0, int l1, int lane) {
     const bool mine = lane >= l0 && lane < l1;
-    const int lane_cnt = min(max(int(un.nsyms) - lane * int(K3HUF_LANE_SYMS), 0), int(K3HUF_LANE_SYMS));
+    constexpr int kPhases = Geo<L>::kPhases;
+    const int lane_cnt = min(max(int(un.nsyms) - lane * int(L), 0), int(L));
     uint32_t pm1 = lane_start - 32u * uint32_t(j0) - 1u;
     const uint32_t pm1_0 = pm1;
     uint32_t bad = 0;
@@ -435,7 +453,7 @@ __device__ __forceinline__ void decode_lanes_tail(const DecodeArgs& a, const uin
 #pragma unroll 1
         for (int rr = 0; rr < kRounds; ++rr) {
             const int c = rr * 8 + sub_line;
-            const uint32_t u = uint32_t(c) * K3HUF_LANE_SYMS + uint32_t(ph * kPhase + part * 8);
+            const uint32_t u = uint32_t(c) * L + uint32_t(ph * kPhase + part * 8);
             if (c < l0 || c >= l1 || u >= un.nsyms) continue;
             const uint2 sy = staged8(stage, c, part);
             const uint2 e = *reinterpret_cast<const uint2*>(un.even + u);
@@ -496,8 +514,9 @@ struct StripeLane {
 __device__ __forceinline__ uint64_t stripe_raw(const DecodeArgs& a, uint32_t s) {
     return min(uint64_t(K3HUF_STRIPE_BYTES), a.out_bytes - uint64_t(s) * K3HUF_STRIPE_BYTES);
 }
+template <uint32_t L>
 __device__ __forceinline__ uint32_t stripe_subblocks(uint32_t n_syms) {
-    return (n_syms + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
+    return (n_syms + Geo<L>::kSubSyms - 1) / Geo<L>::kSubSyms;
 }
 
 // Branch-free: every lane issues its loads (a stripe that does not exist,
@@ -517,19 +536,20 @@ __device__ __forceinline__ StripeOff stripe_offsets(const DecodeArgs& a, uint32_
     const uint32_t in = bit((soff & 15) == 0) & bit(soff + K3HUF_STRIPE_HDR_BYTES <= a.blob_bytes);
     return {in ? soff : 0ull, in};
 }
+template <uint32_t L>
 __device__ __forceinline__ StripeLane stripe_values(const DecodeArgs& a, uint32_t blk, int lane, StripeOff o) {
     const uint32_t s = blk * 64u + uint32_t(lane);
     const bool has = s < a.n_stripes;
     const uint32_t sc = has ? s : 0u;
     const uint64_t raw_s = stripe_raw(a, sc);
     const uint32_t n = uint32_t(raw_s / 2);
-    const uint32_t nsb = stripe_subblocks(n);
+    const uint32_t nsb = stripe_subblocks<L>(n);
     const uint64_t so = o.so;
     const uint4 r0 = *reinterpret_cast<const uint4*>(a.blob + so);
     const uint4 r1 = *reinterpret_cast<const uint4*>(a.blob + so + 16);
     const uint32_t n_bits = r0.z, bit_bytes = r0.w, bits_off = r1.z, even_off = r1.w;
     const uint32_t ok = bit(has) & o.in & bit(r0.x == uint32_t(raw_s)) & bit(r0.y == n) &
-                        bit(r1.x == sc * kSubPerStripe) & bit(r1.y == nsb) &
+                        bit(r1.x == sc * Geo<L>::kSubPerStripe) & bit(r1.y == nsb) &
                         bit(uint64_t(n_bits) <= uint64_t(K3HUF_MAXLEN) * n) &
                         bit(k3huf_bounds::stripe_planes_ok(a.blob_bytes, so, n, nsb, n_bits, bit_bytes,
                                                            bits_off, even_off));
@@ -540,8 +560,9 @@ __device__ __forceinline__ StripeLane stripe_values(const DecodeArgs& a, uint32_
     t.n_bits = ok ? n_bits : kNoStripe;
     return t;
 }
+template <uint32_t L>
 __device__ __forceinline__ StripeLane load_stripes(const DecodeArgs& a, uint32_t blk, int lane) {
-    return stripe_values(a, blk, lane, stripe_offsets(a, blk, lane));
+    return stripe_values<L>(a, blk, lane, stripe_offsets(a, blk, lane));
 }
 
 // A subblock record as vector registers: lanes 0 and 1 hold start_bit and
@@ -562,10 +583,13 @@ __device__ __forceinline__ RecLanes load_rec(const uint8_t* rec, bool has_next, 
     return r;
 }
 
-__global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-    __shared__ uint32_t local_ticket;   // the workgroup's own counter (launches without a slot)
+// The kernel for a layer of lane chunks of L symbols. lds: the workgroup's
+// kLdsBytes; local_ticket: its own counter (launches without a slot).
+template <uint32_t L>
+__device__ __forceinline__ void decode_layer_body(const DecodeArgs& a, uint8_t* lds, uint32_t& local_ticket) {
+    using G = Geo<L>;
     uint32_t* tab = reinterpret_cast<uint32_t*>(lds);  // at LDS address 0
+    const uint32_t n_sub = uint32_t((a.out_bytes + G::kSubBytes - 1) / G::kSubBytes);
 
     // layer header must describe exactly this call (uniform over the grid;
     // every field is tested, so the loads go out together). The set-up below
@@ -573,14 +597,14 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
     // after it and the header's loads travel with its first round trip.
     const uint8_t* b = a.blob;
     const uint32_t hdr_ok = bit(ld32(b) == 0x4648334Bu /* "K3HF" */) & bit(ld32(b + 4) == (1u | (12u << 16))) &
-                            bit(ld32(b + 8) == K3HUF_STRIPE_BYTES) & bit(ld32(b + 12) == K3HUF_SUBBLOCK_BYTES) &
-                            bit(ld32(b + 16) == K3HUF_LANE_SYMS) & bit(ld32(b + 20) == a.n_stripes) &
-                            bit(ld64(b + 24) == a.out_bytes) & bit(ld32(b + 32) == a.n_sub) &
+                            bit(ld32(b + 8) == K3HUF_STRIPE_BYTES) & bit(ld32(b + 12) == G::kSubBytes) &
+                            bit(ld32(b + 16) == L) & bit(ld32(b + 20) == a.n_stripes) &
+                            bit(ld64(b + 24) == a.out_bytes) & bit(ld32(b + 32) == n_sub) &
                             bit(ld64(b + 40) <= a.blob_bytes);
 
     const int lane = threadIdx.x & 63;
     const uint32_t wave = uniform(threadIdx.x >> 6);
-    const uint32_t n_units = a.n_sub * kUnitsPerSub;
+    const uint32_t n_units = n_sub * kUnitsPerSub;
     const uint32_t T = gridDim.x * kWaves;
     const uint32_t groups = min(kGroupsPerSlot, gridDim.x);
     const uint32_t group = blockIdx.x % groups;
@@ -600,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         ta[q] = i < K3HUF_LUT_ENTRIES ? uint32_t(a.lut[i]) : 0u;
     }
     // stripe values of the block holding this wave's first unit
-    uint32_t blk = h < n_units ? unit_of(h) / (kUnitsPerSub * kSubPerStripe * 64u) : 0u;
+    uint32_t blk = h < n_units ? unit_of(h) / (kUnitsPerSub * G::kSubPerStripe * 64u) : 0u;
     const StripeOff so0 = stripe_offsets(a, blk, lane);
     uint32_t pf_h = 0xFFFFFFFFu;   // position whose unit's record `pf` holds
     RecLanes pf = {0u, 0u, 0u};
@@ -609,26 +633,26 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         // the records of a stripe that passes its checks lie inside, so the
         // record is the right one whenever the unit is decoded
         const uint32_t kn = unit_of(h) / kUnitsPerSub;
-        const uint32_t sn = kn / kSubPerStripe, jn = kn % kSubPerStripe;
+        const uint32_t sn = kn / G::kSubPerStripe, jn = kn % G::kSubPerStripe;
         const uint64_t son = uint64_t(lane_value(uint32_t(so0.so >> 4), sn & 63u)) << 4;
-        const bool nx = jn + 1 < stripe_subblocks(uint32_t(stripe_raw(a, sn) / 2));
+        const bool nx = jn + 1 < stripe_subblocks<L>(uint32_t(stripe_raw(a, sn) / 2));
         const uint64_t ro = k3huf_bounds::subblock_rec_in_blob(a.blob_bytes, son, jn, nx)
                                 ? son + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jn
                                 : 0ull;
         pf = load_rec(b + ro, nx, lane);
         pf_h = h;
     }
-    StripeLane sl = stripe_values(a, blk, lane, so0);
+    StripeLane sl = stripe_values<L>(a, blk, lane, so0);
     // request the record of position p's unit (when its stripe is in `sl`)
     auto request_rec = [&](uint32_t p) {
         pf_h = 0xFFFFFFFFu;
         if (p < n_units) {
             const uint32_t kn = unit_of(p) / kUnitsPerSub;
-            const uint32_t sn = kn / kSubPerStripe, jn = kn % kSubPerStripe;
+            const uint32_t sn = kn / G::kSubPerStripe, jn = kn % G::kSubPerStripe;
             if ((sn >> 6) == blk && lane_value(sl.n_bits, sn & 63u) != kNoStripe) {
                 const uint8_t* stn = b + (uint64_t(lane_value(sl.off16, sn & 63u)) << 4);
                 pf = load_rec(stn + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jn,
-                              jn + 1 < stripe_subblocks(uint32_t(stripe_raw(a, sn) / 2)), lane);
+                              jn + 1 < stripe_subblocks<L>(uint32_t(stripe_raw(a, sn) / 2)), lane);
                 pf_h = p;
             }
         }
@@ -684,17 +708,17 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         };
         const uint32_t un_idx = unit_of(h);
         const uint32_t k = un_idx / kUnitsPerSub, half = un_idx % kUnitsPerSub;
-        const uint32_t s = k / kSubPerStripe, jsb = k % kSubPerStripe;
+        const uint32_t s = k / G::kSubPerStripe, jsb = k % G::kSubPerStripe;
         if ((s >> 6) != blk) {
             blk = s >> 6;
-            sl = load_stripes(a, blk, lane);
+            sl = load_stripes<L>(a, blk, lane);
         }
         const uint32_t n_bits = lane_value(sl.n_bits, s & 63u);
         const uint64_t soff = uint64_t(lane_value(sl.off16, s & 63u)) << 4;
         const uint32_t bits_off = lane_value(sl.bits_off, s & 63u);
         const uint32_t even_off = lane_value(sl.even_off, s & 63u);
         const uint32_t n = uint32_t(stripe_raw(a, s) / 2);
-        const uint32_t nsb = stripe_subblocks(n);
+        const uint32_t nsb = stripe_subblocks<L>(n);
         const uint8_t* st = b + soff;
         if (pf_h != h && n_bits != kNoStripe) {
             pf = load_rec(st + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * jsb,
@@ -715,10 +739,10 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
             if (lane == 0 && half == 0) flag(a.status, K3HUF_DEV_STRIPE);
             continue;
         }
-        const uint32_t nsyms = min(uint32_t(K3HUF_SUBBLOCK_SYMS), n - jsb * K3HUF_SUBBLOCK_SYMS);
+        const uint32_t nsyms = min(G::kSubSyms, n - jsb * G::kSubSyms);
         const uint32_t total = unit_bits + other_bits;
         const int gl = int(half) * kUnitLanes + lane;    // lane chunk within the subblock
-        const int cnt = min(max(int(nsyms) - gl * int(K3HUF_LANE_SYMS), 0), int(K3HUF_LANE_SYMS));
+        const int cnt = min(max(int(nsyms) - gl * int(L), 0), int(L));
         // the prefix must also be monotone and end at the unit's sum, which
         // keeps every lane's bit range inside the unit's codes
         const bool lane_ok = lb >= uint32_t(cnt) && lb <= uint32_t(cnt) * K3HUF_MAXLEN &&
@@ -730,27 +754,27 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
             continue;
         }
         Unit un;
-        un.nsyms = uint32_t(min(max(int(nsyms) - int(half) * kUnitSyms, 0), kUnitSyms));
+        un.nsyms = uint32_t(min(max(int(nsyms) - int(half) * G::kUnitSyms, 0), G::kUnitSyms));
         if (un.nsyms == 0) continue;
         const uint32_t unit_start = start_bit + (half ? other_bits : 0u);
         un.bits = st + bits_off;
         un.dmax = k3huf_bounds::stripe_read_dmax(bits_off, even_off, n);
-        un.even = st + even_off + uint64_t(jsb) * K3HUF_SUBBLOCK_SYMS + uint64_t(half) * kUnitSyms;
-        un.out = a.out + uint64_t(k) * K3HUF_SUBBLOCK_BYTES + 2ull * half * kUnitSyms;
+        un.even = st + even_off + uint64_t(jsb) * G::kSubSyms + uint64_t(half) * G::kUnitSyms;
+        un.out = a.out + uint64_t(k) * G::kSubBytes + 2ull * half * G::kUnitSyms;
         const uint32_t lane_start = unit_start + incl - lb;
         const uint32_t lane_end = unit_start + incl;
 
-        if (un.nsyms == uint32_t(kUnitSyms)) {
+        if (un.nsyms == uint32_t(G::kUnitSyms)) {
             const int j0 = first_dword(lane_value(lane_start, 0));
             const int units = (end_dword(lane_value(lane_end, 63)) - j0) / 4;
             if (units * 16 <= kBufBytes) {
                 fill_buffer(buf, un, j0, units, lane);
                 drain_vm();   // fill_buffer has just drained it
-                decode_unit<false>(a, tab, buf, stage, un, j0, lane_start, lb, lane, ask, learn);
+                decode_unit<L, false>(a, tab, buf, stage, un, j0, lane_start, lb, lane, ask, learn);
             } else {
                 // codes exceed the buffer (long codes, e.g. a vector of
                 // norm gains): each lane gathers its codes phase by phase
-                decode_unit<true>(a, tab, buf, stage, un, 0, lane_start, lb, lane, ask, learn);
+                decode_unit<L, true>(a, tab, buf, stage, un, 0, lane_start, lb, lane, ask, learn);
             }
         } else {
             // the layer's partial last unit: passes over consecutive lane
@@ -762,7 +786,7 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
                 const int l1 = m ? int(__builtin_ctzll(m)) : 64;   // > l0: one chunk always fits
                 const int units = (end_dword(lane_value(lane_end, l1 - 1)) - j0) / 4;
                 fill_buffer(buf, un, j0, units, lane);
-                decode_lanes_tail(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
+                decode_lanes_tail<L>(a, tab, buf, stage, un, j0, lane_start, lb, l0, l1, lane);
                 l0 = l1;
             }
         }
@@ -781,6 +805,17 @@ __global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
         if (done == gridDim.x - 1)
             for (uint32_t g = 0; g <= kGroupsPerSlot; ++g) atomicExch(&slot[g * kCounterStride], 0u);
     }
+}
+
+// The layer's lane-chunk length picks the body (uniform over the grid; any
+// other value fails the body's header check).
+__global__ __launch_bounds__(kThreads) void k3huf_decode_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    __shared__ uint32_t local_ticket;
+    if (ld32(a.blob + 16) == K3HUF_LANE_SYMS_SHORT)
+        decode_layer_body<K3HUF_LANE_SYMS_SHORT>(a, lds, local_ticket);
+    else
+        decode_layer_body<K3HUF_LANE_SYMS>(a, lds, local_ticket);
 }
 
 struct DevInfo {
@@ -841,7 +876,11 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
         (reinterpret_cast<uintptr_t>(d_lut) & 1) || (reinterpret_cast<uintptr_t>(d_status) & 3))
         return K3HUF_E_ARG;
     if (blob_bytes < K3HUF_HDR_BYTES + 8 || out_bytes == 0 || (out_bytes & 1)) return K3HUF_E_ARG;
+    // subblocks of the 256-symbol and of the 64-symbol layout (the kernel
+    // reads which one the blob uses from its header)
     const uint64_t n_sub = (uint64_t(out_bytes) + K3HUF_SUBBLOCK_BYTES - 1) / K3HUF_SUBBLOCK_BYTES;
+    const uint64_t n_sub_short = (uint64_t(out_bytes) + Geo<K3HUF_LANE_SYMS_SHORT>::kSubBytes - 1) /
+                                 Geo<K3HUF_LANE_SYMS_SHORT>::kSubBytes;
     const uint64_t n_stripes = (uint64_t(out_bytes) + K3HUF_STRIPE_BYTES - 1) / K3HUF_STRIPE_BYTES;
     if (n_sub > 0xFFFFFFFFull || blob_bytes < K3HUF_HDR_BYTES + 8 * n_stripes ||
         uint64_t(blob_bytes) >= (1ull << 36) || uint64_t(out_bytes) > 2ull * blob_bytes)
@@ -863,8 +902,10 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     // (trunk-recipe layers: 0.94-1.00x of the device-counter time at 1.1-4.6
     // rounds, 1.03-1.05x at 6.9-20 rounds)
     const uint64_t want = n_sub * kUnitsPerSub;
+    const uint64_t want_short = n_sub_short * kUnitsPerSub;
     const uint64_t resident = uint64_t(di.cus) * uint64_t(di.wg_per_cu);
-    const unsigned grid = unsigned(want < resident ? want : resident);
+    // one workgroup per unit of the finer layout, up to a full chip
+    const unsigned grid = unsigned(want_short < resident ? want_short : resident);
     const bool dyn = slot != kNoSlot && capture == hipStreamCaptureStatusNone &&
                      want > uint64_t(kDynRounds) * grid * kWaves;
     DecodeArgs a;
@@ -873,7 +914,6 @@ int k3huf_decode_layer(const void* d_blob, size_t blob_bytes, const uint16_t* d_
     a.lut = d_lut;
     a.out = static_cast<uint8_t*>(d_out);
     a.out_bytes = out_bytes;
-    a.n_sub = uint32_t(n_sub);
     a.n_stripes = uint32_t(n_stripes);
     a.status = d_status;
     a.slot = dyn ? slot : 0u;

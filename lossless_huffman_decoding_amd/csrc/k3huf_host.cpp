@@ -163,8 +163,9 @@ void canonical_codes(const uint8_t* len, uint32_t* code) {
 }
 
 uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len, StripeGeom* g,
-                uint32_t* nsb_total) {
+                uint32_t* nsb_total, uint32_t lane_syms) {
     const uint32_t ns = stripes_for(raw_bytes);
+    const uint32_t sub_syms = K3HUF_LANES * lane_syms;
     for (uint32_t s = 0; s < ns; ++s) g[s] = StripeGeom{};
     uint64_t o = pad256(K3HUF_HDR_BYTES + 8ull * ns);
     uint32_t nsb = 0;
@@ -173,7 +174,7 @@ uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len, St
         G.raw0 = uint64_t(s) * K3HUF_STRIPE_BYTES;
         G.raw = uint32_t(std::min<uint64_t>(K3HUF_STRIPE_BYTES, raw_bytes - G.raw0));
         G.n = G.raw / 2;
-        G.nsb = (G.n + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
+        G.nsb = (G.n + sub_syms - 1) / sub_syms;
         uint64_t nbits = 0;
         for (int v = 0; v < 256; ++v) nbits += hist[size_t(s) * 256 + v] * len[v];
         G.nbits = uint32_t(nbits);
@@ -189,15 +190,15 @@ uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len, St
 }
 
 void write_layer_header(uint8_t* out, uint64_t raw_bytes, const uint8_t* len, const StripeGeom* g,
-                        uint32_t nsb_total, uint64_t total) {
+                        uint32_t nsb_total, uint64_t total, uint32_t lane_syms) {
     const uint32_t ns = stripes_for(raw_bytes);
     std::memset(out, 0, pad256(K3HUF_HDR_BYTES + 8ull * ns));
     std::memcpy(out, "K3HF", 4);
     wr(out + 4, 1, 2);
     wr(out + 6, K3HUF_MAXLEN, 2);
     wr(out + 8, K3HUF_STRIPE_BYTES, 4);
-    wr(out + 12, K3HUF_SUBBLOCK_BYTES, 4);
-    wr(out + 16, K3HUF_LANE_SYMS, 4);
+    wr(out + 12, 2ull * K3HUF_LANES * lane_syms, 4);
+    wr(out + 16, lane_syms, 4);
     wr(out + 20, ns, 4);
     wr(out + 24, raw_bytes, 8);
     wr(out + 32, nsb_total, 4);
@@ -210,6 +211,7 @@ void write_layer_header(uint8_t* out, uint64_t raw_bytes, const uint8_t* len, co
 }  // namespace k3huf_detail
 
 using k3huf_detail::canonical_codes;
+using k3huf_detail::lane_syms_ok;
 using k3huf_detail::limited_lengths;
 
 extern "C" {
@@ -264,17 +266,19 @@ int k3huf_build_table(const uint8_t codelen[256], uint16_t lut[4096]) {
 int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out) {
     if (!h_blob || !out || h_bytes < K3HUF_HDR_BYTES) return K3HUF_E_ARG;
     const uint8_t* b = static_cast<const uint8_t*>(h_blob);
+    const uint32_t lane_syms = uint32_t(rd(b + 16, 4));
+    const uint64_t sub_bytes = 2ull * K3HUF_LANES * lane_syms;
     if (std::memcmp(b, "K3HF", 4) != 0 || rd(b + 4, 2) != 1 || rd(b + 6, 2) != K3HUF_MAXLEN ||
-        rd(b + 8, 4) != K3HUF_STRIPE_BYTES || rd(b + 12, 4) != K3HUF_SUBBLOCK_BYTES ||
-        rd(b + 16, 4) != K3HUF_LANE_SYMS)
+        rd(b + 8, 4) != K3HUF_STRIPE_BYTES || !lane_syms_ok(lane_syms) || rd(b + 12, 4) != sub_bytes)
         return K3HUF_E_FORMAT;
     k3huf_info I;
+    I.lane_syms = lane_syms;
     I.n_stripes = uint32_t(rd(b + 20, 4));
     I.raw_bytes = rd(b + 24, 8);
     I.n_subblocks = uint32_t(rd(b + 32, 4));
     I.container_bytes = rd(b + 40, 8);
     if (!I.raw_bytes || (I.raw_bytes & 1) || I.n_stripes != stripes_for(I.raw_bytes) ||
-        I.n_subblocks != (I.raw_bytes + K3HUF_SUBBLOCK_BYTES - 1) / K3HUF_SUBBLOCK_BYTES ||
+        I.n_subblocks != (I.raw_bytes + sub_bytes - 1) / sub_bytes ||
         I.container_bytes < K3HUF_HDR_BYTES + 8ull * I.n_stripes)
         return K3HUF_E_FORMAT;
     std::memcpy(I.codelen, b + 48, 256);
@@ -282,23 +286,31 @@ int k3huf_layer_info(const void* h_blob, size_t h_bytes, k3huf_info* out) {
     return K3HUF_OK;
 }
 
-int64_t k3huf_encode_bound(uint64_t raw) {
-    if (!raw || (raw & 1)) return K3HUF_E_ARG;
+int64_t k3huf_encode_bound_lanes(uint64_t raw, uint32_t lane_syms) {
+    if (!raw || (raw & 1) || !lane_syms_ok(lane_syms)) return K3HUF_E_ARG;
+    const uint64_t sub_syms = uint64_t(K3HUF_LANES) * lane_syms;
     const uint64_t ns = stripes_for(raw);
     uint64_t b = pad256(K3HUF_HDR_BYTES + 8 * ns);
     for (uint64_t s = 0; s < ns; ++s) {
         const uint64_t rb = std::min<uint64_t>(K3HUF_STRIPE_BYTES, raw - s * K3HUF_STRIPE_BYTES);
-        const uint64_t n = rb / 2, nsb = (n + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
+        const uint64_t n = rb / 2, nsb = (n + sub_syms - 1) / sub_syms;
         b += pad256(K3HUF_STRIPE_HDR_BYTES + K3HUF_SUBBLOCK_REC_BYTES * nsb) +
              pad256(pad16((n * K3HUF_MAXLEN + 7) / 8)) + pad256(n);
     }
     return int64_t(b);
 }
 
-int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, uint64_t cap,
-                           int n_threads) {
-    if (!h_raw || !h_out || !raw_bytes || (raw_bytes & 1)) return K3HUF_E_ARG;
-    if (uint64_t(k3huf_encode_bound(raw_bytes)) > cap) return K3HUF_E_ARG;
+int64_t k3huf_encode_bound(uint64_t raw) { return k3huf_encode_bound_lanes(raw, K3HUF_LANE_SYMS); }
+
+uint32_t k3huf_lane_syms_for(uint64_t raw_bytes) {
+    return raw_bytes <= K3HUF_SHORT_LANES_MAX_RAW ? K3HUF_LANE_SYMS_SHORT : K3HUF_LANE_SYMS;
+}
+
+int64_t k3huf_encode_layer_lanes(const void* h_raw, uint64_t raw_bytes, uint32_t lane_syms, void* h_out,
+                                 uint64_t cap, int n_threads) {
+    if (!h_raw || !h_out || !raw_bytes || (raw_bytes & 1) || !lane_syms_ok(lane_syms)) return K3HUF_E_ARG;
+    if (uint64_t(k3huf_encode_bound_lanes(raw_bytes, lane_syms)) > cap) return K3HUF_E_ARG;
+    const uint32_t sub_syms = K3HUF_LANES * lane_syms;
     const uint8_t* raw = static_cast<const uint8_t*>(h_raw);
     uint8_t* out = static_cast<uint8_t*>(h_out);
     const int threads = pick_threads(n_threads);
@@ -333,8 +345,8 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
 
     // layout: every stripe's size is known from its histogram
     uint32_t nsb_total = 0;
-    const uint64_t total = k3huf_detail::layout(raw_bytes, hist.data(), len, g.data(), &nsb_total);
-    k3huf_detail::write_layer_header(out, raw_bytes, len, g.data(), nsb_total, total);
+    const uint64_t total = k3huf_detail::layout(raw_bytes, hist.data(), len, g.data(), &nsb_total, lane_syms);
+    k3huf_detail::write_layer_header(out, raw_bytes, len, g.data(), nsb_total, total, lane_syms);
 
     // stripes are independent (K3 page, "key design points"): pack in parallel
     parallel_for(int(ns), threads, [&](int s) {
@@ -346,7 +358,7 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
         wr(st + 4, G.n, 4);
         wr(st + 8, G.nbits, 4);
         wr(st + 12, G.bit_bytes, 4);
-        wr(st + 16, uint64_t(s) * (K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES), 4);
+        wr(st + 16, uint64_t(s) * (K3HUF_STRIPE_BYTES / (2ull * sub_syms)), 4);
         wr(st + 20, G.nsb, 4);
         wr(st + 24, G.bits_off, 4);
         wr(st + 28, G.even_off, 4);
@@ -359,13 +371,13 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
         size_t wbyte = 0;
         for (uint32_t b = 0; b < G.nsb; ++b) {
             uint8_t* rec = st + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * b;
-            const uint32_t i0 = b * K3HUF_SUBBLOCK_SYMS;
-            const uint32_t m = std::min<uint32_t>(K3HUF_SUBBLOCK_SYMS, G.n - i0);
+            const uint32_t i0 = b * sub_syms;
+            const uint32_t m = std::min<uint32_t>(sub_syms, G.n - i0);
             wr(rec, pos, 4);
             wr(rec + 4, m, 4);
             for (uint32_t t = 0; t < K3HUF_LANES; ++t) {
-                const uint32_t j0 = i0 + t * K3HUF_LANE_SYMS;
-                const uint32_t j1 = std::min<uint32_t>(j0 + K3HUF_LANE_SYMS, i0 + m);
+                const uint32_t j0 = i0 + t * lane_syms;
+                const uint32_t j1 = std::min<uint32_t>(j0 + lane_syms, i0 + m);
                 const uint64_t p0 = pos;
                 for (uint32_t i = j0; i < j1; ++i) {
                     const uint8_t v = p[2ull * i + 1];
@@ -386,6 +398,10 @@ int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, u
         if (nacc > 0) bits[wbyte++] = uint8_t(acc >> 56);
     });
     return int64_t(total);
+}
+
+int64_t k3huf_encode_layer(const void* h_raw, uint64_t raw_bytes, void* h_out, uint64_t cap, int n_threads) {
+    return k3huf_encode_layer_lanes(h_raw, raw_bytes, K3HUF_LANE_SYMS, h_out, cap, n_threads);
 }
 
 }  // extern "C"

@@ -33,16 +33,23 @@ struct StripeGeom {
     uint32_t raw, n, nsb, nbits, bit_bytes, bits_off, even_off;
 };
 
+// the lane-chunk lengths the format allows (K3HUF_LANE_SYMS and
+// K3HUF_LANE_SYMS_SHORT); a subblock holds K3HUF_LANES chunks
+inline bool lane_syms_ok(uint32_t lane_syms) {
+    return lane_syms == K3HUF_LANE_SYMS || lane_syms == K3HUF_LANE_SYMS_SHORT;
+}
+
 // Geometry of every stripe from the per-stripe histograms (hist[s * 256 + v])
-// and the code lengths; returns the container size. Fills g (caller storage
-// of stripes_for(raw_bytes) entries) and the subblock total. No allocation.
+// and the code lengths, for lane chunks of lane_syms symbols; returns the
+// container size. Fills g (caller storage of stripes_for(raw_bytes) entries)
+// and the subblock total. No allocation.
 uint64_t layout(uint64_t raw_bytes, const uint64_t* hist, const uint8_t* len, StripeGeom* g,
-                uint32_t* nsb_total);
+                uint32_t* nsb_total, uint32_t lane_syms = K3HUF_LANE_SYMS);
 
 // The layer header and stripe offset table (pad256(K3HUF_HDR_BYTES + 8 ns)
 // bytes, zero padded) into out, from the stripes_for(raw_bytes) entries of g.
 void write_layer_header(uint8_t* out, uint64_t raw_bytes, const uint8_t* len, const StripeGeom* g,
-                        uint32_t nsb_total, uint64_t total);
+                        uint32_t nsb_total, uint64_t total, uint32_t lane_syms = K3HUF_LANE_SYMS);
 
 }  // namespace k3huf_detail
 

@@ -24,6 +24,7 @@ DEV_HEADER, DEV_STRIPE, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 2, 4, 8, 16
 # names the C header declares, checked by the ABI test
 EXPORTS = ("k3huf_build_table", "k3huf_layer_info", "k3huf_decode_layer", "k3huf_decode_ring",
            "k3huf_decode_ring_host", "k3huf_encode_bound", "k3huf_encode_layer",
+           "k3huf_encode_bound_lanes", "k3huf_encode_layer_lanes", "k3huf_lane_syms_for",
            "k3huf_encode_work_bytes", "k3huf_encode_layer_dev", "k3huf_encode_layer_dev_static",
            "k3huf_stream_ref", "k3huf_strerror")
 STATIC_MAX_RAW = 1 << 32   # K3HUF_STATIC_MAX_RAW
@@ -38,7 +39,7 @@ class K3HufError(RuntimeError):
 class Info(ctypes.Structure):
     _fields_ = [("raw_bytes", ctypes.c_uint64), ("container_bytes", ctypes.c_uint64),
                 ("n_stripes", ctypes.c_uint32), ("n_subblocks", ctypes.c_uint32),
-                ("codelen", ctypes.c_uint8 * 256)]
+                ("codelen", ctypes.c_uint8 * 256), ("lane_syms", ctypes.c_uint32)]
 
 
 class RingLayer(ctypes.Structure):
@@ -84,6 +85,13 @@ def lib() -> ctypes.CDLL:
         L.k3huf_encode_bound.restype = ctypes.c_int64
         L.k3huf_encode_layer.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, ctypes.c_int]
         L.k3huf_encode_layer.restype = ctypes.c_int64
+        L.k3huf_encode_bound_lanes.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+        L.k3huf_encode_bound_lanes.restype = ctypes.c_int64
+        L.k3huf_encode_layer_lanes.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint32, vp, ctypes.c_uint64,
+                                               ctypes.c_int]
+        L.k3huf_encode_layer_lanes.restype = ctypes.c_int64
+        L.k3huf_lane_syms_for.argtypes = [ctypes.c_uint64]
+        L.k3huf_lane_syms_for.restype = ctypes.c_uint32
         L.k3huf_encode_work_bytes.argtypes = [ctypes.c_uint64]
         L.k3huf_encode_work_bytes.restype = ctypes.c_int64
         L.k3huf_encode_layer_dev.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp,
@@ -141,20 +149,27 @@ def layer_info(blob) -> dict:
     _check(lib().k3huf_layer_info(b.ctypes.data, b.size, ctypes.byref(info)), "k3huf_layer_info")
     return dict(raw_bytes=info.raw_bytes, container_bytes=info.container_bytes,
                 n_stripes=info.n_stripes, n_subblocks=info.n_subblocks,
-                codelen=np.frombuffer(bytes(info.codelen), np.uint8).copy())
+                codelen=np.frombuffer(bytes(info.codelen), np.uint8).copy(), lane_syms=info.lane_syms)
 
 
-def encode_bound(raw_bytes: int) -> int:
-    return _check(lib().k3huf_encode_bound(raw_bytes), "k3huf_encode_bound")
+def encode_bound(raw_bytes: int, lane_syms: int = 256) -> int:
+    return _check(lib().k3huf_encode_bound_lanes(raw_bytes, lane_syms), "k3huf_encode_bound_lanes")
 
 
-def encode_layer(raw, n_threads: int = 0) -> np.ndarray:
-    """Pack one bf16 layer (bytes) into a container (numpy uint8)."""
+def lane_syms_for(raw_bytes: int) -> int:
+    """The lane-chunk length the library picks for a layer of raw_bytes
+    (k3huf_lane_syms_for: 64 up to 16 MiB, else 256)."""
+    return int(lib().k3huf_lane_syms_for(raw_bytes))
+
+
+def encode_layer(raw, n_threads: int = 0, lane_syms: int = 256) -> np.ndarray:
+    """Pack one bf16 layer (bytes) into a container (numpy uint8) with lane
+    chunks of lane_syms symbols (256, or 64 for small layers)."""
     r = _u8(raw)
-    cap = encode_bound(r.size)
+    cap = encode_bound(r.size, lane_syms)
     out = np.empty(cap, np.uint8)
-    n = _check(lib().k3huf_encode_layer(r.ctypes.data, r.size, out.ctypes.data, cap, n_threads),
-               "k3huf_encode_layer")
+    n = _check(lib().k3huf_encode_layer_lanes(r.ctypes.data, r.size, lane_syms, out.ctypes.data, cap,
+                                              n_threads), "k3huf_encode_layer_lanes")
     return out[:n]
 
 

@@ -2,8 +2,9 @@
 // with g++ by tests/test_read_bounds.py: the same functions the kernel calls,
 // with the device qualifiers defined away.
 //
-// For stripe records the kernel accepts, over blob sizes up to 2^36 - 1 and
-// record offsets anywhere in the blob:
+// For stripe records the kernel accepts (in both lane-chunk layouts: 128
+// chunks of 256 or of 64 symbols per subblock), over blob sizes up to
+// 2^36 - 1 and record offsets anywhere in the blob:
 //   1. every clamped 16-byte bitstream read (fill path, dword index j >= -4)
 //      and 8-byte read (gather path, j >= -2) lies inside the stripe's record
 //      and planes, so inside [0, blob_bytes);
@@ -44,9 +45,13 @@ static int fail(const char* what, uint64_t blob, uint64_t soff, uint32_t n, uint
     return 1;
 }
 
+// symbols per subblock of the two lane-chunk layouts (128 chunks of 256 or
+// of 64 symbols)
+static const uint32_t kSubSyms[2] = {K3HUF_LANES * K3HUF_LANE_SYMS, K3HUF_LANES * K3HUF_LANE_SYMS_SHORT};
+
 static int check(uint64_t blob, uint64_t soff, uint32_t n, uint32_t n_bits, uint32_t bit_bytes, uint32_t bits_off,
-                 uint32_t even_off, long* accepted) {
-    const uint32_t nsb = (n + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
+                 uint32_t even_off, uint32_t sub_syms, long* accepted) {
+    const uint32_t nsb = (n + sub_syms - 1) / sub_syms;
     if (!stripe_planes_ok(blob, soff, n, nsb, n_bits, bit_bytes, bits_off, even_off)) return 0;
     ++*accepted;
     const int32_t dmax = stripe_read_dmax(bits_off, even_off, n);
@@ -104,7 +109,8 @@ int main() {
     for (uint64_t blob : blobs)
         for (uint32_t n : ns)
             for (int k = 0; k < 64; ++k) {
-                const uint32_t nsb = (n + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
+                const uint32_t sub_syms = kSubSyms[k & 1];
+                const uint32_t nsb = (n + sub_syms - 1) / sub_syms;
                 const uint64_t n_bits = n + below(uint64_t(K3HUF_MAXLEN - 1) * n + 1);
                 const uint64_t bit_bytes = pad16((n_bits + 7) / 8);
                 const uint64_t bits_off = pad256(K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * nsb);
@@ -115,14 +121,15 @@ int main() {
                                           below(blob - span + 1) & ~15ull};
                 for (uint64_t soff : where)
                     if (check(blob, soff, n, uint32_t(n_bits), uint32_t(bit_bytes), uint32_t(bits_off),
-                              uint32_t(even_off), &accepted))
+                              uint32_t(even_off), sub_syms, &accepted))
                         return 1;
             }
     // arbitrary records (any field values the checks let through)
     for (long t = 0; t < 4000000; ++t) {
         const uint64_t blob = 304 + below(kMaxBlob - 303);
         const uint32_t n = 1 + uint32_t(below(1u << 25));
-        const uint32_t nsb = (n + K3HUF_SUBBLOCK_SYMS - 1) / K3HUF_SUBBLOCK_SYMS;
+        const uint32_t sub_syms = kSubSyms[(t >> 3) & 1];
+        const uint32_t nsb = (n + sub_syms - 1) / sub_syms;
         const uint32_t bit_bytes = uint32_t(below(1ull << 32)) & ~15u;
         const uint32_t n_bits = uint32_t(below(uint64_t(8) * bit_bytes + 1 < (1ull << 32) ? uint64_t(8) * bit_bytes + 1
                                                                                          : (1ull << 32)));
@@ -132,15 +139,15 @@ int main() {
         const uint32_t even_off = uint32_t((t & 2) ? uint64_t(bits_off) + bit_bytes + (below(1ull << 12) & ~15ull)
                                                    : below(1ull << 32) & ~15ull);
         const uint64_t soff = (t & 4) ? below(blob) & ~15ull : (blob - (blob >> (1 + t % 30))) & ~15ull;
-        if (check(blob, soff, n, n_bits, bit_bytes, bits_off, even_off, &accepted)) return 1;
+        if (check(blob, soff, n, n_bits, bit_bytes, bits_off, even_off, sub_syms, &accepted)) return 1;
     }
     // a record that passes subblock_rec_in_blob ends inside the blob, for
-    // any offset and index the kernel can form (offsets below 2^36, j < 1024)
+    // any offset and index the kernel can form (offsets below 2^36, j < 4096)
     for (long t = 0; t < 4000000; ++t) {
         const uint64_t blob = 304 + below(kMaxBlob - 303);
         const uint64_t back = below(blob < (1ull << 20) ? blob : (1ull << 20));
         const uint64_t soff = (t & 1) ? below(blob) & ~15ull : (blob - back) & ~15ull;
-        const uint32_t j = uint32_t(below(1024));
+        const uint32_t j = uint32_t(below(4096));
         const bool nx = (t & 2) != 0;
         const uint64_t end = soff + K3HUF_STRIPE_HDR_BYTES + uint64_t(K3HUF_SUBBLOCK_REC_BYTES) * j +
                              K3HUF_SUBBLOCK_REC_BYTES + (nx ? 4 : 0);

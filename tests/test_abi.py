@@ -269,3 +269,38 @@ def test_stream_ref_rejects_bad_arguments_before_any_device_call():
     assert L.k3huf_stream_ref(good, 16, good + 4, 16, 1, 0, None) == k3huf.E_ARG
     assert L.k3huf_stream_ref(good, 16, good, 16, 0, 0, None) == k3huf.E_ARG        # grid
     assert L.k3huf_stream_ref(good, 16, good, 16, (1 << 20) + 1, 0, None) == k3huf.E_ARG
+
+
+@pytest.mark.parametrize("n_bytes", [2, 130, 16382, 16384, 16386, 3 * 16384 + 514, (1 << 20) + 6,
+                                     (1 << 26) + 3 * 16384 + 66])
+def test_packer_short_lane_chunks_equal_oracle(n_bytes):
+    """The host packer's 64-symbol lane-chunk layout equals the oracle's
+    container byte for byte, and layer_info reports its geometry."""
+    x = synth.small_random(n_bytes + 5, n_bytes)
+    got = k3huf.encode_layer(x, lane_syms=64)
+    want = O.encode_layer(x, 64)
+    assert got.size == want.size and (got == want).all()
+    info = k3huf.layer_info(got)
+    assert info["lane_syms"] == 64 and info["n_subblocks"] == -(-n_bytes // 16384)
+    assert k3huf.layer_info(k3huf.encode_layer(x))["lane_syms"] == 256
+    assert k3huf.encode_bound(n_bytes, 64) == O.encode_bound(n_bytes, 64) >= got.size
+
+
+def test_lane_syms_other_than_64_or_256_rejected():
+    x = synth.small_random(6, 4096)
+    L = k3huf.lib()
+    for bad in (0, 32, 128, 512):
+        assert L.k3huf_encode_bound_lanes(x.size, bad) == k3huf.E_ARG
+        with pytest.raises(k3huf.K3HufError):
+            k3huf.encode_layer(x, lane_syms=bad)
+    blob = k3huf.encode_layer(x, lane_syms=64).copy()
+    blob[16:20] = np.frombuffer(np.uint32(128).tobytes(), np.uint8)   # lane_syms 128
+    with pytest.raises(k3huf.K3HufError):
+        k3huf.layer_info(blob)
+
+
+def test_lane_syms_for_layer_sizes():
+    assert k3huf.lane_syms_for(2) == 64
+    assert k3huf.lane_syms_for(16 << 20) == 64
+    assert k3huf.lane_syms_for((16 << 20) + 2) == 256
+    assert k3huf.lane_syms_for(1_170_000_000) == 256
