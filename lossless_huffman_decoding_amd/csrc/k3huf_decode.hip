@@ -10,8 +10,9 @@
 //   - "key design points": each decoded symbol is the high byte at an odd
 //     offset; the raw even-plane byte goes back at the even offset before it.
 // How it is laid out on the GPU (not from the pages): one wave decodes one
-// half subblock (32 KiB of output); lane t decodes its lane chunk t (256
-// symbols) starting at the bit offset the subblock index gives it (the ECF8
+// half subblock (32 KiB of output, or 8 KiB in the layout of 64-symbol lane
+// chunks); lane t decodes its lane chunk t (256 or 64 symbols, as the layer
+// header says) starting at the bit offset the subblock index gives it (the ECF8
 // page, section 2.1, keeps such per-thread bit offsets beside its code); the
 // table lives in LDS; decoded bytes are staged in LDS so that the even-plane
 // loads and the output stores of a wave cover whole 128-byte lines.
@@ -30,15 +31,17 @@ namespace {
 // One 7-wave workgroup per CU (measured on the trunk layer: 7 waves per CU
 // ran 6% faster than 12, and 6, 8, 9 or 10 were in between; 4 or 5 cannot
 // hide the table lookups' latency). A work unit is half a subblock: 64 lane
-// chunks of 256 symbols, lane t decoding chunk t. Every HBM line is read or
-// written in one burst:
+// chunks of L symbols (256, or 64 for small layers), lane t decoding chunk t
+// in L / 64 phases of 64 symbols. Every HBM line is read or written in one
+// burst:
 //   - the unit's bitstream is copied into the wave's LDS buffer with
 //     coalesced 16-byte loads before its lanes decode (when a full unit's
 //     codes exceed the buffer, each lane gathers its own codes phase by
 //     phase instead; the layer's partial last unit is decoded in passes over
 //     consecutive lane ranges);
-//   - the even-plane bytes of all four phases (two whole 128-byte lines per
-//     chunk) are requested together into registers as the unit starts;
+//   - the even-plane bytes of all of a unit's phases (up to four: two whole
+//     128-byte lines per 256-symbol chunk) are requested together into
+//     registers as the unit starts;
 //   - each phase's 64 symbols per chunk are staged in LDS, so every output
 //     store instruction writes whole 128-byte lines.
 constexpr int kWaves = 7;
@@ -235,7 +238,7 @@ struct Unit {
     const uint8_t* even;   // this unit's even-plane bytes
     uint8_t* out;          // this unit's output bytes
     int dmax;              // last readable 16-byte unit (dwords from `bits`, within the stripe)
-    uint32_t nsyms;        // symbols in this unit (16384 unless last in stripe)
+    uint32_t nsyms;        // symbols in this unit (64 L unless last in stripe)
 };
 
 // Per-lane decode state across the phases of a unit.
