@@ -283,8 +283,7 @@ int64_t k3huf_encode_layer_lanes(const void* h_raw, uint64_t raw_bytes, uint32_t
  *   needs for raw_bytes of layer data (or K3HUF_E_ARG for an odd or zero size).
  * k3huf_encode_layer_dev -- the packer on the GPU: the bf16 layer in device
  * memory becomes, in device memory, the container k3huf_encode_layer writes
- * for the same bytes (byte for byte; lane chunks of 256 symbols: the GPU
- * packer writes only that layout). K3 page, "what was implemented": one
+ * for the same bytes (byte for byte). K3 page, "what was implemented": one
  * histogram and codelen[256] for the whole layer's odd bytes, MSB-first
  * Huffman bitstream per stripe, even plane raw; "canonical code assignment
  * and Kraft check": depths limited to 12 bits, longest-first canonical codes.
@@ -310,6 +309,15 @@ int64_t k3huf_encode_layer_lanes(const void* h_raw, uint64_t raw_bytes, uint32_t
 int64_t k3huf_encode_work_bytes(uint64_t raw_bytes);
 int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
                                void* d_work, uint64_t work_bytes, void* stream);
+/* The same for lane chunks of lane_syms symbols (256, or K3HUF_LANE_SYMS_SHORT
+ * = 64; any other value is K3HUF_E_ARG): the container
+ * k3huf_encode_layer_lanes writes, with cap >=
+ * k3huf_encode_bound_lanes(raw_bytes, lane_syms) and work_bytes >=
+ * k3huf_encode_work_bytes_lanes(raw_bytes, lane_syms) (the 64-symbol layout
+ * has four times as many packing units, so its work buffer is larger). */
+int64_t k3huf_encode_work_bytes_lanes(uint64_t raw_bytes, uint32_t lane_syms);
+int64_t k3huf_encode_layer_dev_lanes(const void* d_raw, uint64_t raw_bytes, uint32_t lane_syms, void* d_out,
+                                     uint64_t cap, void* d_work, uint64_t work_bytes, void* stream);
 
 /*
  * k3huf_encode_layer_dev_static -- k3huf_encode_layer_dev without any

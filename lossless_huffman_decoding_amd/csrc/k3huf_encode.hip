@@ -12,7 +12,8 @@
 // host from the GPU's histograms (they are 256-entry problems); the byte work
 // runs in three kernels:
 //   enc_hist   per-stripe histograms of the odd bytes;
-//   enc_pack   one wave per half subblock (64 lane chunks, one per lane): the
+//   enc_pack   one wave per half subblock (64 lane chunks of 256, or of 64
+//              symbols in the layout for small layers; one chunk per lane): the
 //              chunks' code bits, the unit's start bit from the units before
 //              it (a look-back), its codes packed in LDS and written out, its
 //              records, its even bytes and the stripe's zero padding; a
@@ -36,14 +37,23 @@ namespace {
 using k3huf_detail::pad256;
 using k3huf_detail::StripeGeom;
 
-constexpr uint32_t kChunksPerStripe = (K3HUF_STRIPE_BYTES / 2) / K3HUF_LANE_SYMS;   // 131072
 constexpr int kHistThreads = 1024;
 constexpr int kHistCopies = 32;        // sub-histograms per block (lane mod 32)
-constexpr uint32_t kSubPerStripe = K3HUF_STRIPE_BYTES / K3HUF_SUBBLOCK_BYTES;   // 1024
 constexpr int kPackWaves = 4;          // waves (units) per packing block
 constexpr int kPackWords = 2048;       // per-wave LDS bit buffer (8 KiB)
 constexpr uint32_t kUnitChunks = 64;   // lane chunks per packing unit
-constexpr uint32_t kUnitsPerStripe = kChunksPerStripe / kUnitChunks;
+
+// Geometry of a layer with lane chunks of L symbols (K3HUF_LANE_SYMS, or
+// K3HUF_LANE_SYMS_SHORT): a subblock holds K3HUF_LANES chunks, a packing unit
+// half of them, and a chunk is packed in L / 64 phases.
+template <uint32_t L>
+struct EGeo {
+    static constexpr uint32_t kChunksPerStripe = (K3HUF_STRIPE_BYTES / 2) / L;      // 131072 or 524288
+    static constexpr uint32_t kSubSyms = K3HUF_LANES * L;
+    static constexpr uint32_t kSubPerStripe = K3HUF_STRIPE_BYTES / (2 * kSubSyms);  // 1024 or 4096
+    static constexpr uint32_t kUnitsPerStripe = kChunksPerStripe / kUnitChunks;
+    static constexpr int kPhases = int(L) / 64;
+};
 
 // stripe geometry as the kernels read it
 struct StripeDev {
@@ -70,9 +80,9 @@ struct UnitEdges {
 // work buffer: per-stripe histograms (u64), stripe geometry, unit edges,
 // the units' look-back words (u64), then a status word and the packing
 // kernel's block ticket
-WorkLayout work_layout(uint64_t raw_bytes) {
+WorkLayout work_layout(uint64_t raw_bytes, uint32_t lane_syms = K3HUF_LANE_SYMS) {
     const uint64_t ns = k3huf_detail::stripes_for(raw_bytes);
-    const uint64_t n_chunks = (raw_bytes / 2 + K3HUF_LANE_SYMS - 1) / K3HUF_LANE_SYMS;
+    const uint64_t n_chunks = (raw_bytes / 2 + lane_syms - 1) / lane_syms;
     const uint64_t n_units = (n_chunks + 63) / 64;
     WorkLayout w;
     w.hist = 0;
@@ -200,10 +210,10 @@ __device__ __forceinline__ void look_store(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kPackPhases = 4;
-constexpr int kPhSyms = K3HUF_LANE_SYMS / kPackPhases;   // 64 symbols per chunk per phase
+constexpr int kPhSyms = 64;               // symbols per chunk per phase
 constexpr int kRowBytes = kPhSyms + 4;    // 64 odd bytes + 4: rows start in distinct LDS banks
 
+template <uint32_t L>
 __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, uint64_t raw_bytes,
                                                             uint64_t n_chunks, CodeTable ct,
                                                             const StripeDev* g, UnitEdges* edges,
@@ -225,19 +235,22 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     const uint64_t u = uint64_t(blk) * kPackWaves + wave;   // unit
     const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
     if (u >= n_units) return;
-    const uint32_t s = uint32_t(u / kUnitsPerStripe);
+    using EG = EGeo<L>;
+    constexpr int kPackPhases = EG::kPhases;
+    constexpr uint32_t kChunkRaw = 2 * L;   // raw bytes of a lane chunk
+    const uint32_t s = uint32_t(u / EG::kUnitsPerStripe);
     const StripeDev G = g[s];
     const uint64_t sbg = u / 2;                         // global subblock
     const uint32_t half = uint32_t(u & 1);
-    const uint32_t sbl = uint32_t(sbg % kSubPerStripe);  // subblock within the stripe
-    const uint64_t us0 = uint64_t(s) * kUnitsPerStripe;  // the stripe's first unit
+    const uint32_t sbl = uint32_t(sbg % EG::kSubPerStripe);  // subblock within the stripe
+    const uint64_t us0 = uint64_t(s) * EG::kUnitsPerStripe;  // the stripe's first unit
     const uint64_t c0 = u * kUnitChunks;                // first chunk of the unit
     const uint64_t c = c0 + lane;
     const bool has = c < n_chunks;
-    const uint8_t* uraw = raw + c0 * 2 * K3HUF_LANE_SYMS;
+    const uint8_t* uraw = raw + c0 * kChunkRaw;
     const uint64_t n_syms = raw_bytes / 2;
-    const bool tail = (c0 + kUnitChunks) * K3HUF_LANE_SYMS > n_syms;   // layer's last unit, partial
-    const int cnt = has ? int(min(uint64_t(K3HUF_LANE_SYMS), n_syms - c * K3HUF_LANE_SYMS)) : 0;
+    const bool tail = (c0 + kUnitChunks) * L > n_syms;   // layer's last unit, partial
+    const int cnt = has ? int(min(uint64_t(L), n_syms - c * L)) : 0;
 
     // phase ph's raw bytes: chunk i * 8 + sub, bytes [q * 16, q * 16 + 16) of
     // its phase (8 lanes per chunk phase of 128 raw bytes)
@@ -247,7 +260,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     auto load_into = [&](uint4* r, int ph) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            r[i] = *reinterpret_cast<const uint4*>(uraw + uint64_t(i * 8 + sub) * 512 + ph * 2 * kPhSyms + q * 16);
+            r[i] = *reinterpret_cast<const uint4*>(uraw + uint64_t(i * 8 + sub) * kChunkRaw + ph * 2 * kPhSyms + q * 16);
     };
     auto load_raw = [&](int ph) { load_into(rv, ph); };
 
@@ -268,14 +281,19 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
                            lens[o1 & 0xFFu] + lens[(o1 >> 8) & 0xFFu] + lens[(o1 >> 16) & 0xFFu] + lens[o1 >> 24];
             }
         };
-        load_into(ra, 3);
-        load_into(rb, 2);
-        count(ra);
-        load_into(ra, 1);
-        load_into(rv, 0);
-        count(rb);
-        count(ra);
-        count(rv);
+        if (kPackPhases == 4) {
+            load_into(ra, 3);
+            load_into(rb, 2);
+            count(ra);
+            load_into(ra, 1);
+            load_into(rv, 0);
+            count(rb);
+            count(ra);
+            count(rv);
+        } else {
+            load_into(rv, 0);
+            count(rv);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t p = part[i];
@@ -286,7 +304,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
             bits = (lane >> 3) == i ? x : bits;
         }
     } else {
-        for (int j = 0; j < cnt; ++j) bits += lens[uraw[uint64_t(lane) * 512 + 2 * j + 1]];
+        for (int j = 0; j < cnt; ++j) bits += lens[uraw[uint64_t(lane) * kChunkRaw + 2 * j + 1]];
     }
 
     // B. the unit's bits, published; the look-back's first window (64 units,
@@ -336,7 +354,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     // the stripe record (its first unit) and the stripe's total (its last);
     // false when the unit would pass the stripe's bits (its input changed
     // since the histogram): it then writes no bitstream words
-    const bool last_unit = u + 1 == n_units || (u + 1) % kUnitsPerStripe == 0;
+    const bool last_unit = u + 1 == n_units || (u + 1) % EG::kUnitsPerStripe == 0;
     uint32_t* words = reinterpret_cast<uint32_t*>(out + G.off + G.bits_off);
     auto records = [&]() -> bool {
         const uint32_t u1 = u0 + total;
@@ -346,10 +364,10 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
         if (u + 1 == n_units && half == 0) lane_bits[kUnitChunks + lane] = 0;
         if (half == 0 && lane == 0) {
             reinterpret_cast<uint32_t*>(rec)[0] = u0;
-            reinterpret_cast<uint32_t*>(rec)[1] = min(uint32_t(K3HUF_SUBBLOCK_SYMS), G.n - sbl * K3HUF_SUBBLOCK_SYMS);
+            reinterpret_cast<uint32_t*>(rec)[1] = min(EG::kSubSyms, G.n - sbl * EG::kSubSyms);
         }
         if (first_unit && lane < 8) {
-            const uint32_t hv[8] = {G.raw, G.n, G.nbits, G.bit_bytes, s * kSubPerStripe, G.nsb, G.bits_off, G.even_off};
+            const uint32_t hv[8] = {G.raw, G.n, G.nbits, G.bit_bytes, s * EG::kSubPerStripe, G.nsb, G.bits_off, G.even_off};
             uint32_t x = 0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) x = lane == k ? hv[k] : x;
@@ -395,7 +413,7 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
     if (staged)
         for (uint32_t i = lane; i <= nrel; i += 64) buf[i] = 0u;
     // the unit's even plane (stripe symbol index)
-    uint8_t* ueven = out + G.off + G.even_off + uint32_t(c0 % kChunksPerStripe) * K3HUF_LANE_SYMS;
+    uint8_t* ueven = out + G.off + G.even_off + uint32_t(c0 % EG::kChunksPerStripe) * L;
 
     const uint32_t b0 = (staged ? 0u : u0) + incl - bits;
     // in-place packing: the unit's first and last words when shared
@@ -501,12 +519,18 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
                 ev[i] = make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
                                    __builtin_amdgcn_perm(v.w, v.z, 0x06040200u));
             }
-            if (ph == 2) load_raw(3);
-            if (ph & 1) {
+            if (kPackPhases == 4 && ph == 2) load_raw(3);
+            if (kPackPhases == 1) {
+                // 64-byte chunks: eight consecutive chunks' even bytes are
+                // four whole 128-byte lines
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    *reinterpret_cast<uint2*>(ueven + (i * 8 + sub) * L + q * 8) = ev[i];
+            } else if (ph & 1) {
                 // both halves of each 128-byte even-plane line, back to back
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    uint8_t* e = ueven + (i * 8 + sub) * K3HUF_LANE_SYMS + (ph - 1) * kPhSyms + q * 8;
+                    uint8_t* e = ueven + (i * 8 + sub) * L + (ph - 1) * kPhSyms + q * 8;
                     *reinterpret_cast<uint2*>(e) = evp[i];
                     *reinterpret_cast<uint2*>(e + kPhSyms) = ev[i];
                 }
@@ -522,9 +546,9 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
 #pragma unroll 1
         for (int ph = 0; ph < kPackPhases; ++ph) {
             for (int j = ph * kPhSyms; j < min(cnt, (ph + 1) * kPhSyms); ++j) {
-                const uint8_t* p = uraw + uint64_t(lane) * 512 + 2 * j;
+                const uint8_t* p = uraw + uint64_t(lane) * kChunkRaw + 2 * j;
                 row[lane * kRowBytes + (j - ph * kPhSyms)] = p[1];
-                ueven[lane * K3HUF_LANE_SYMS + j] = p[0];
+                ueven[lane * L + j] = p[0];
             }
             wave_sync();
             pack_phase(ph);
@@ -573,7 +597,9 @@ __global__ __launch_bounds__(kPackWaves * 64) void enc_pack(const uint8_t* raw, 
 // (a unit clears its last word when it ends inside it), so the parts are
 // OR-ed onto zero; OR-ing also gives the right word when a unit's first and
 // last words are one word.
+template <uint32_t L>
 __global__ void enc_edges(const UnitEdges* edges, uint64_t n_units, const StripeDev* g, uint8_t* out) {
+    constexpr uint32_t kUnitsPerStripe = EGeo<L>::kUnitsPerStripe;
     const uint64_t u = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (u >= n_units) return;
     const UnitEdges e = edges[u];
@@ -669,15 +695,16 @@ int resident_blocks(K kernel, int threads) {
     return cus * per;
 }
 
-// One encode: device layer raw -> container out, with the device work buffer
-// `work` (work_layout(raw_bytes).total bytes), host staging `host`
+// One encode: device layer raw -> container out with lane chunks of
+// lane_syms symbols, with the device work buffer `work`
+// (work_layout(raw_bytes, lane_syms).total bytes), host staging `host`
 // (host_stage_layout(ns).total bytes) and stripe geometry storage g (ns
 // entries). Allocates nothing; synchronous.
-int64_t encode_dev(const uint8_t* raw, uint64_t raw_bytes, uint8_t* out, uint64_t cap, uint8_t* work,
-                   hipStream_t st, uint8_t* host, StripeGeom* g) {
-    const WorkLayout wl = work_layout(raw_bytes);
+int64_t encode_dev(const uint8_t* raw, uint64_t raw_bytes, uint32_t lane_syms, uint8_t* out, uint64_t cap,
+                   uint8_t* work, hipStream_t st, uint8_t* host, StripeGeom* g) {
+    const WorkLayout wl = work_layout(raw_bytes, lane_syms);
     const uint32_t ns = k3huf_detail::stripes_for(raw_bytes);
-    const uint64_t n_chunks = (raw_bytes / 2 + K3HUF_LANE_SYMS - 1) / K3HUF_LANE_SYMS;
+    const uint64_t n_chunks = (raw_bytes / 2 + lane_syms - 1) / lane_syms;
     auto* hist = reinterpret_cast<unsigned long long*>(work + wl.hist);
     auto* geom = reinterpret_cast<StripeDev*>(work + wl.geom);
     auto* look = reinterpret_cast<uint64_t*>(work + wl.look);
@@ -715,9 +742,9 @@ int64_t encode_dev(const uint8_t* raw, uint64_t raw_bytes, uint8_t* out, uint64_
     CodeTable ct;
     for (int v = 0; v < 256; ++v) ct.e[v] = (uint32_t(len[v]) << 16) | code[v];
     uint32_t nsb_total = 0;
-    const uint64_t total = k3huf_detail::layout(raw_bytes, h, len, g, &nsb_total);
+    const uint64_t total = k3huf_detail::layout(raw_bytes, h, len, g, &nsb_total, lane_syms);
     if (total > cap) return K3HUF_E_ARG;
-    k3huf_detail::write_layer_header(host_hdr, raw_bytes, len, g, nsb_total, total);
+    k3huf_detail::write_layer_header(host_hdr, raw_bytes, len, g, nsb_total, total, lane_syms);
     for (uint32_t s = 0; s < ns; ++s)
         gd[s] = StripeDev{g[s].raw0, g[s].off, g[s].raw, g[s].n, g[s].nsb, g[s].nbits,
                           g[s].bit_bytes, g[s].bits_off, g[s].even_off, 0u};
@@ -727,11 +754,16 @@ int64_t encode_dev(const uint8_t* raw, uint64_t raw_bytes, uint8_t* out, uint64_
         hipMemcpyAsync(geom, gd, size_t(ns) * sizeof(StripeDev), hipMemcpyHostToDevice, st) != hipSuccess)
         return K3HUF_E_HIP;
     const uint64_t n_units = (n_chunks + kUnitChunks - 1) / kUnitChunks;
-    hipLaunchKernelGGL(enc_pack, dim3(unsigned((n_units + kPackWaves - 1) / kPackWaves)),
-                       dim3(kPackWaves * 64), 0, st, raw, raw_bytes, n_chunks, ct, geom, edges, look,
-                       status + 1, status, out);
-    hipLaunchKernelGGL(enc_edges, dim3(unsigned((n_units + 255) / 256)), dim3(256), 0, st, edges,
-                       n_units, geom, out);
+    const dim3 pack_grid(unsigned((n_units + kPackWaves - 1) / kPackWaves)), edge_grid(unsigned((n_units + 255) / 256));
+    if (lane_syms == K3HUF_LANE_SYMS_SHORT) {
+        hipLaunchKernelGGL(enc_pack<K3HUF_LANE_SYMS_SHORT>, pack_grid, dim3(kPackWaves * 64), 0, st, raw, raw_bytes,
+                           n_chunks, ct, geom, edges, look, status + 1, status, out);
+        hipLaunchKernelGGL(enc_edges<K3HUF_LANE_SYMS_SHORT>, edge_grid, dim3(256), 0, st, edges, n_units, geom, out);
+    } else {
+        hipLaunchKernelGGL(enc_pack<K3HUF_LANE_SYMS>, pack_grid, dim3(kPackWaves * 64), 0, st, raw, raw_bytes,
+                           n_chunks, ct, geom, edges, look, status + 1, status, out);
+        hipLaunchKernelGGL(enc_edges<K3HUF_LANE_SYMS>, edge_grid, dim3(256), 0, st, edges, n_units, geom, out);
+    }
     if (launched()) return K3HUF_E_HIP;
     if (hipMemcpyAsync(host_status, status, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
@@ -741,11 +773,13 @@ int64_t encode_dev(const uint8_t* raw, uint64_t raw_bytes, uint8_t* out, uint64_
     return (bad & 2u) ? K3HUF_E_HIP : bad ? K3HUF_E_CORRUPT : int64_t(total);
 }
 
-// Argument checks shared by the two entry points (sizes, alignment, capacity).
-bool encode_args_ok(const void* d_raw, uint64_t raw_bytes, const void* d_out, uint64_t cap) {
-    if (!d_raw || !d_out || !raw_bytes || (raw_bytes & 1)) return false;
+// Argument checks shared by the entry points (sizes, alignment, lane-chunk
+// length, capacity).
+bool encode_args_ok(const void* d_raw, uint64_t raw_bytes, const void* d_out, uint64_t cap,
+                    uint32_t lane_syms = K3HUF_LANE_SYMS) {
+    if (!d_raw || !d_out || !raw_bytes || (raw_bytes & 1) || !k3huf_detail::lane_syms_ok(lane_syms)) return false;
     if ((reinterpret_cast<uintptr_t>(d_raw) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15)) return false;
-    const int64_t bound = k3huf_encode_bound(raw_bytes);
+    const int64_t bound = k3huf_encode_bound_lanes(raw_bytes, lane_syms);
     return bound >= 0 && uint64_t(bound) <= cap;
 }
 
@@ -771,23 +805,33 @@ uint8_t* g_scratch_ptr[kMaxDevices] = {};  // per device: the address of `scratc
 
 extern "C" {
 
-int64_t k3huf_encode_work_bytes(uint64_t raw_bytes) {
-    if (!raw_bytes || (raw_bytes & 1)) return K3HUF_E_ARG;
-    return int64_t(work_layout(raw_bytes).total);
+int64_t k3huf_encode_work_bytes_lanes(uint64_t raw_bytes, uint32_t lane_syms) {
+    if (!raw_bytes || (raw_bytes & 1) || !k3huf_detail::lane_syms_ok(lane_syms)) return K3HUF_E_ARG;
+    return int64_t(work_layout(raw_bytes, lane_syms).total);
 }
 
-int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
-                               void* d_work, uint64_t work_bytes, void* stream) {
-    if (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 15) || !encode_args_ok(d_raw, raw_bytes, d_out, cap))
+int64_t k3huf_encode_work_bytes(uint64_t raw_bytes) {
+    return k3huf_encode_work_bytes_lanes(raw_bytes, K3HUF_LANE_SYMS);
+}
+
+int64_t k3huf_encode_layer_dev_lanes(const void* d_raw, uint64_t raw_bytes, uint32_t lane_syms, void* d_out,
+                                     uint64_t cap, void* d_work, uint64_t work_bytes, void* stream) {
+    if (!d_work || (reinterpret_cast<uintptr_t>(d_work) & 15) ||
+        !encode_args_ok(d_raw, raw_bytes, d_out, cap, lane_syms))
         return K3HUF_E_ARG;
-    if (work_bytes < work_layout(raw_bytes).total) return K3HUF_E_ARG;
+    if (work_bytes < work_layout(raw_bytes, lane_syms).total) return K3HUF_E_ARG;
     const uint32_t ns = k3huf_detail::stripes_for(raw_bytes);
     PinnedLease pin(host_stage_layout(ns).total);
     if (!pin.p) return K3HUF_E_HIP;
     std::vector<StripeGeom> g(ns);
-    return encode_dev(static_cast<const uint8_t*>(d_raw), raw_bytes, static_cast<uint8_t*>(d_out), cap,
+    return encode_dev(static_cast<const uint8_t*>(d_raw), raw_bytes, lane_syms, static_cast<uint8_t*>(d_out), cap,
                       static_cast<uint8_t*>(d_work), static_cast<hipStream_t>(stream),
                       static_cast<uint8_t*>(pin.p), g.data());
+}
+
+int64_t k3huf_encode_layer_dev(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
+                               void* d_work, uint64_t work_bytes, void* stream) {
+    return k3huf_encode_layer_dev_lanes(d_raw, raw_bytes, K3HUF_LANE_SYMS, d_out, cap, d_work, work_bytes, stream);
 }
 
 int64_t k3huf_encode_layer_dev_static(const void* d_raw, uint64_t raw_bytes, void* d_out, uint64_t cap,
@@ -806,8 +850,8 @@ int64_t k3huf_encode_layer_dev_static(const void* d_raw, uint64_t raw_bytes, voi
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return K3HUF_E_HIP;
         g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
     }
-    return encode_dev(static_cast<const uint8_t*>(d_raw), raw_bytes, static_cast<uint8_t*>(d_out), cap,
-                      g_scratch_ptr[dev], static_cast<hipStream_t>(stream), g_static_host, g_static_geom);
+    return encode_dev(static_cast<const uint8_t*>(d_raw), raw_bytes, K3HUF_LANE_SYMS, static_cast<uint8_t*>(d_out),
+                      cap, g_scratch_ptr[dev], static_cast<hipStream_t>(stream), g_static_host, g_static_geom);
 }
 
 }  // extern "C"

@@ -25,7 +25,8 @@ DEV_HEADER, DEV_STRIPE, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 2, 4, 8, 16
 EXPORTS = ("k3huf_build_table", "k3huf_layer_info", "k3huf_decode_layer", "k3huf_decode_ring",
            "k3huf_decode_ring_host", "k3huf_encode_bound", "k3huf_encode_layer",
            "k3huf_encode_bound_lanes", "k3huf_encode_layer_lanes", "k3huf_lane_syms_for",
-           "k3huf_encode_work_bytes", "k3huf_encode_layer_dev", "k3huf_encode_layer_dev_static",
+           "k3huf_encode_work_bytes", "k3huf_encode_layer_dev", "k3huf_encode_work_bytes_lanes",
+           "k3huf_encode_layer_dev_lanes", "k3huf_encode_layer_dev_static",
            "k3huf_stream_ref", "k3huf_strerror")
 STATIC_MAX_RAW = 1 << 32   # K3HUF_STATIC_MAX_RAW
 
@@ -97,6 +98,11 @@ def lib() -> ctypes.CDLL:
         L.k3huf_encode_layer_dev.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp,
                                              ctypes.c_uint64, vp]
         L.k3huf_encode_layer_dev.restype = ctypes.c_int64
+        L.k3huf_encode_work_bytes_lanes.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+        L.k3huf_encode_work_bytes_lanes.restype = ctypes.c_int64
+        L.k3huf_encode_layer_dev_lanes.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint32, vp, ctypes.c_uint64, vp,
+                                                   ctypes.c_uint64, vp]
+        L.k3huf_encode_layer_dev_lanes.restype = ctypes.c_int64
         L.k3huf_encode_layer_dev_static.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp]
         L.k3huf_encode_layer_dev_static.restype = ctypes.c_int64
         L.k3huf_stream_ref.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
@@ -173,24 +179,25 @@ def encode_layer(raw, n_threads: int = 0, lane_syms: int = 256) -> np.ndarray:
     return out[:n]
 
 
-def encode_work_bytes(raw_bytes: int) -> int:
-    return _check(lib().k3huf_encode_work_bytes(raw_bytes), "k3huf_encode_work_bytes")
+def encode_work_bytes(raw_bytes: int, lane_syms: int = 256) -> int:
+    return _check(lib().k3huf_encode_work_bytes_lanes(raw_bytes, lane_syms), "k3huf_encode_work_bytes_lanes")
 
 
-def encode_layer_dev(d_raw, d_out=None, d_work=None, stream=None):
-    """Pack the bf16 layer in device uint8 tensor ``d_raw`` on the GPU.
-    ``d_out`` (device uint8, at least encode_bound bytes) and ``d_work``
-    (device uint8, at least encode_work_bytes) are allocated when None.
-    Returns the container as a view of d_out (synchronous call)."""
+def encode_layer_dev(d_raw, d_out=None, d_work=None, stream=None, lane_syms: int = 256):
+    """Pack the bf16 layer in device uint8 tensor ``d_raw`` on the GPU, with
+    lane chunks of lane_syms symbols (256, or 64). ``d_out`` (device uint8, at
+    least encode_bound bytes) and ``d_work`` (device uint8, at least
+    encode_work_bytes) are allocated when None. Returns the container as a
+    view of d_out (synchronous call)."""
     import torch
     n = _nbytes(d_raw)
     if d_out is None:
-        d_out = torch.empty(encode_bound(n), dtype=torch.uint8, device=d_raw.device)
+        d_out = torch.empty(encode_bound(n, lane_syms), dtype=torch.uint8, device=d_raw.device)
     if d_work is None:
-        d_work = torch.empty(encode_work_bytes(n), dtype=torch.uint8, device=d_raw.device)
-    size = _check(lib().k3huf_encode_layer_dev(d_raw.data_ptr(), n, d_out.data_ptr(), _nbytes(d_out),
-                                               d_work.data_ptr(), _nbytes(d_work),
-                                               _stream_handle(stream)), "k3huf_encode_layer_dev")
+        d_work = torch.empty(encode_work_bytes(n, lane_syms), dtype=torch.uint8, device=d_raw.device)
+    size = _check(lib().k3huf_encode_layer_dev_lanes(d_raw.data_ptr(), n, lane_syms, d_out.data_ptr(),
+                                                     _nbytes(d_out), d_work.data_ptr(), _nbytes(d_work),
+                                                     _stream_handle(stream)), "k3huf_encode_layer_dev_lanes")
     return d_out[:size]
 
 

@@ -6,8 +6,9 @@ decompression buffer the size of the largest layer, and decodes a layer's
 weights into it from a forward pre-hook just before the layer runs. This
 module does that with this library's codec. A group of modules (a trunk
 layer: the K3 page packs each layer's tensors together, with one code table
-per layer) is packed on the GPU as one container (k3huf_encode_layer_dev) of
-its weights laid end to end; only the container and its 4096-entry table stay
+per layer) is packed on the GPU as one container (k3huf_encode_layer_dev_lanes,
+in the lane-chunk layout k3huf_lane_syms_for picks for its size) of its
+weights laid end to end; only the container and its 4096-entry table stay
 resident. When a member module is about to run, its group is decoded (once)
 into a buffer and every member's weight becomes a view of its slice.
 
@@ -91,7 +92,10 @@ class OnDemandWeights:
             parts.append(raw)
             off += raw.numel()
         raw = parts[0] if len(parts) == 1 else torch.cat(parts)
-        blob = k3huf.encode_layer_dev(raw).clone()   # trimmed copy; the bound-sized output is freed
+        # the lane-chunk layout by the library's rule (64-symbol chunks for
+        # containers of up to 16 MiB, whose decode is one lane's chain of
+        # lookups); trimmed copy, the bound-sized output is freed
+        blob = k3huf.encode_layer_dev(raw, lane_syms=k3huf.lane_syms_for(raw.numel())).clone()
         del raw, parts
         info = k3huf.layer_info(blob[: k3huf.HDR_BYTES].cpu().numpy())
         lut = torch.from_numpy(k3huf.build_table(info["codelen"]).view(np.int16)).to(self.device)

@@ -304,3 +304,12 @@ def test_lane_syms_for_layer_sizes():
     assert k3huf.lane_syms_for(16 << 20) == 64
     assert k3huf.lane_syms_for((16 << 20) + 2) == 256
     assert k3huf.lane_syms_for(1_170_000_000) == 256
+
+
+def test_gpu_packer_lane_syms_checked_before_any_device_call():
+    L = k3huf.lib()
+    good = 1 << 12
+    for bad in (0, 32, 128):
+        assert L.k3huf_encode_work_bytes_lanes(1024, bad) == k3huf.E_ARG
+        assert L.k3huf_encode_layer_dev_lanes(good, 1024, bad, good, 1 << 20, good, 1 << 20, None) == k3huf.E_ARG
+    assert k3huf.encode_work_bytes(1 << 20, 64) > k3huf.encode_work_bytes(1 << 20)

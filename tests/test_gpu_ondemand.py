@@ -9,7 +9,7 @@ prints its name before touching the GPU.
 import pytest
 import torch
 
-from lossless_huffman_decoding_amd import synth
+from lossless_huffman_decoding_amd import k3huf, synth
 from lossless_huffman_decoding_amd.ondemand import OnDemandWeights
 
 pytestmark = pytest.mark.gpu
@@ -55,6 +55,9 @@ def test_on_demand_forward_equals_dense(batch, lookahead, n_layers):
         od.attach(m)
     assert od.buffer_bytes == max(o * i for o, i in shapes) * 2 * (2 if lookahead else 1)
     assert od.resident_bytes < sum(o * i for o, i in shapes) * 2
+    # modules of a few MB get the 64-symbol lane-chunk layout
+    assert all(k3huf.layer_info(g["blob"][: k3huf.HDR_BYTES].cpu().numpy())["lane_syms"] == 64
+               for g in od._groups)
     say("ondemand hooked forward", batch, lookahead, n_layers)
     with torch.no_grad():
         got = model(x)

@@ -152,3 +152,72 @@ def test_ring_mixes_layouts():
     assert int(status.item()) == 0
     for k in range(len(xs)):
         assert (results[k].cpu().numpy() == xs[k]).all(), k
+
+
+# ---------------------------------------------------------------------------
+# the GPU packer in the 64-symbol layout
+
+def gpu_encode64(x, d_out=None, d_work=None):
+    d_x = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    if d_out is None:   # non-zero patterns: a byte the kernels fail to write shows up
+        d_out = torch.full((k3huf.encode_bound(x.size, 64),), 0x5A, dtype=torch.uint8, device=DEV)
+        d_work = torch.full((k3huf.encode_work_bytes(x.size, 64),), 0xC3, dtype=torch.uint8, device=DEV)
+    return k3huf.encode_layer_dev(d_x, d_out, d_work, lane_syms=64), d_x
+
+
+@pytest.mark.parametrize("n_bytes", [2, 4, 126, 128, 130, 8190, 8192, 8194, 16382, 16384, 16386,
+                                     3 * 16384 + 514, 64 * 16384 - 2, (1 << 26) - 2, 1 << 26,
+                                     (1 << 26) + 3 * 16384 + 18])
+def test_gpu_packer_sizes_match_oracle(n_bytes):
+    x = synth.small_random(n_bytes + 17, n_bytes)
+    want = O.encode_layer(x, 64)
+    say("short lanes GPU packer", n_bytes)
+    got, _ = gpu_encode64(x)
+    got = got.cpu().numpy()
+    assert got.size == want.size and (got == want).all()
+
+
+@pytest.mark.parametrize("layer", ["tiny", "edge_fib40", "edge_single", "edge_uniform"])
+def test_gpu_packer_configs_match_oracle(layer):
+    gen = {"tiny": synth.tiny, **dict(synth.CONFIGS["edge"])}[layer]
+    x = gen()
+    want = O.encode_layer(x, 64)
+    say("short lanes GPU packer config", layer)
+    got, _ = gpu_encode64(x)
+    got = got.cpu().numpy()
+    assert got.size == want.size and (got == want).all()
+
+
+def test_gpu_packer_mixed_spans_and_round_trip():
+    """Uniform-byte spans (8-bit codes) among weight spans over three stripes,
+    then decoded back on the GPU."""
+    x = synth.mixed_spans(80, (2 << 26) + 3 * 16384 + 1234)
+    want = O.encode_layer(x, 64)
+    say("short lanes GPU packer mixed", x.size)
+    got, d_x = gpu_encode64(x)
+    assert got.numel() == want.size and (got.cpu().numpy() == want).all()
+    out, st = gpu_decode(got.cpu().numpy())
+    assert st == 0 and torch.equal(out, d_x)
+
+
+def test_gpu_packer_reuses_buffers():
+    big = synth.small_random(903, 5 * 16384 + 66)
+    small = synth.small_random(904, 2 * 16384 + 10)
+    d_out = torch.full((k3huf.encode_bound(big.size, 64),), 0x5A, dtype=torch.uint8, device=DEV)
+    d_work = torch.full((k3huf.encode_work_bytes(big.size, 64),), 0xC3, dtype=torch.uint8, device=DEV)
+    say("short lanes GPU packer reuse")
+    a, _ = gpu_encode64(big, d_out, d_work)
+    a = a.cpu().numpy()
+    b, _ = gpu_encode64(small, d_out, d_work)
+    b = b.cpu().numpy()
+    assert (a == O.encode_layer(big, 64)).all()
+    assert (b == O.encode_layer(small, 64)).all()
+
+
+def test_gpu_packer_trunk_layer_equals_host_packer():
+    x = synth.trunk_layer()
+    say("short lanes GPU packer trunk", x.size)
+    got, d_x = gpu_encode64(x)
+    want = k3huf.encode_layer(x, lane_syms=64)
+    assert got.numel() == want.size
+    assert torch.equal(got, torch.from_numpy(want).to(DEV))
