@@ -59,15 +59,18 @@ constexpr int kLdsStatic = kWaveOff + kWaves * kWaveLds;
 static_assert(kLdsStatic + 16 + E8HUF_LUT_MAX * 2 <= 163840, "LDS budget, with the largest two-level table");
 
 // 12-bit table entry:
-//   [23:0]  up to three exponent symbols, one per byte, first code lowest
-//   [25:24] symbols in the entry (0 for an escape)
-//   [29:26] bits the entry's codes take (0..12)
-//   [30]    no code covers the prefix (decoded as one bad 12-bit code)
-//   [31]    escape: the first code is longer than 12 bits; [7:0] holds its
-//           level-2 table
-constexpr uint32_t kEsc = 1u << 31;
-constexpr uint32_t kBadE = 1u << 30;
-__device__ __forceinline__ uint32_t e_count(uint32_t e) { return (e >> 24) & 3u; }
+//   [23:0]  up to three exponent symbols, one per byte, first code lowest;
+//           each already shifted left by the mantissa width, so it is the
+//           FP8 byte's exponent field in place
+//   [27:24] symbols in the entry
+//   [31:28] bits the entry's codes take (1..12)
+// count and length are both 4-bit fields, so one field width (4, or 0 for a
+// lane that has its symbols) masks both extractions. An escape entry (the
+// first code is longer than 12 bits, or no code covers the prefix) has
+// count and length 0 and holds in [7:0] the level-2 table of its first 8
+// bits plus one (0: no code).
+constexpr uint32_t kBadE = 1u << 7;   // in Lane::bad: a code that no table covers
+constexpr uint32_t kCntPos = 24, kLenPos = 28;
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -116,24 +119,21 @@ __device__ __forceinline__ uint32_t two_level(const uint16_t* l2, uint32_t l2_la
 }
 
 // 12-bit table entry for prefix i: up to three whole codes of the 12 bits.
-__device__ uint32_t make_entry(const uint16_t* l2, uint32_t l2_last, uint32_t i) {
+__device__ uint32_t make_entry(const uint16_t* l2, uint32_t l2_last, uint32_t i, uint32_t m) {
     uint32_t syms = 0, k = 0, pos = 0;
     const uint32_t first = two_level(l2, l2_last, i << 4);
-    if ((first & 31u) == 0u) return kBadE | (1u << 24) | (12u << 26);   // no code: one bad 12-bit code
-    if ((first & 31u) > 12u) {
-        const uint32_t t = l2[i >> 4] >> 8;   // the level-1 link of the first 8 bits
-        return kEsc | t;
-    }
+    if ((first & 31u) == 0u) return 0u;   // no code
+    if ((first & 31u) > 12u) return (l2[i >> 4] >> 8) + 1u;   // the level-1 link of the first 8 bits
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
         const uint32_t e = two_level(l2, l2_last, ((i << pos) & 0xFFFu) << 4);
         const uint32_t l = e & 31u;
         if (l == 0u || pos + l > 12u) break;
-        syms |= (e >> 8) << (8 * k);
+        syms |= ((e >> 8) << m) << (8 * k);
         ++k;
         pos += l;
     }
-    return syms | (k << 24) | (pos << 26);
+    return syms | (k << kCntPos) | (pos << kLenPos);
 }
 
 // 64-bit window whose top bit is the bit after buffer bit pm1 (buffer dwords
@@ -149,30 +149,38 @@ __device__ __forceinline__ uint64_t window(const uint32_t* buf, uint32_t pm1) {
 struct Lane {
     uint32_t pm1;      // buffer bit index of the next code, minus one
     uint32_t cnt;      // symbols decoded so far (may pass the lane's count by two)
-    uint32_t last;     // the last entry that yielded symbols
-    uint32_t bad;      // OR of the entries taken (bit 30: a prefix no code covers)
+    uint32_t bad;      // kBadE: a code the second-level table does not cover
+    uint32_t m;        // staged symbols are exponents shifted left by m (mantissa bits)
 };
 
 // Decode of a lane's symbols [base, target) into its stage row (byte i of the
 // row is symbol base + i). Each 64-bit window feeds kLookups lookups of the
 // 12-bit table; an entry's symbols are written as three bytes at the lane's
-// count (bytes past the entry's symbols are overwritten by the next lookup or
-// lie past the phase). A lane that has its symbols takes zero entries until
-// the wave's slowest lane is done. An escape entry (the first code is longer
-// than 12 bits) yields nothing, so the lane stays on that code for the rest
-// of the window; after the window, lanes on an escape take that one code
-// through the second-level table. Every window either yields a symbol on each
-// live lane or resolves an escape, so 2 * 64 windows always finish a phase.
-// A lookup that ends past the phase leaves up to two symbols in the row's
-// spare bytes; they move to the start of the next phase's row.
+// write position p (bytes past the entry's symbols are overwritten by the
+// next lookup or lie past the phase). A lane that has its symbols takes zero
+// entries until the wave's slowest lane is done; their zero bytes land after
+// its last symbol. An escape entry (the first code is longer than 12 bits)
+// yields nothing, so the lane stays on that code for the rest of the window;
+// after the window, lanes on an escape take that one code through the
+// second-level table. Every window either yields a symbol on each live lane
+// or resolves an escape, so 2 * 64 windows always finish a phase. A lookup
+// that ends past the phase leaves up to two symbols in the row's bytes
+// kPhase and kPhase + 1; they move to the start of the next phase's row. A
+// lane with nothing to decode in the phase writes only to the spare bytes.
 __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint16_t* l2, uint32_t l2_last,
                                              const uint32_t* buf, uint8_t* row, uint32_t target, uint32_t base,
                                              Lane& ls) {
-    if (ls.cnt > base) {   // symbols the previous phase's last lookup carried over
-        const uint32_t k = e_count(ls.last), j = ls.cnt - base;
-        row[0] = uint8_t(ls.last >> (8 * (k - j)));
-        row[1] = uint8_t(ls.last >> (8 * (k - j + 1)));
+    const bool act = target > base;
+    uint8_t* p = row + kSpare;
+    if (act) {
+        const uint32_t j = ls.cnt - base;   // 0..2 symbols carried over
+        if (j) {
+            row[0] = row[kPhase];
+            row[1] = row[kPhase + 1];
+        }
+        p = row + j;
     }
+    uint8_t* const pend = act ? row + (target - base) : p;
     // each lookup's three bytes are written after the next table read has
     // been issued (a wave's LDS operations complete in order, so that read
     // waits for no write); the first pending write is a dummy in the spare
@@ -181,53 +189,51 @@ __device__ __forceinline__ void decode_phase(const uint32_t* tab, const uint16_t
     uint32_t we = 0;
 #pragma unroll 1
     for (int win = 0; win < 2 * kPhase; ++win) {
-        if (!__any(ls.cnt < target)) break;
+        if (!__any(p < pend)) break;
         uint64_t acc = window(buf, ls.pm1);
-        uint32_t fl = 0;
+        uint32_t t = 0;
 #pragma unroll
         for (int q = 0; q < kLookups; ++q) {
             const uint32_t e = tab[uint32_t(acc >> 52)];
             wp[0] = uint8_t(we);
             wp[1] = uint8_t(we >> 8);
             wp[2] = uint8_t(we >> 16);
-            // a lane that has its symbols takes a zero entry: its field
-            // widths are zero, so the mask stays off the chain of reads
-            const bool live = ls.cnt < target;
-            const uint32_t t = __builtin_amdgcn_ubfe(e, 26u, live ? 4u : 0u);
-            const uint32_t ez = live ? e : 0u;
-            fl |= ez;
-            // lanes past the phase (or before it) write to the row's spare bytes
-            wp = row + min(ls.cnt - base, kSpare);
-            we = ez;
-            const uint32_t k = e_count(ez);
-            ls.last = k ? ez : ls.last;
-            ls.cnt += k;
+            // a lane that has its symbols extracts zero-width fields: no
+            // bits, no symbols, and the mask stays off the chain of reads;
+            // its entry's bytes go after its last symbol
+            const uint32_t w = p < pend ? 4u : 0u;
+            t = __builtin_amdgcn_ubfe(e, kLenPos, w);
+            wp = p;
+            we = e;
+            p += __builtin_amdgcn_ubfe(e, kCntPos, w);
             ls.pm1 += t;
             acc <<= t;
         }
-        ls.bad |= fl;
-        if (__any(fl & kEsc)) {
+        // a live lane's lookup takes no bits only on an escape entry, which
+        // it then repeats to the end of the window; at most 48 of the
+        // window's bits were taken before it, so the window still holds the
+        // code's 16 bits, and the pending entry is the escape entry (a
+        // second-level entry of length 0, or no link: a bad code)
+        if (__any(t == 0u && p < pend)) {
             wp[0] = uint8_t(we);
             wp[1] = uint8_t(we >> 8);
             wp[2] = uint8_t(we >> 16);
-            wp = row + kSpare;
-            we = 0;
-            const uint64_t w = window(buf, ls.pm1);
-            const uint32_t e = tab[uint32_t(w >> 52)];
-            if ((e & kEsc) && ls.cnt < target) {
-                const uint32_t e2 = l2[min(256u * (1u + (e & 0xFFu)) + uint32_t((w >> 48) & 0xFFu), l2_last)];
+            if (t == 0u && p < pend) {
+                const uint32_t link = we & 0xFFu;
+                const uint32_t e2 = link ? l2[min(256u * link + uint32_t((acc >> 48) & 0xFFu), l2_last)] : 0u;
                 const uint32_t l = e2 & 31u;
-                row[ls.cnt - base] = uint8_t(e2 >> 8);
-                ls.last = (e2 >> 8) | (1u << 24);
+                *p++ = uint8_t((e2 >> 8) << ls.m);
                 ls.bad |= l ? 0u : kBadE;
-                ls.cnt += 1;
                 ls.pm1 += l ? l : 16u;
             }
+            wp = row + kSpare;
+            we = 0;
         }
     }
     wp[0] = uint8_t(we);
     wp[1] = uint8_t(we >> 8);
     wp[2] = uint8_t(we >> 16);
+    if (act) ls.cnt = base + uint32_t(p - row);
 }
 
 // the 16 staged exponents of chunk c at phase offset 16 part (rows are 4-byte
@@ -253,7 +259,7 @@ __device__ __forceinline__ v4u combine(v4u ex, uint2 nib, uint32_t m, uint32_t s
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t e = i == 0 ? ex.x : i == 1 ? ex.y : i == 2 ? ex.z : ex.w;
-        const uint32_t v = ((nb[i] << (7u - m)) & smask) | (e << m) | (nb[i] & mmask);
+        const uint32_t v = ((nb[i] << (7u - m)) & smask) | e | (nb[i] & mmask);
         if (i == 0) o.x = v;
         else if (i == 1) o.y = v;
         else if (i == 2) o.z = v;
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void e8huf_decode_kernel(Args a) {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const uint32_t i = threadIdx.x + uint32_t(q) * kThreads;
-        ent[q] = i < uint32_t(kTabEntries) ? make_entry(l2, l2_last, i) : 0u;
+        ent[q] = i < uint32_t(kTabEntries) ? make_entry(l2, l2_last, i, m) : 0u;
     }
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
@@ -377,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void e8huf_decode_kernel(Args a) {
                 }
                 const uint32_t my_cnt = mine ? uint32_t(lane_cnt) : 0u;
                 // lanes outside the pass keep their windows at the buffer start
-                Lane ls = {mine ? uint32_t(lane_start - uint64_t(32 * j0) - 1) : 0u, 0u, 0u, 0u};
+                Lane ls = {mine ? uint32_t(lane_start - uint64_t(32 * j0) - 1) : 0u, 0u, 0u, m};
                 const uint32_t pm1_0 = ls.pm1;
                 uint8_t* row = stage + lane * kStageStride;
 #pragma unroll 1
@@ -425,10 +431,12 @@ __global__ __launch_bounds__(kThreads) void e8huf_decode_kernel(Args a) {
                 }
                 // the last lookup may have taken symbols past the lane's
                 // count; their bits are not the lane's
+                // (they sit in the row right after its last symbol)
                 uint32_t used = ls.pm1 - pm1_0;
-                const uint32_t k = e_count(ls.last);
-                for (uint32_t j = 0; j < ls.cnt - min(ls.cnt, my_cnt) && j < k; ++j)
-                    used -= lenof[(ls.last >> (8 * (k - 1 - j))) & 31u];
+                if (my_cnt) {
+                    const uint8_t* over = row + (my_cnt - (my_cnt - 1u) / kPhase * kPhase);
+                    for (uint32_t j = 0; j < 2u && my_cnt + j < ls.cnt; ++j) used -= lenof[(over[j] >> m) & 31u];
+                }
                 bad |= mine ? (ls.bad & kBadE) : 0u;
                 end_bad |= bit(mine && used != lb);
                 l0 = l1;
