@@ -378,3 +378,28 @@ def e8_fib_exponents(seed: int, n: int, k: int = 18) -> np.ndarray:
     sign = rng.integers(0, 2, n, dtype=np.uint8) << 7
     mant = rng.integers(0, 4, n, dtype=np.uint8)
     return (sign | (exps << 2) | mant).astype(np.uint8)
+
+
+def e8_rare_at_edges(seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """8 blocks of 16,384 E4M3 values plus a partial block of 700. Exponent
+    field f in 4..15 occurs with probability proportional to 2^(f - 15) (a
+    chain of code lengths 1..12); two fields (0 and 1) occur only at 18
+    listed positions, so their codes are longer than 12 bits. Those
+    positions sit at lane-chunk edges (chunks of 256 values: offsets 0, 1,
+    254, 255), at the half-chunk edge (offsets 126-130, pairs across it) and
+    at the end of the partial block's last lane. Returns the bytes and the
+    positions."""
+    rng = np.random.default_rng((SEED_BASE, 8500, seed))
+    n = 8 * 16384 + 700
+    w = 2.0 ** np.arange(-11, 1, dtype=np.float64)
+    exps = rng.choice(np.arange(4, 16, dtype=np.uint8), size=n, p=w / w.sum())
+    lanes = [0, 17, 63, 5, 40, 63, 31, 1]
+    offs = [[0, 1], [126, 127], [127, 128], [128, 129], [129, 130], [254, 255], [255], [0, 255]]
+    pos = [b * 16384 + 256 * lanes[b] + o for b in range(8) for o in offs[b]]
+    pos += [8 * 16384 + 256 * 1 + 255, 8 * 16384 + 256 * 2 + 186, 8 * 16384 + 256 * 2 + 187]
+    pos = np.array(pos, dtype=np.int64)
+    exps[pos] = (np.arange(pos.size) % 2).astype(np.uint8)
+    sign = rng.integers(0, 2, n, dtype=np.uint8) << 7
+    mant = rng.integers(0, 8, n, dtype=np.uint8)
+    return (sign | (exps << 3) | mant).astype(np.uint8), pos
+

@@ -95,7 +95,7 @@ def test_trunk_parity():
                                   "fib_e5m2"])
 def test_edge_parity(case):
     """One exponent value (1-bit codes); uniform bytes (every block's codes
-    exceed the wave's 8 KiB buffer, so lanes decode in passes); Fibonacci
+    exceed the wave's 6 KiB buffer, so lanes decode in passes); Fibonacci
     exponent counts over 18 E5M2 fields (smoothed codes up to 16 bits, taken
     through the second-level table)."""
     n = 40 * 16384 + 123
@@ -111,6 +111,23 @@ def test_edge_parity(case):
     assert (got == x).all()
     if case == "fib_e5m2":
         assert e8huf.layer_info(blob)["codelen"].max() > 12      # escapes were taken
+
+
+def test_long_codes_at_chunk_and_phase_edges():
+    """Codes longer than 12 bits (taken through the second-level table) at
+    the first and last values of lane chunks, on both sides of the edge
+    between a lane's two 128-value halves (alone and in pairs), and at the
+    end of a partial block's last lane: the cases where such a code meets a
+    lookup that ran past a half or past the lane's count."""
+    x, pos = synth.e8_rare_at_edges(1)
+    blob = O.e8_encode(x, 4)
+    cl = e8huf.layer_info(blob)["codelen"]
+    assert cl[0] > 12 and cl[1] > 12
+    say("e8 long codes at edges", x.size)
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got[pos] == x[pos]).all()
+    assert (got == x).all()
 
 
 def test_packer_container_decodes_on_gpu():
