@@ -14,9 +14,11 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // 16-byte unit u of the output is unit u of the input while the input lasts,
 // then {u mod 2^32, 0, 0, 0}; input units past the output are read and
 // folded into one word, written to output unit 0 only when it equals a
-// value the caller never sees in practice, so the reads are kept.
+// value the caller never sees in practice, so the reads are kept. The store
+// kind is a template parameter, so the loop carries no branch for it.
+template <bool kNonTemporal>
 __global__ __launch_bounds__(256) void stream_kernel(const v4u* __restrict__ in, uint64_t n_in,
-                                                     v4u* __restrict__ out, uint64_t n_out, int nontemporal) {
+                                                     v4u* __restrict__ out, uint64_t n_out) {
     const uint64_t stride = uint64_t(gridDim.x) * blockDim.x;
     const uint64_t n = n_in > n_out ? n_in : n_out;
     uint32_t fold = 0;
@@ -24,7 +26,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const v4u* __restrict__ in,
         v4u v = {uint32_t(u), 0u, 0u, 0u};
         if (u < n_in) v = in[u];
         if (u < n_out) {
-            if (nontemporal)
+            if (kNonTemporal)
                 __builtin_nontemporal_store(v, out + u);
             else
                 out[u] = v;
@@ -43,8 +45,11 @@ extern "C" int k3huf_stream_ref(const void* d_in, uint64_t in_bytes, void* d_out
         (reinterpret_cast<uintptr_t>(d_in) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15) || grid < 1 ||
         grid > (1 << 20))
         return K3HUF_E_ARG;
-    hipLaunchKernelGGL(stream_kernel, dim3(unsigned(grid)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const v4u*>(d_in), in_bytes / 16, static_cast<v4u*>(d_out), out_bytes / 16,
-                       nontemporal);
+    if (nontemporal)
+        hipLaunchKernelGGL(stream_kernel<true>, dim3(unsigned(grid)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const v4u*>(d_in), in_bytes / 16, static_cast<v4u*>(d_out), out_bytes / 16);
+    else
+        hipLaunchKernelGGL(stream_kernel<false>, dim3(unsigned(grid)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const v4u*>(d_in), in_bytes / 16, static_cast<v4u*>(d_out), out_bytes / 16);
     return hipGetLastError() == hipSuccess ? K3HUF_OK : K3HUF_E_HIP;
 }
