@@ -149,7 +149,7 @@ __device__ __forceinline__ uint64_t window(const uint32_t* buf, uint32_t pm1) {
 struct Lane {
     uint32_t pm1;      // buffer bit index of the next code, minus one
     uint32_t cnt;      // symbols decoded so far (may pass the lane's count by two)
-    uint32_t bad;      // kBadE: a code the second-level table does not cover
+    uint32_t bad;      // kBadE: a code that no table covers
     uint32_t m;        // staged symbols are exponents shifted left by m (mantissa bits)
 };
 
@@ -157,12 +157,13 @@ struct Lane {
 // row is symbol base + i). Each 64-bit window feeds kLookups lookups of the
 // 12-bit table; an entry's symbols are written as three bytes at the lane's
 // write position p (bytes past the entry's symbols are overwritten by the
-// next lookup or lie past the phase). A lane that has its symbols takes zero
-// entries until the wave's slowest lane is done; their zero bytes land after
-// its last symbol. An escape entry (the first code is longer than 12 bits)
-// yields nothing, so the lane stays on that code for the rest of the window;
-// after the window, lanes on an escape take that one code through the
-// second-level table. Every window either yields a symbol on each live lane
+// next lookup or lie past the phase). A lane that has its symbols extracts
+// both fields with width 0 (no bits, no symbols) until the wave's slowest
+// lane is done; the bytes of its entries land after its last symbol. An
+// escape entry (the first code is longer than 12 bits, or no code covers the
+// prefix) yields nothing, so the lane stays on that code for the rest of the
+// window; after the window, lanes on an escape take that one code through
+// the second-level table, or flag it. Every window either yields a symbol on each live lane
 // or resolves an escape, so 2 * 64 windows always finish a phase. A lookup
 // that ends past the phase leaves up to two symbols in the row's bytes
 // kPhase and kPhase + 1; they move to the start of the next phase's row. A
