@@ -403,3 +403,16 @@ def e8_rare_at_edges(seed: int) -> tuple[np.ndarray, np.ndarray]:
     mant = rng.integers(0, 8, n, dtype=np.uint8)
     return (sign | (exps << 3) | mant).astype(np.uint8), pos
 
+
+def e8_long_codes_in_passes(seed: int, n: int) -> np.ndarray:
+    """n E5M2 bytes whose exponent fields 0..19 have probabilities falling by
+    a factor 0.86 each and fields 20..31 by a further factor 2 each: the
+    codes average about 4 bits, so a block's codes (about 8 KB) exceed a
+    6 KiB buffer, and the rare fields get codes of 13-16 bits."""
+    rng = np.random.default_rng((SEED_BASE, 8600, seed))
+    w = np.concatenate([0.86 ** np.arange(20), 0.86 ** 19 * 0.5 ** np.arange(1, 13)])
+    exps = rng.choice(np.arange(32, dtype=np.uint8), size=n, p=w / w.sum())
+    sign = rng.integers(0, 2, n, dtype=np.uint8) << 7
+    mant = rng.integers(0, 4, n, dtype=np.uint8)
+    return (sign | (exps << 2) | mant).astype(np.uint8)
+

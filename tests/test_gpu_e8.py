@@ -92,25 +92,30 @@ def test_trunk_parity():
 
 
 @pytest.mark.parametrize("case", ["one_exponent", "one_exponent_e5m2", "uniform_e4m3", "uniform_e5m2",
-                                  "fib_e5m2"])
+                                  "fib_e5m2", "long_codes_in_passes"])
 def test_edge_parity(case):
     """One exponent value (1-bit codes); uniform bytes (every block's codes
     exceed the wave's 6 KiB buffer, so lanes decode in passes); Fibonacci
     exponent counts over 18 E5M2 fields (smoothed codes up to 16 bits, taken
-    through the second-level table)."""
+    through the second-level table); and both at once: E5M2 blocks whose
+    codes exceed the buffer (decoded in passes) holding codes of 13-16 bits."""
     n = 40 * 16384 + 123
     x, eb = {"one_exponent": (synth.e8_one_exponent(11, n), 4),
              "one_exponent_e5m2": (synth.e8_one_exponent(12, n, "e5m2"), 5),
              "uniform_e4m3": (synth.e8_uniform_bytes(13, n), 4),
              "uniform_e5m2": (synth.e8_uniform_bytes(14, n), 5),
-             "fib_e5m2": (synth.e8_fib_exponents(15, n), 5)}[case]
+             "fib_e5m2": (synth.e8_fib_exponents(15, n), 5),
+             "long_codes_in_passes": (synth.e8_long_codes_in_passes(16, n), 5)}[case]
     blob = O.e8_encode(x, eb)
     say("e8 edge", case, n)
     got, st = gpu_decode(blob)
     assert st == 0
     assert (got == x).all()
-    if case == "fib_e5m2":
+    if case in ("fib_e5m2", "long_codes_in_passes"):
         assert e8huf.layer_info(blob)["codelen"].max() > 12      # escapes were taken
+    if case in ("uniform_e4m3", "uniform_e5m2", "long_codes_in_passes"):
+        info = e8huf.layer_info(blob)
+        assert info["n_bits"] / info["n_blocks"] > 6144 * 8      # blocks decode in passes
 
 
 def test_long_codes_at_chunk_and_phase_edges():
