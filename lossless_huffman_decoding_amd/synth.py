@@ -416,3 +416,45 @@ def e8_long_codes_in_passes(seed: int, n: int) -> np.ndarray:
     mant = rng.integers(0, 4, n, dtype=np.uint8)
     return (sign | (exps << 2) | mant).astype(np.uint8)
 
+
+def e8_fuzz_tensor(seed: int, max_values: int = 4 << 20) -> tuple[np.ndarray, int, str]:
+    """A seeded random FP8 tensor for sweeps: a size log-uniform in
+    [1, max_values], E4M3 or E5M2, and one of several exponent laws (normal
+    values of a random scale, uniform bytes, a few live exponent fields with
+    Dirichlet weights, Zipf-like exponent ranks, a chain of fields whose
+    probabilities fall by a random factor); signs and mantissas uniform
+    unless drawn from the values. Returns the bytes, the exponent width and a
+    short description."""
+    rng = np.random.default_rng((SEED_BASE, 9100, seed))
+    n = max(1, int(math.exp(rng.uniform(0.0, math.log(max_values)))))
+    fmt = "e4m3" if rng.integers(0, 2) == 0 else "e5m2"
+    eb = FP8_EXP_BITS[fmt]
+    m = 7 - eb
+    law = int(rng.integers(0, 5))
+    if law == 0:
+        sigma = float(10.0 ** rng.uniform(-4, 2))
+        x = rng.standard_normal(n) * sigma
+        return fp8_bytes(x, fmt), eb, "%s normal sigma %.3g, %d values" % (fmt, sigma, n)
+    if law == 1:
+        return rng.integers(0, 256, n, dtype=np.uint8), eb, "%s uniform bytes, %d values" % (fmt, n)
+    nf = 1 << eb
+    if law == 2:
+        k = int(rng.choice([1, 2, 3, 5, 9, nf]))
+        fields = rng.choice(nf, size=k, replace=False)
+        w = rng.dirichlet(np.full(k, 0.3))
+        exps = fields[rng.choice(k, size=n, p=w)].astype(np.uint8)
+        what = "%s %d live exponent fields (Dirichlet 0.3), %d values" % (fmt, k, n)
+    elif law == 3:
+        a = float(rng.uniform(1.05, 3.0))
+        ranks = np.minimum(rng.zipf(a, size=n), nf) - 1
+        exps = rng.permutation(nf)[ranks].astype(np.uint8)
+        what = "%s Zipf a=%.2f exponent ranks, %d values" % (fmt, a, n)
+    else:
+        r = float(rng.uniform(0.3, 0.9))
+        w = r ** np.arange(nf)
+        exps = rng.permutation(nf)[rng.choice(nf, size=n, p=w / w.sum())].astype(np.uint8)
+        what = "%s exponent chain r=%.2f, %d values" % (fmt, r, n)
+    sign = rng.integers(0, 2, n, dtype=np.uint8) << 7
+    mant = rng.integers(0, 1 << m, n, dtype=np.uint8)
+    return (sign | (exps << m) | mant).astype(np.uint8), eb, what
+

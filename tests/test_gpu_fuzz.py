@@ -1,11 +1,17 @@
-"""Seeded random sweep: GPU encoder and decoder against the CPU oracle.
+"""Seeded random sweeps: GPU encoder and decoders against the CPU oracles.
 
-Each case draws a layer with lossless_huffman_decoding_amd.synth.fuzz_layer
+bf16: each case draws a layer with lossless_huffman_decoding_amd.synth.fuzz_layer
 (random size and high-byte law). The GPU encoder must give the oracle's
 container byte for byte (into output and work buffers filled with a non-zero
 pattern), and the GPU decoder must give the layer back with a clean status
 word (decode(encode(x)) = x, K3 trunk-compression page, "verification
-results"). Every case prints its seed and layer before touching the GPU.
+results").
+
+FP8: each case draws a tensor with synth.e8_fuzz_tensor (random size, format
+and exponent law); the FP8 decoder must give it back from the oracle's
+container with a clean status word (ECF8 page, pwwt.cn/news/2030120, section
+2.2: lossless decode). Every case prints its seed and input before touching
+the GPU.
 """
 
 import numpy as np
@@ -13,7 +19,7 @@ import pytest
 import torch
 
 import oracle as O
-from lossless_huffman_decoding_amd import k3huf, synth
+from lossless_huffman_decoding_amd import e8huf, k3huf, synth
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -38,3 +44,21 @@ def test_fuzz_encode_and_decode(seed):
     torch.cuda.synchronize()
     assert int(st.item()) == 0, what
     assert torch.equal(dec, d_x), what
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_fuzz_e8_decode(seed):
+    x, eb, what = synth.e8_fuzz_tensor(seed)
+    blob = O.e8_encode(x, eb)
+    info = e8huf.layer_info(blob)
+    lut = e8huf.build_table(info["codelen"], eb)
+    print("[gpu-case] fuzz e8", seed, what, flush=True)
+    d_blob = torch.from_numpy(blob).to(DEV)
+    d_lut = torch.from_numpy(lut.view(np.int16)).to(DEV)
+    dec = torch.full((x.size,), 0xA5, dtype=torch.uint8, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    e8huf.decode(d_blob, d_lut, dec, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0, what
+    assert (dec.cpu().numpy() == x).all(), what
+
