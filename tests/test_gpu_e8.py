@@ -176,6 +176,35 @@ def test_corrupt_header_is_flagged_and_nothing_written():
     assert st & e8huf.DEV_HEADER
 
 
+def test_null_status_word():
+    """The status word is optional (include/e8huf.h): a decode without one
+    gives a valid tensor back, and a corrupt one (noise in the bitstream, a
+    bad lane count) completes with nothing to report, after which a valid
+    decode still gives its tensor back."""
+    x = synth.e8_small(24, 5 * 16384 + 77)
+    blob = O.e8_encode(x)
+    info = e8huf.layer_info(blob)
+    d_lut = torch.from_numpy(e8huf.build_table(info["codelen"], 4).view(np.int16)).to(DEV)
+
+    def run(b):
+        d_blob = torch.from_numpy(np.ascontiguousarray(b)).to(DEV)
+        d_out = torch.full((x.size,), 0xA5, dtype=torch.uint8, device=DEV)
+        e8huf.decode(d_blob, d_lut, d_out, None)
+        torch.cuda.synchronize()
+        return d_out.cpu().numpy()
+
+    say("e8 null status: valid")
+    assert (run(blob) == x).all()
+    bad = blob.copy()
+    boff, noff = _u64(blob, 40), _u64(blob, 48)
+    bad[boff: noff] = np.random.default_rng(25).integers(0, 256, noff - boff, dtype=np.uint8)
+    bad[128 + 136 * 2 + 8 + 2 * 5] ^= 1       # and a lane count of block 2
+    say("e8 null status: corrupt")
+    run(bad)
+    say("e8 null status: valid again")
+    assert (run(blob) == x).all()
+
+
 def test_corrupt_index_and_bits_are_flagged():
     x = synth.e8_small(22, 3 * 16384 + 5)
     blob = O.e8_encode(x)
