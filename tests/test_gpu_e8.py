@@ -176,6 +176,44 @@ def test_corrupt_header_is_flagged_and_nothing_written():
     assert st & e8huf.DEV_HEADER
 
 
+def test_graph_replays_beside_an_eager_decode():
+    """An FP8 decode captured into a graph on stream s and replayed on the
+    default stream while another FP8 decode runs on s: both tensors come
+    back on every replay (eager fills and synchronization between replays;
+    the kernel keeps no state between launches)."""
+    x1 = synth.e8_small(26, 70 * 16384 + 19)
+    x2 = synth.e8_small(27, 50 * 16384 + 3, "e5m2")
+    b1, b2 = O.e8_encode(x1, 4), O.e8_encode(x2, 5)
+    dev = []
+    for b, eb in ((b1, 4), (b2, 5)):
+        lut = e8huf.build_table(e8huf.layer_info(b)["codelen"], eb)
+        dev.append((torch.from_numpy(b).to(DEV), torch.from_numpy(lut.view(np.int16)).to(DEV)))
+    out1 = torch.empty(x1.size, dtype=torch.uint8, device=DEV)
+    out2 = torch.empty(x2.size, dtype=torch.uint8, device=DEV)
+    st1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    st2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("e8 graph capture of a decode")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        e8huf.decode(dev[0][0], dev[0][1], out1, st1)
+    for rep in range(3):
+        out1.fill_(0xA5)
+        out2.fill_(0x5A)
+        st1.zero_()
+        st2.zero_()
+        torch.cuda.synchronize()
+        say("e8 graph replay beside a decode", rep)
+        with torch.cuda.stream(s):
+            e8huf.decode(dev[1][0], dev[1][1], out2, st2)
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(st1.item()) == 0 and int(st2.item()) == 0
+        assert (out1.cpu().numpy() == x1).all(), rep
+        assert (out2.cpu().numpy() == x2).all(), rep
+
+
 def test_null_status_word():
     """The status word is optional (include/e8huf.h): a decode without one
     gives a valid tensor back, and a corrupt one (noise in the bitstream, a
