@@ -1,4 +1,4 @@
-"""Decode-on-demand of compressed bf16 module weights.
+"""Decode-on-demand of compressed bf16 and FP8 module weights.
 
 The ECF8 page (pwwt.cn/news/2030120), section 2.2 ("zero-copy tensor
 management"), keeps weights compressed in device memory, pre-allocates a
@@ -11,6 +11,12 @@ in the lane-chunk layout k3huf_lane_syms_for picks for its size) of its
 weights laid end to end; only the container and its 4096-entry table stay
 resident. When a member module is about to run, its group is decoded (once)
 into a buffer and every member's weight becomes a view of its slice.
+
+FP8 weights (float8_e4m3fn, float8_e5m2: the ECF8 page's case) are packed
+instead in the FP8 exponent format (e8huf_encode, the library's native host
+packer: the group's bytes go to the host once, at attach time) with its
+two-level table, and decoded by e8huf_decode into the same buffers. The
+members of one group share one dtype; groups of either kind mix freely.
 
 Two schedules:
   - lookahead=False (default): one buffer; the group's decode is queued on
@@ -38,11 +44,15 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import k3huf
+from . import e8huf, k3huf
+
+# FP8 dtypes and the width of their exponent field
+_FP8_EXP_BITS = {torch.float8_e4m3fn: 4, torch.float8_e5m2: 5}
 
 
 class OnDemandWeights:
-    """Hold modules' bf16 weights compressed in HBM; decode each group on use.
+    """Hold modules' bf16 or FP8 weights compressed in HBM; decode each
+    group on use.
 
     ``attach(module)`` makes a group of one; ``attach_group(modules)`` packs
     the modules' weights together. Attach in the order the groups run. The
@@ -64,7 +74,7 @@ class OnDemandWeights:
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
         # decodes may run on any stream: the cleared status must be in place
         torch.cuda.current_stream(self.device).synchronize()
-        self._lib = k3huf.lib()
+        self._lib = e8huf.lib()   # (loads libk3huf.so and declares both codecs' calls)
         self._decoded = [torch.cuda.Event() for _ in range(n)]
         if lookahead:
             self._side = torch.cuda.Stream(device=self.device)
@@ -82,35 +92,54 @@ class OnDemandWeights:
         self.attach_group([module], name)
 
     def attach_group(self, modules, name: str = "weight") -> None:
-        members, parts, off = [], [], 0
+        members, parts, off, dtype = [], [], 0, None
         for m in modules:
             w = getattr(m, name)
-            if w is None or w.dtype != torch.bfloat16 or w.device != self.device:
-                raise ValueError("decode-on-demand needs bf16 weights on %s" % self.device)
+            if (w is None or w.device != self.device
+                    or (w.dtype != torch.bfloat16 and w.dtype not in _FP8_EXP_BITS)):
+                raise ValueError("decode-on-demand needs bf16, float8_e4m3fn or float8_e5m2 weights on %s"
+                                 % self.device)
+            if dtype is not None and w.dtype != dtype:
+                raise ValueError("the weights of one group must share a dtype (%s, %s)" % (dtype, w.dtype))
+            dtype = w.dtype
             raw = w.detach().contiguous().view(torch.uint8).reshape(-1)
             members.append((m, off, raw.numel(), tuple(w.shape)))
             parts.append(raw)
             off += raw.numel()
+        if not members:
+            raise ValueError("an empty group")
         raw = parts[0] if len(parts) == 1 else torch.cat(parts)
-        # the lane-chunk layout by the library's rule (64-symbol chunks for
-        # containers of up to 16 MiB, whose decode is one lane's chain of
-        # lookups); trimmed copy, the bound-sized output is freed
-        blob = k3huf.encode_layer_dev(raw, lane_syms=k3huf.lane_syms_for(raw.numel())).clone()
+        if dtype == torch.bfloat16:
+            # the lane-chunk layout by the library's rule (64-symbol chunks for
+            # containers of up to 16 MiB, whose decode is one lane's chain of
+            # lookups); trimmed copy, the bound-sized output is freed
+            blob = k3huf.encode_layer_dev(raw, lane_syms=k3huf.lane_syms_for(raw.numel())).clone()
+            info = k3huf.layer_info(blob[: k3huf.HDR_BYTES].cpu().numpy())
+            lut = torch.from_numpy(k3huf.build_table(info["codelen"]).view(np.int16)).to(self.device)
+            fn, fname = self._lib.k3huf_decode_layer, "k3huf_decode_layer"
+        else:
+            eb = _FP8_EXP_BITS[dtype]
+            hblob = e8huf.encode(raw.cpu().numpy(), exp_bits=eb)
+            info = e8huf.layer_info(hblob[: e8huf.HDR_BYTES])
+            blob = torch.from_numpy(hblob).to(self.device)
+            lut = torch.from_numpy(e8huf.build_table(info["codelen"], eb).view(np.int16)).to(self.device)
+            fn, fname = self._lib.e8huf_decode, "e8huf_decode"
         del raw, parts
-        info = k3huf.layer_info(blob[: k3huf.HDR_BYTES].cpu().numpy())
-        lut = torch.from_numpy(k3huf.build_table(info["codelen"]).view(np.int16)).to(self.device)
         g = {"blob": blob, "lut": lut, "raw_bytes": off, "name": name, "members": members,
-             "index": len(self._groups)}
+             "index": len(self._groups), "dtype": dtype, "fn": fn, "fname": fname}
         self._groups.append(g)
         for i, b in enumerate(self._bufs):
             if off > b.numel():
                 self._bufs[i] = torch.empty(off, dtype=torch.uint8, device=self.device)
         # per buffer: the decode call's arguments and the members' weight views
         # (the hooks run per forward, so they only look these up)
+        # (both decode calls end in stream, status)
         for x in self._groups:
             x["calls"] = [(x["blob"].data_ptr(), x["blob"].numel(), x["lut"].data_ptr(), b.data_ptr(),
-                           x["raw_bytes"]) for b in self._bufs]
-            x["views"] = [[b[o: o + n].view(torch.bfloat16).view(shape) for (_, o, n, shape) in x["members"]]
+                           x["raw_bytes"]) if x["dtype"] == torch.bfloat16 else
+                          (x["blob"].data_ptr(), x["blob"].numel(), x["lut"].data_ptr(), x["lut"].numel(),
+                           b.data_ptr(), x["raw_bytes"]) for b in self._bufs]
+            x["views"] = [[b[o: o + n].view(x["dtype"]).view(shape) for (_, o, n, shape) in x["members"]]
                           for b in self._bufs]
         for j, (m, _, _, _) in enumerate(members):
             self._by_module[id(m)] = (g, j)
@@ -122,11 +151,9 @@ class OnDemandWeights:
                 self._handles.append(m.register_forward_hook(self._post_hook))
 
     def _decode(self, g, slot: int, stream_handle: int) -> None:
-        blob, blob_bytes, lut, out, raw = g["calls"][slot]
-        rc = self._lib.k3huf_decode_layer(blob, blob_bytes, lut, out, raw, stream_handle,
-                                          self.status.data_ptr())
+        rc = g["fn"](*g["calls"][slot], stream_handle, self.status.data_ptr())
         if rc:
-            raise k3huf.K3HufError(rc, "k3huf_decode_layer")
+            raise k3huf.K3HufError(rc, g["fname"])
 
     def _pre_hook(self, module, inputs):
         g, j = self._by_module[id(module)]
@@ -167,7 +194,9 @@ class OnDemandWeights:
         self._free[g["index"] % 2].record(torch.cuda.current_stream(self.device))
 
     def check(self) -> None:
-        """Raise if any decode so far flagged malformed input (synchronizes)."""
+        """Raise if any decode so far flagged malformed input (synchronizes).
+        The word holds the codecs' own device bits (K3HUF_DEV_* from bf16
+        groups, E8HUF_DEV_* from FP8 groups), OR-ed together."""
         torch.cuda.synchronize(self.device)
         st = int(self.status.item())
         if st:

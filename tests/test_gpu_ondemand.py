@@ -1,8 +1,8 @@
 """Decode-on-demand of module weights (ECF8 page, section 2.2: one buffer the
 size of the largest layer, filled by a forward pre-hook before each layer).
 
-The decoded weights are the original bf16 bytes, so a forward pass through
-the hooked modules must equal the dense forward pass bit for bit. Every case
+The decoded weights are the original bf16 or FP8 bytes, so a forward pass
+through the hooked modules must equal the dense forward pass bit for bit. Every case
 prints its name before touching the GPU.
 """
 
@@ -141,3 +141,77 @@ def test_on_demand_groups(lookahead):
         b = model(x)
     od.check()
     assert torch.equal(a, want) and torch.equal(b, want)
+
+
+class _FP8Linear(torch.nn.Module):
+    """A weight-only FP8 linear map: y = x (scale * W)^T, W held as FP8 and
+    widened to bf16 on use (the ECF8 page's setting: FP8 weights, decoded
+    from their compressed form just before the layer runs)."""
+
+    def __init__(self, w, scale):
+        super().__init__()
+        self.weight = torch.nn.Parameter(w, requires_grad=False)
+        self.scale = scale
+
+    def forward(self, x):
+        return torch.nn.functional.linear(x, self.weight.to(torch.bfloat16) * self.scale)
+
+
+def _fp8_stack(shapes, fmts, seed):
+    layers = []
+    for k, ((o, i), fmt) in enumerate(zip(shapes, fmts)):
+        if fmt == "bf16":
+            lin = torch.nn.Linear(i, o, bias=False, dtype=torch.bfloat16, device=DEV)
+            with torch.no_grad():
+                lin.weight.copy_(_trunk_like(o, i, seed + k).to(DEV))
+        else:
+            dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+            raw = synth.e8_small(seed + k, o * i, fmt)
+            w = torch.from_numpy(raw).view(dt).view(o, i).to(DEV)
+            lin = _FP8Linear(w, 0.03 / synth.FP8_MAX[fmt])
+        layers.append(lin)
+    return torch.nn.Sequential(*layers)
+
+
+@pytest.mark.parametrize("lookahead", [False, True])
+def test_on_demand_fp8_weights(lookahead):
+    """FP8 weights (E4M3 and E5M2 groups) beside a bf16 group: each FP8
+    group is one E8HF container decoded by e8huf_decode into the shared
+    buffers. Every forward equals the dense one bit for bit, the FP8 views
+    hold the original bytes, and the containers are smaller than the
+    weights."""
+    shapes = [(1024, 512), (768, 1024), (512, 768), (640, 512), (512, 640)]
+    fmts = ["e4m3", "e4m3", "bf16", "e5m2", "e5m2"]
+    model = _fp8_stack(shapes, fmts, 1100)
+    x = torch.randn(3, 512, generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).to(DEV)
+    dense = [m.weight.detach().clone() for m in model]
+    say("ondemand fp8 dense forward", lookahead)
+    with torch.no_grad():
+        want = model(x)
+        want_last = model[4](model[3](torch.ones(2, 512, dtype=torch.bfloat16, device=DEV)))
+    od = OnDemandWeights(DEV, lookahead=lookahead)
+    od.attach_group([model[0], model[1]])
+    od.attach(model[2])
+    od.attach_group([model[3], model[4]])
+    weight_bytes = [1024 * 512 + 768 * 1024, 512 * 768 * 2, 640 * 512 * 2]
+    assert od.buffer_bytes == max(weight_bytes) * (2 if lookahead else 1)
+    assert od._groups[0]["blob"][:4].cpu().numpy().tobytes() == b"E8HF"
+    assert od._groups[1]["blob"][:4].cpu().numpy().tobytes() == b"K3HF"
+    fp8_blobs = od._groups[0]["blob"].numel() + od._groups[2]["blob"].numel()
+    assert fp8_blobs < weight_bytes[0] + weight_bytes[2] // 2
+    say("ondemand fp8 hooked forward", lookahead)
+    with torch.no_grad():
+        got = model(x)
+        got2 = model(x)
+        got_last = model[4](model[3](torch.ones(2, 512, dtype=torch.bfloat16, device=DEV)))
+    od.check()
+    assert torch.equal(got, want) and torch.equal(got2, want)
+    assert torch.equal(got_last, want_last)
+    # the weight each module sees right after its own decode (the buffers are
+    # shared, so an earlier module's view holds a later group's bytes)
+    for (o, i), m, d in zip(shapes, model, dense):
+        with torch.no_grad():
+            m(torch.ones(1, i, dtype=torch.bfloat16, device=DEV))
+        assert m.weight.dtype == d.dtype and m.weight.shape == (o, i)
+        assert torch.equal(m.weight.view(torch.uint8), d.view(torch.uint8))
+    od.check()
