@@ -87,11 +87,15 @@ def test_on_demand_on_a_side_stream(lookahead):
     assert torch.equal(got, want)
 
 
-def test_on_demand_forward_captured_in_a_graph():
+@pytest.mark.parametrize("weights", ["bf16", "fp8"])
+def test_on_demand_forward_captured_in_a_graph(weights):
     """The hooked forward (one buffer, decodes on the capturing stream)
     captured once and replayed: every replay equals the dense forward, with
-    eager work and synchronizations between replays."""
-    model = _stack([(1024, 512), (768, 1024), (512, 768)], 800)
+    eager work and synchronizations between replays. fp8: E4M3, E5M2 and
+    bf16 modules, so the graph holds both codecs' decodes."""
+    shapes = [(1024, 512), (768, 1024), (512, 768)]
+    model = (_stack(shapes, 800) if weights == "bf16" else
+             _fp8_stack(shapes, ["e4m3", "bf16", "e5m2"], 850))
     x = torch.randn(4, 512, generator=torch.Generator().manual_seed(8)).to(torch.bfloat16).to(DEV)
     with torch.no_grad():
         want = model(x)
@@ -100,7 +104,7 @@ def test_on_demand_forward_captured_in_a_graph():
         od.attach(m)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    say("ondemand graph capture")
+    say("ondemand graph capture", weights)
     with torch.cuda.stream(s), torch.no_grad():
         model(x)
     torch.cuda.current_stream().wait_stream(s)
