@@ -48,8 +48,18 @@
  *   bitstream at bits_off: n_bits code bits, MSB first, zero padded to a
  *     multiple of 16 bytes, then to 256;
  *   nibble plane at nib_off: ceil(n / 2) bytes, zero padded to 256; that
- *     offset plus the padded plane is container_bytes.
+ *     offset plus the padded plane is container_bytes. *
+ * Widening (section 2.2: the page's decoder hands its output over as 16-bit
+ * floating-point values rather than FP8 bytes). Reading: output value i is the
+ * FP8 value of decoded byte i (section 1.2's format: sign, exponent field with
+ * bias 2^(e-1) - 1, mantissa with an implicit one unless the exponent field is
+ * zero; E4M3 has no infinities and S.1111.111 is NaN, E5M2 keeps IEEE's
+ * all-ones exponent for infinities and NaNs) times a per-tensor scale, the
+ * product taken in single precision, then rounded to the nearest value of the
+ * 16-bit output format (bfloat16: 8 exponent and 7 mantissa bits; IEEE half:
+ * 5 and 10), ties to an even mantissa, overflow to infinity; a NaN stays a NaN.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -376,4 +386,62 @@ int64_t e8_n_values(const uint8_t *blob, uint64_t size) {
     e8_hdr_t H;
     int rc = parse(blob, size, &H);
     return rc ? rc : (int64_t)H.n;
+}
+
+/* The value an FP8 byte stands for (section 1.2's format), exactly, as a
+ * double. */
+static double fp8_value(uint8_t b, int exp_bits) {
+    const int mb = 7 - exp_bits;                       /* mantissa bits */
+    const int bias = (1 << (exp_bits - 1)) - 1;        /* 7 (E4M3), 15 (E5M2) */
+    const int e = (b >> mb) & ((1 << exp_bits) - 1);
+    const int f = b & ((1 << mb) - 1);
+    double v;
+    if (exp_bits == 4 && e == 15 && f == 7)
+        v = NAN;                                       /* E4M3: the one NaN pattern */
+    else if (exp_bits == 5 && e == 31)
+        v = f ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)f, 1 - bias - mb);           /* subnormal: f * 2^(1 - bias - mb) */
+    else
+        v = ldexp(1.0 + ldexp((double)f, -mb), e - bias);
+    return (b & 0x80) ? -v : v;
+}
+
+/* x rounded to the nearest value of a 16-bit binary format with eb exponent
+ * and mb mantissa bits (bias 2^(eb-1) - 1), ties to the even significand,
+ * magnitudes past the largest finite value's rounding range to infinity. */
+static uint16_t round16(float x, int eb, int mb) {
+    const int bias = (1 << (eb - 1)) - 1, eall = (1 << eb) - 1;
+    const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x)) return (uint16_t)(sign | (eall << mb) | (1u << (mb - 1)));
+    if (isinf(x)) return (uint16_t)(sign | (eall << mb));
+    const double a = fabs((double)x);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);                                     /* a = f * 2^e2, f in [0.5, 1) */
+    int ue = e2 - 1;                                   /* a in [2^ue, 2^(ue+1)) */
+    if (ue < 1 - bias) ue = 1 - bias;                  /* below the normal range: subnormal quantum */
+    double q = rint(ldexp(a, mb - ue));                /* significand in quanta of 2^(ue - mb), ties to even */
+    if (q < ldexp(1.0, mb)) return (uint16_t)(sign | (uint32_t)q);   /* subnormal or zero */
+    if (q == ldexp(1.0, mb + 1)) {                     /* rounded up to the next power of two */
+        q = ldexp(1.0, mb);
+        ue += 1;
+    }
+    const int field = ue + bias;
+    if (field >= eall) return (uint16_t)(sign | (eall << mb));
+    return (uint16_t)(sign | ((uint32_t)field << mb) | ((uint32_t)q - (1u << mb)));
+}
+
+/* out[i] = round16(float(value(x[i])) * scale) for the output kind (1:
+ * bfloat16, 2: IEEE half). Returns 0, or E8_E_ARG. */
+int e8_widen(const uint8_t *x, uint64_t n, int exp_bits, float scale, int out_kind, uint16_t *out) {
+    if ((exp_bits != 4 && exp_bits != 5) || (out_kind != 1 && out_kind != 2) || (n && (!x || !out)))
+        return E8_E_ARG;
+    const int eb = out_kind == 1 ? 8 : 5, mb = out_kind == 1 ? 7 : 10;
+    for (uint64_t i = 0; i < n; i++) {
+        const float v = (float)fp8_value(x[i], exp_bits);   /* exact: every FP8 value is a float */
+        const float p = v * scale;                           /* single-precision product */
+        out[i] = round16(p, eb, mb);
+    }
+    return E8_OK;
 }

@@ -30,7 +30,7 @@ def build(force: bool = False) -> str:
         os.makedirs(os.path.dirname(_LIB), exist_ok=True)
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC",
-                               "-o", tmp, *_SRCS])
+                               "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -99,6 +99,9 @@ def lib():
         L.e8_check_index.restype = ctypes.c_int
         L.e8_n_values.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
         L.e8_n_values.restype = ctypes.c_int64
+        L.e8_widen.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                               ctypes.c_void_p]
+        L.e8_widen.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -295,3 +298,17 @@ def e8_decode_rc(blob) -> int:
 def e8_check_index(blob) -> int:
     b = _u8(blob)
     return lib().e8_check_index(b.ctypes.data, b.size)
+
+
+E8_OUT_BF16, E8_OUT_F16 = 1, 2
+
+
+def e8_widen(x, exp_bits: int, scale: float, out_kind: int) -> np.ndarray:
+    """16-bit output words (bfloat16: out_kind 1, IEEE half: 2) of
+    value(x[i]) * scale in single precision, rounded to nearest even."""
+    r = _u8(x)
+    out = np.empty(r.size, np.uint16)
+    rc = lib().e8_widen(r.ctypes.data, r.size, exp_bits, float(scale), out_kind, out.ctypes.data)
+    if rc:
+        raise ValueError("oracle e8 widen: bad arguments (%d)" % rc)
+    return out

@@ -263,3 +263,84 @@ def test_index_checker_detects_tampering():
     blob2[boff + 50] ^= 0x10
     rc = O.e8_decode_rc(blob2)
     assert rc != O.OK or not (O.e8_decode(blob2) == x).all()
+
+
+# ---------------------------------------------------------------------------
+# widening to 16-bit floats (ECF8 page, section 2.2: the decoder hands over
+# 16-bit floats; value(byte) * scale in single precision, rounded to nearest
+# even)
+
+def _f32(bits):
+    return struct.unpack("<f", struct.pack("<I", bits))[0]
+
+
+def test_widen_golden():
+    """Hand-derived values from the formats' definitions, with ties,
+    subnormals, overflow and infinities (tests/golden/e8_widen.txt)."""
+    rows = [line.split("#")[0].split() for line in open(os.path.join(GOLD, "e8_widen.txt"))
+            if line.strip() and not line.startswith("#")]
+    assert len(rows) == 22
+    for eb, b, sc, bf, h in rows:
+        x = np.array([int(b, 16)], np.uint8)
+        assert int(O.e8_widen(x, int(eb), _f32(int(sc, 16)), O.E8_OUT_BF16)[0]) == int(bf, 16), (eb, b, sc)
+        assert int(O.e8_widen(x, int(eb), _f32(int(sc, 16)), O.E8_OUT_F16)[0]) == int(h, 16), (eb, b, sc)
+
+
+def _torch_widen(codes, exp_bits, scale, out_kind):
+    """The same definition through torch's CPU conversions (a library's
+    FP8 decode, float32 product and round-to-nearest-even narrowing)."""
+    import torch
+    dt = torch.float8_e4m3fn if exp_bits == 4 else torch.float8_e5m2
+    v = torch.from_numpy(codes.copy()).view(dt).to(torch.float32)
+    p = v * torch.tensor(scale, dtype=torch.float32)
+    return p, p.to(torch.bfloat16 if out_kind == O.E8_OUT_BF16 else torch.float16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _same_or_both_nan(got, want, p, kind):
+    nan = np.isnan(p.numpy())
+    assert np.array_equal(got[~nan], want[~nan])
+    # a NaN product gives a NaN word (all-ones exponent, nonzero fraction)
+    ex, fr = (0x7F80, 0x007F) if kind == O.E8_OUT_BF16 else (0x7C00, 0x03FF)
+    g = got[nan].astype(np.uint32)
+    assert np.all((g & ex) == ex) and np.all((g & fr) != 0)
+
+
+@pytest.mark.parametrize("exp_bits", [4, 5])
+def test_widen_every_code_equals_the_library_decode(exp_bits):
+    """All 256 bytes at scale 1: every FP8 value is exact in both outputs,
+    so this pins the value decode (signs, subnormals, NaN, infinities)."""
+    codes = np.arange(256, dtype=np.uint8)
+    for kind in (O.E8_OUT_BF16, O.E8_OUT_F16):
+        p, want = _torch_widen(codes, exp_bits, 1.0, kind)
+        _same_or_both_nan(O.e8_widen(codes, exp_bits, 1.0, kind), want, p, kind)
+
+
+@pytest.mark.parametrize("exp_bits", [4, 5])
+def test_widen_rounding_equals_the_library(exp_bits):
+    """All 256 bytes times 400 scales (log-uniform over 2^-149..2^127, both
+    signs) and special ones (products on ties, the largest float, the
+    smallest subnormal, infinities, NaN, -0): the rounding of the product to
+    bfloat16 and half equals torch's, and half also numpy's astype."""
+    rng = np.random.default_rng(9)
+    scales = list(np.float32(rng.choice([-1, 1], 400) * np.exp2(rng.uniform(-149, 127, 400))))
+    scales += [_f32(b) for b in (0x3F808000, 0x3F818000, 0x3F801000, 0x3F803000, 0x33000000, 0x7F7FFFFF,
+                                 0x00000001, 0x7F800000, 0xFF800000, 0x7FC00000, 0x80000000)]
+    codes = np.arange(256, dtype=np.uint8)
+    for sc in scales:
+        for kind in (O.E8_OUT_BF16, O.E8_OUT_F16):
+            p, want = _torch_widen(codes, exp_bits, float(sc), kind)
+            got = O.e8_widen(codes, exp_bits, float(sc), kind)
+            _same_or_both_nan(got, want, p, kind)
+            if kind == O.E8_OUT_F16:
+                with np.errstate(over="ignore", invalid="ignore"):
+                    h = p.numpy().astype(np.float16).view(np.uint16)
+                _same_or_both_nan(got, h, p, kind)
+
+
+def test_widen_rejects_bad_arguments():
+    x = np.zeros(4, np.uint8)
+    with pytest.raises(ValueError):
+        O.e8_widen(x, 3, 1.0, O.E8_OUT_BF16)
+    with pytest.raises(ValueError):
+        O.e8_widen(x, 4, 1.0, 0)
+    assert O.e8_widen(np.zeros(0, np.uint8), 4, 1.0, O.E8_OUT_F16).size == 0
