@@ -150,6 +150,29 @@ int64_t e8huf_encode(const void* h_x, uint64_t n, int exp_bits, void* h_out, uin
 int e8huf_decode(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut, int lut_entries,
                  void* d_out, uint64_t n_values, void* stream, uint32_t* d_status);
 
+/* output kinds of e8huf_decode_widen */
+#define E8HUF_OUT_BF16 1   /* bfloat16: 8 exponent, 7 mantissa bits */
+#define E8HUF_OUT_F16 2    /* IEEE half: 5 exponent, 10 mantissa bits */
+
+/*
+ * e8huf_decode_widen -- e8huf_decode whose output is 16-bit floats instead of
+ * FP8 bytes (ECF8 page, section 2.2: the page's decoder writes its values out
+ * as 16-bit floats). Element i of d_out is the FP8 value of the tensor's byte
+ * i (E4M3 or E5M2 as the header's exp_bits says; section 1.2), multiplied by
+ * scale in single precision and rounded to the nearest out_kind value, ties
+ * to even, overflow to infinity; a NaN (an E4M3 S.1111.111 byte, an E5M2 NaN,
+ * or a product such as 0 * infinity) gives a NaN whose payload is not
+ * specified. scale = 1 widens exactly: every E4M3 and E5M2 value is a
+ * bfloat16 value, and every E5M2 value a half value.
+ * d_out: device, 16-byte aligned, 2 * n_values bytes. out_kind:
+ * E8HUF_OUT_BF16 or E8HUF_OUT_F16 (anything else is K3HUF_E_ARG). Every other
+ * argument, the status bits, the errors and the concurrency rules are
+ * e8huf_decode's.
+ */
+int e8huf_decode_widen(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut, int lut_entries,
+                       void* d_out, uint64_t n_values, int out_kind, float scale, void* stream,
+                       uint32_t* d_status);
+
 #ifdef __cplusplus
 }
 #endif

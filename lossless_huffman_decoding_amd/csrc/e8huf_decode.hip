@@ -18,9 +18,16 @@
 // table, kept in LDS too. Decoded exponents are staged in LDS rows, so that
 // each output store instruction writes whole 128-byte lines, combined with
 // the sign/mantissa nibbles on the way out.
+//
+// The page's decoder hands its output over as 16-bit floats (section 2.2);
+// e8huf_decode_widen does that: each rebuilt FP8 value goes through the
+// hardware's FP8-to-float conversion, is multiplied by the caller's scale in
+// single precision and is rounded to bfloat16 or half (nearest even) by the
+// packed narrowing conversion, on the way out.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "e8huf.h"
@@ -37,10 +44,6 @@ constexpr int kLanes = 64;
 constexpr int kChunk = int(E8HUF_LANE_VALUES);        // values per lane chunk
 constexpr int kPhase = 128;                           // values per lane per phase
 constexpr int kPhases = kChunk / kPhase;              // 2
-constexpr int kPartLanes = kPhase / 16;               // lanes storing one chunk's phase, 16 bytes each
-constexpr int kPartShift = kPartLanes == 8 ? 3 : kPartLanes == 4 ? 2 : 1;
-constexpr int kRounds = kPartLanes;                   // store rounds per phase (64 / kPartLanes chunks each)
-static_assert((1 << kPartShift) == kPartLanes, "phase of 32, 64 or 128 values");
 constexpr int kBufBytes = 6144;                       // per-wave bitstream buffer (a block's codes take ~5.2 KB on weights)
 constexpr int kBufUnits = kBufBytes / 16;
 // stage row: the phase's 128 symbols, up to two carried past it plus the
@@ -73,6 +76,26 @@ constexpr uint32_t kBadE = 1u << 7;   // in Lane::bad: a code that no table cove
 constexpr uint32_t kCntPos = 24, kLenPos = 28;
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// output kinds: FP8 bytes, or 16-bit floats (E8HUF_OUT_BF16, E8HUF_OUT_F16)
+constexpr int kOutFp8 = 0;
+
+// Output stage per kind: each lane stores 16 bytes per round, so FP8 output
+// takes 16 values per lane (8 lanes per chunk's phase) and 16-bit output 8
+// (16 lanes); either way a store instruction writes whole 128-byte lines.
+template <int kOut>
+struct OutStage {
+    static constexpr int kVals = kOut == kOutFp8 ? 16 : 8;       // values per lane and round
+    static constexpr int kPartLanes = kPhase / kVals;            // lanes storing one chunk's phase
+    static constexpr int kPartShift = kPartLanes == 16 ? 4 : 3;
+    static constexpr int kRounds = kPartLanes;                   // rounds per phase (64 / kPartLanes chunks each)
+    static constexpr int kOutBytes = kOut == kOutFp8 ? 1 : 2;
+    using Nib = typename std::conditional<kOut == kOutFp8, uint2, uint32_t>::type;   // the round's nibbles
+    static_assert((1 << kPartShift) == kPartLanes, "phase of 128 values");
+};
 
 struct Args {
     const uint8_t* blob;
@@ -82,6 +105,7 @@ struct Args {
     uint8_t* out;
     uint64_t n;
     uint32_t* status;
+    float scale;   // 16-bit output: the factor each value is multiplied by
 };
 
 __device__ __forceinline__ uint32_t ld32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
@@ -269,7 +293,107 @@ __device__ __forceinline__ v4u combine(v4u ex, uint2 nib, uint32_t m, uint32_t s
     return o;
 }
 
+// the 8 staged exponents of chunk c at phase offset 8 part (two dword reads)
+__device__ __forceinline__ uint2 staged8(const uint8_t* stage, int c, int part) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(stage + c * kStageStride + part * 8);
+    return make_uint2(p[0], p[1]);
+}
+
+// FP8 bytes from 8 staged exponents (two dwords) and their 8 nibbles (four
+// bytes: value 2i low nibble, 2i + 1 high nibble).
+__device__ __forceinline__ uint2 combine8(uint2 ex, uint32_t nib, uint32_t m, uint32_t smask, uint32_t mmask) {
+    const uint32_t lo = nib & 0x0F0F0F0Fu, hi = (nib >> 4) & 0x0F0F0F0Fu;
+    const uint32_t n0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u), n1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+    return make_uint2(((n0 << (7u - m)) & smask) | ex.x | (n0 & mmask), ((n1 << (7u - m)) & smask) | ex.y | (n1 & mmask));
+}
+
+// Four FP8 values (one dword, value k in byte k) as floats: the hardware
+// conversions take E4M3 (fp8) or E5M2 (bf8) from either 16-bit half.
+template <bool kE5M2, bool kHigh>
+__device__ __forceinline__ v2f fp8_pair(uint32_t x) {
+    if constexpr (kE5M2)
+        return __builtin_amdgcn_cvt_pk_f32_bf8(x, kHigh);
+    else
+        return __builtin_amdgcn_cvt_pk_f32_fp8(x, kHigh);
+}
+
+// Eight FP8 values (two dwords) times scale, rounded to the output kind:
+// sixteen bytes of output, value k in halfword k.
+template <int kOut, bool kE5M2>
+__device__ __forceinline__ v4u widen8(uint2 f, float scale) {
+    v2f v[4] = {fp8_pair<kE5M2, false>(f.x), fp8_pair<kE5M2, true>(f.x), fp8_pair<kE5M2, false>(f.y),
+                fp8_pair<kE5M2, true>(f.y)};
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i].x *= scale;
+        v[i].y *= scale;
+        if (kOut == E8HUF_OUT_BF16)
+            w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[i], v2bf));
+        else
+            w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[i], v2h));
+    }
+    v4u o;
+    o.x = w[0];
+    o.y = w[1];
+    o.z = w[2];
+    o.w = w[3];
+    return o;
+}
+
+// The 16 output bytes of round rr's lane part: FP8 bytes, or 8 values
+// widened to 16 bits.
+template <int kOut, bool kE5M2>
+__device__ __forceinline__ v4u out16(const uint8_t* stage, int c, int part, typename OutStage<kOut>::Nib nib,
+                                     uint32_t m, uint32_t smask, uint32_t mmask, float scale) {
+    if constexpr (kOut == kOutFp8)
+        return combine(staged16(stage, c, part), nib, m, smask, mmask);
+    else
+        return widen8<kOut, kE5M2>(combine8(staged8(stage, c, part), nib, m, smask, mmask), scale);
+}
+
+// One phase's output: every chunk's 128 staged exponents with their nibbles
+// (requested into nb before the phase's decode), as FP8 bytes or widened
+// 16-bit values. A whole block in one pass stores every part unchecked and
+// non-temporal; otherwise only the pass's chunks and the tensor's values.
+template <int kOut, bool kE5M2>
+__device__ __forceinline__ void store_phase(const Args& a, const uint8_t* stage,
+                                            const typename OutStage<kOut>::Nib* nb, uint64_t v0, uint32_t nvals,
+                                            int ph, bool whole, int l0, int l1, int lane, uint32_t m,
+                                            uint32_t smask, uint32_t mmask) {
+    using S = OutStage<kOut>;
+    if (whole) {
+#pragma unroll
+        for (int rr = 0; rr < S::kRounds; ++rr) {
+            const int c = rr * (kLanes / S::kPartLanes) + (lane >> S::kPartShift), part = lane & (S::kPartLanes - 1);
+            const v4u o = out16<kOut, kE5M2>(stage, c, part, nb[rr], m, smask, mmask, a.scale);
+            __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(a.out + (v0 + uint64_t(c) * kChunk +
+                                                                           uint64_t(ph * kPhase + part * S::kVals)) *
+                                                                              S::kOutBytes));
+        }
+    } else {
+#pragma unroll
+        for (int rr = 0; rr < S::kRounds; ++rr) {
+            const int c = rr * (kLanes / S::kPartLanes) + (lane >> S::kPartShift), part = lane & (S::kPartLanes - 1);
+            const uint32_t v = uint32_t(c * kChunk + ph * kPhase + part * S::kVals);
+            if (c < l0 || c >= l1 || v >= nvals) continue;
+            const v4u o = out16<kOut, kE5M2>(stage, c, part, nb[rr], m, smask, mmask, a.scale);
+            uint8_t* dst = a.out + (v0 + v) * S::kOutBytes;
+            if (v + S::kVals <= nvals) {
+                *reinterpret_cast<v4u*>(dst) = o;
+            } else {
+                for (uint32_t i = 0; i < (nvals - v) * S::kOutBytes; ++i) {
+                    const uint32_t wd = i < 4 ? o.x : i < 8 ? o.y : i < 12 ? o.z : o.w;
+                    dst[i] = uint8_t(wd >> (8 * (i & 3)));
+                }
+            }
+        }
+    }
+}
+
+template <int kOut>
 __global__ __launch_bounds__(kThreads) void e8huf_decode_kernel(Args a) {
+    using S = OutStage<kOut>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsStatic];
     __shared__ uint32_t local_ticket;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
@@ -392,42 +516,50 @@ __global__ __launch_bounds__(kThreads) void e8huf_decode_kernel(Args a) {
                     const uint32_t base = uint32_t(ph * kPhase);
                     // the phase's nibbles, requested before its decode so that
                     // the loads overlap it
-                    uint2 nb[kRounds];
+                    typename S::Nib nb[S::kRounds];
 #pragma unroll
-                    for (int rr = 0; rr < kRounds; ++rr) {
-                        const uint32_t v = uint32_t((rr * (kLanes / kPartLanes) + (lane >> kPartShift)) * kChunk +
-                                                    ph * kPhase + (lane & (kPartLanes - 1)) * 16);
+                    for (int rr = 0; rr < S::kRounds; ++rr) {
+                        const uint32_t v = uint32_t((rr * (kLanes / S::kPartLanes) + (lane >> S::kPartShift)) * kChunk +
+                                                    ph * kPhase + (lane & (S::kPartLanes - 1)) * S::kVals);
                         const uint64_t at = v < nvals ? (v0 + v) / 2 : 0ull;
-                        nb[rr] = *reinterpret_cast<const uint2*>(nib + at);
+                        nb[rr] = *reinterpret_cast<const typename S::Nib*>(nib + at);
                     }
                     decode_phase(tab, l2, l2_last, buf, row, min(base + kPhase, my_cnt), base, ls);
                     wave_sync();
-                    if (full && l0 == 0 && l1 == kLanes) {
+                    const bool whole = full && l0 == 0 && l1 == kLanes;
+                    if constexpr (kOut == kOutFp8) {
+                        if (whole) {
 #pragma unroll
-                        for (int rr = 0; rr < kRounds; ++rr) {
-                            const int c = rr * (kLanes / kPartLanes) + (lane >> kPartShift), part = lane & (kPartLanes - 1);
-                            const v4u o = combine(staged16(stage, c, part), nb[rr], m, smask, mmask);
-                            __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(a.out + v0 + uint64_t(c) * kChunk +
-                                                                                   uint64_t(ph * kPhase + part * 16)));
-                        }
-                    } else {
+                            for (int rr = 0; rr < S::kRounds; ++rr) {
+                                const int c = rr * (kLanes / S::kPartLanes) + (lane >> S::kPartShift),
+                                          part = lane & (S::kPartLanes - 1);
+                                const v4u o = combine(staged16(stage, c, part), nb[rr], m, smask, mmask);
+                                __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(a.out + v0 + uint64_t(c) * kChunk +
+                                                                                       uint64_t(ph * kPhase + part * 16)));
+                            }
+                        } else {
 #pragma unroll
-                        for (int rr = 0; rr < kRounds; ++rr) {
-                            const int c = rr * (kLanes / kPartLanes) + (lane >> kPartShift), part = lane & (kPartLanes - 1);
-                            const uint32_t v = uint32_t(c * kChunk + ph * kPhase + part * 16);
-                            if (c < l0 || c >= l1 || v >= nvals) continue;
-                            const v4u o = combine(staged16(stage, c, part), nb[rr], m, smask, mmask);
-                            uint8_t* dst = a.out + v0 + v;
-                            if (v + 16 <= nvals) {
-                                *reinterpret_cast<v4u*>(dst) = o;
-                            } else {
-                                for (uint32_t i = 0; i < nvals - v; ++i) {
-                                    const uint32_t wd = i < 4 ? o.x : i < 8 ? o.y : i < 12 ? o.z : o.w;
-                                    dst[i] = uint8_t(wd >> (8 * (i & 3)));
+                            for (int rr = 0; rr < S::kRounds; ++rr) {
+                                const int c = rr * (kLanes / S::kPartLanes) + (lane >> S::kPartShift),
+                                          part = lane & (S::kPartLanes - 1);
+                                const uint32_t v = uint32_t(c * kChunk + ph * kPhase + part * 16);
+                                if (c < l0 || c >= l1 || v >= nvals) continue;
+                                const v4u o = combine(staged16(stage, c, part), nb[rr], m, smask, mmask);
+                                uint8_t* dst = a.out + v0 + v;
+                                if (v + 16 <= nvals) {
+                                    *reinterpret_cast<v4u*>(dst) = o;
+                                } else {
+                                    for (uint32_t i = 0; i < nvals - v; ++i) {
+                                        const uint32_t wd = i < 4 ? o.x : i < 8 ? o.y : i < 12 ? o.z : o.w;
+                                        dst[i] = uint8_t(wd >> (8 * (i & 3)));
+                                    }
                                 }
                             }
                         }
-                    }
+                    } else if (exp_bits == 5u)
+                        store_phase<kOut, true>(a, stage, nb, v0, nvals, ph, whole, l0, l1, lane, m, smask, mmask);
+                    else
+                        store_phase<kOut, false>(a, stage, nb, v0, nvals, ph, whole, l0, l1, lane, m, smask, mmask);
                     wave_sync();
                 }
                 // the last lookup may have taken symbols past the lane's
@@ -471,12 +603,10 @@ int device_cus(int* out) {
     return K3HUF_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int e8huf_decode(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut, int lut_entries, void* d_out,
-                 uint64_t n_values, void* stream, uint32_t* d_status) {
+// Argument checks and the launch shared by both entry points.
+template <int kOut>
+int launch(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut, int lut_entries, void* d_out,
+           uint64_t n_values, float scale, void* stream, uint32_t* d_status) {
     if (!d_blob || !d_lut || !d_out) return K3HUF_E_ARG;
     if ((reinterpret_cast<uintptr_t>(d_blob) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 15) ||
         (reinterpret_cast<uintptr_t>(d_lut) & 1) || (reinterpret_cast<uintptr_t>(d_status) & 3))
@@ -500,9 +630,28 @@ int e8huf_decode(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut, i
     a.out = static_cast<uint8_t*>(d_out);
     a.n = n_values;
     a.status = d_status;
-    hipLaunchKernelGGL(e8huf_decode_kernel, dim3(grid), dim3(kThreads), size_t(lut_entries) * 2,
+    a.scale = scale;
+    hipLaunchKernelGGL(e8huf_decode_kernel<kOut>, dim3(grid), dim3(kThreads), size_t(lut_entries) * 2,
                        static_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? K3HUF_OK : K3HUF_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int e8huf_decode(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut, int lut_entries, void* d_out,
+                 uint64_t n_values, void* stream, uint32_t* d_status) {
+    return launch<kOutFp8>(d_blob, blob_bytes, d_lut, lut_entries, d_out, n_values, 1.0f, stream, d_status);
+}
+
+int e8huf_decode_widen(const void* d_blob, size_t blob_bytes, const uint16_t* d_lut, int lut_entries, void* d_out,
+                       uint64_t n_values, int out_kind, float scale, void* stream, uint32_t* d_status) {
+    if (out_kind == E8HUF_OUT_BF16)
+        return launch<E8HUF_OUT_BF16>(d_blob, blob_bytes, d_lut, lut_entries, d_out, n_values, scale, stream, d_status);
+    if (out_kind == E8HUF_OUT_F16)
+        return launch<E8HUF_OUT_F16>(d_blob, blob_bytes, d_lut, lut_entries, d_out, n_values, scale, stream, d_status);
+    return K3HUF_E_ARG;
 }
 
 }  // extern "C"

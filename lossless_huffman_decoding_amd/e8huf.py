@@ -13,8 +13,9 @@ from . import k3huf
 LUT_MAX = 256 * 18        # E8HUF_LUT_MAX
 HDR_BYTES = 128
 DEV_HEADER, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 4, 8, 16
+OUT_BF16, OUT_F16 = 1, 2  # E8HUF_OUT_*
 EXPORTS = ("e8huf_build_table", "e8huf_layer_info", "e8huf_encode_bound", "e8huf_encode",
-           "e8huf_decode")
+           "e8huf_decode", "e8huf_decode_widen")
 
 
 class Info(ctypes.Structure):
@@ -41,6 +42,9 @@ def lib() -> ctypes.CDLL:
         L.e8huf_encode.restype = ctypes.c_int64
         L.e8huf_decode.argtypes = [vp, sz, vp, ctypes.c_int, vp, ctypes.c_uint64, vp, vp]
         L.e8huf_decode.restype = ctypes.c_int
+        L.e8huf_decode_widen.argtypes = [vp, sz, vp, ctypes.c_int, vp, ctypes.c_uint64, ctypes.c_int,
+                                         ctypes.c_float, vp, vp]
+        L.e8huf_decode_widen.restype = ctypes.c_int
         _ready = True
     return L
 
@@ -100,3 +104,28 @@ def decode_raw(blob_ptr, blob_bytes, lut_ptr, lut_entries, out_ptr, n_values, st
     """Unchecked pointer-level call; returns the C return code."""
     return lib().e8huf_decode(blob_ptr, blob_bytes, lut_ptr, lut_entries, out_ptr, n_values, stream,
                               status_ptr)
+
+
+def decode_widen(d_blob, d_lut, d_out, out_kind=None, scale: float = 1.0, d_status=None, stream=None) -> None:
+    """Queue the decode of one container into 16-bit floats: d_out holds the
+    tensor's value count of bfloat16 or float16 elements (out_kind defaults
+    from its dtype: OUT_BF16, OUT_F16); element i is value i times scale,
+    rounded to nearest even."""
+    if out_kind is None:
+        import torch
+        out_kind = {torch.bfloat16: OUT_BF16, torch.float16: OUT_F16}.get(d_out.dtype)
+        if out_kind is None:
+            raise ValueError("decode_widen: d_out must be bfloat16 or float16 (or give out_kind)")
+    if d_out.element_size() != 2:
+        raise ValueError("decode_widen: d_out must hold 16-bit elements")
+    rc = lib().e8huf_decode_widen(d_blob.data_ptr(), k3huf._nbytes(d_blob), d_lut.data_ptr(), d_lut.numel(),
+                                  d_out.data_ptr(), d_out.numel(), out_kind, float(scale),
+                                  k3huf._stream_handle(stream), d_status.data_ptr() if d_status is not None else None)
+    k3huf._check(rc, "e8huf_decode_widen")
+
+
+def decode_widen_raw(blob_ptr, blob_bytes, lut_ptr, lut_entries, out_ptr, n_values, out_kind, scale, stream,
+                     status_ptr) -> int:
+    """Unchecked pointer-level call; returns the C return code."""
+    return lib().e8huf_decode_widen(blob_ptr, blob_bytes, lut_ptr, lut_entries, out_ptr, n_values, out_kind, scale,
+                                    stream, status_ptr)

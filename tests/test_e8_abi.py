@@ -172,3 +172,14 @@ def test_decode_rejects_bad_arguments_before_any_device_call():
     assert raw(blob, good, lut, 256 * 19, out, 100, None, None) == k3huf.E_ARG
     assert raw(blob, 1 << 44, lut, 256, out, 100, None, None) == k3huf.E_ARG    # blob too large
     assert raw(blob, good, lut, 256, out, (1 << 40) + 1, None, None) == k3huf.E_ARG
+    # the widening entry point: the same checks, and the output kind
+    w = e8huf.decode_widen_raw
+    for kind in (e8huf.OUT_BF16, e8huf.OUT_F16):
+        assert w(0, good, lut, 256, out, 100, kind, 1.0, None, None) == k3huf.E_ARG
+        assert w(blob, good, lut, 256, out + 2, 100, kind, 1.0, None, None) == k3huf.E_ARG   # misaligned output
+        assert w(blob, good, lut + 1, 256, out, 100, kind, 1.0, None, None) == k3huf.E_ARG
+        assert w(blob, good, lut, 256, out, 0, kind, 1.0, None, None) == k3huf.E_ARG
+        assert w(blob, good, lut, 300, out, 100, kind, 1.0, None, None) == k3huf.E_ARG
+        assert w(blob, 1 << 44, lut, 256, out, 100, kind, 1.0, None, None) == k3huf.E_ARG
+    for kind in (0, 3, -1):
+        assert w(blob, good, lut, 256, out, 100, kind, 1.0, None, None) == k3huf.E_ARG
