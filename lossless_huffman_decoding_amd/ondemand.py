@@ -17,6 +17,11 @@ instead in the FP8 exponent format (e8huf_encode, the library's native host
 packer: the group's bytes go to the host once, at attach time) with its
 two-level table, and decoded by e8huf_decode into the same buffers. The
 members of one group share one dtype; groups of either kind mix freely.
+With fp8_as=torch.bfloat16 (or torch.float16) FP8 groups are decoded by
+e8huf_decode_widen straight into that type instead (scale 1: every E4M3 and
+E5M2 value is exact in bfloat16, and every E5M2 value in half), as the
+page's decoder hands over 16-bit floats: members then see 16-bit weights
+holding their FP8 values, and no widening pass runs before their products.
 
 Two schedules:
   - lookahead=False (default): one buffer; the group's decode is queued on
@@ -55,16 +60,20 @@ class OnDemandWeights:
     group on use.
 
     ``attach(module)`` makes a group of one; ``attach_group(modules)`` packs
-    the modules' weights together. Attach in the order the groups run. The
+    the modules' weights together. ``fp8_as`` (None, torch.bfloat16,
+    torch.float16): the type FP8 weights are handed to their modules in. Attach in the order the groups run. The
     dense weights are freed. ``buffer_bytes`` reports the decode buffers (one
     or two of the largest group's size); ``resident_bytes`` the containers and
     tables kept in HBM. ``status`` is the device word the decodes flag
     malformed input in (read by ``check()``, which synchronizes).
     """
 
-    def __init__(self, device="cuda:0", lookahead: bool = False):
+    def __init__(self, device="cuda:0", lookahead: bool = False, fp8_as=None):
+        if fp8_as not in (None, torch.bfloat16, torch.float16):
+            raise ValueError("fp8_as: None (FP8 bytes), torch.bfloat16 or torch.float16")
         self.device = torch.device(device)
         self.lookahead = lookahead
+        self.fp8_as = fp8_as
         n = 2 if lookahead else 1
         self._bufs = [torch.empty(0, dtype=torch.uint8, device=self.device) for _ in range(n)]
         self._groups = []
@@ -123,24 +132,36 @@ class OnDemandWeights:
             info = e8huf.layer_info(hblob[: e8huf.HDR_BYTES])
             blob = torch.from_numpy(hblob).to(self.device)
             lut = torch.from_numpy(e8huf.build_table(info["codelen"], eb).view(np.int16)).to(self.device)
-            fn, fname = self._lib.e8huf_decode, "e8huf_decode"
+            if self.fp8_as is None:
+                fn, fname = self._lib.e8huf_decode, "e8huf_decode"
+            else:
+                fn, fname = self._lib.e8huf_decode_widen, "e8huf_decode_widen"
         del raw, parts
+        # what the buffer holds for this group: its dtype and bytes per value
+        # of the weights (FP8 widened: 2 bytes per FP8 byte)
+        out_dtype = dtype if dtype == torch.bfloat16 or self.fp8_as is None else self.fp8_as
+        k = 2 if (dtype != torch.bfloat16 and self.fp8_as is not None) else 1
         g = {"blob": blob, "lut": lut, "raw_bytes": off, "name": name, "members": members,
-             "index": len(self._groups), "dtype": dtype, "fn": fn, "fname": fname}
+             "index": len(self._groups), "dtype": dtype, "out_dtype": out_dtype, "k": k, "fn": fn,
+             "fname": fname}
         self._groups.append(g)
         for i, b in enumerate(self._bufs):
-            if off > b.numel():
-                self._bufs[i] = torch.empty(off, dtype=torch.uint8, device=self.device)
+            if off * k > b.numel():
+                self._bufs[i] = torch.empty(off * k, dtype=torch.uint8, device=self.device)
         # per buffer: the decode call's arguments and the members' weight views
         # (the hooks run per forward, so they only look these up)
-        # (both decode calls end in stream, status)
+        # (every decode call ends in stream, status)
         for x in self._groups:
             x["calls"] = [(x["blob"].data_ptr(), x["blob"].numel(), x["lut"].data_ptr(), b.data_ptr(),
                            x["raw_bytes"]) if x["dtype"] == torch.bfloat16 else
                           (x["blob"].data_ptr(), x["blob"].numel(), x["lut"].data_ptr(), x["lut"].numel(),
-                           b.data_ptr(), x["raw_bytes"]) for b in self._bufs]
-            x["views"] = [[b[o: o + n].view(x["dtype"]).view(shape) for (_, o, n, shape) in x["members"]]
+                           b.data_ptr(), x["raw_bytes"]) if x["k"] == 1 else
+                          (x["blob"].data_ptr(), x["blob"].numel(), x["lut"].data_ptr(), x["lut"].numel(),
+                           b.data_ptr(), x["raw_bytes"],
+                           e8huf.OUT_BF16 if x["out_dtype"] == torch.bfloat16 else e8huf.OUT_F16, 1.0)
                           for b in self._bufs]
+            x["views"] = [[b[o * x["k"]: (o + n) * x["k"]].view(x["out_dtype"]).view(shape)
+                           for (_, o, n, shape) in x["members"]] for b in self._bufs]
         for j, (m, _, _, _) in enumerate(members):
             self._by_module[id(m)] = (g, j)
             if name in m._parameters:

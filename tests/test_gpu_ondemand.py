@@ -87,7 +87,7 @@ def test_on_demand_on_a_side_stream(lookahead):
     assert torch.equal(got, want)
 
 
-@pytest.mark.parametrize("weights", ["bf16", "fp8"])
+@pytest.mark.parametrize("weights", ["bf16", "fp8", "fp8_as_bf16"])
 def test_on_demand_forward_captured_in_a_graph(weights):
     """The hooked forward (one buffer, decodes on the capturing stream)
     captured once and replayed: every replay equals the dense forward, with
@@ -99,7 +99,7 @@ def test_on_demand_forward_captured_in_a_graph(weights):
     x = torch.randn(4, 512, generator=torch.Generator().manual_seed(8)).to(torch.bfloat16).to(DEV)
     with torch.no_grad():
         want = model(x)
-    od = OnDemandWeights(DEV, lookahead=False)
+    od = OnDemandWeights(DEV, lookahead=False, fp8_as=torch.bfloat16 if weights == "fp8_as_bf16" else None)
     for m in model:
         od.attach(m)
     s = torch.cuda.Stream()
@@ -177,33 +177,37 @@ def _fp8_stack(shapes, fmts, seed):
     return torch.nn.Sequential(*layers)
 
 
+@pytest.mark.parametrize("fp8_as", [None, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("lookahead", [False, True])
-def test_on_demand_fp8_weights(lookahead):
+def test_on_demand_fp8_weights(lookahead, fp8_as):
     """FP8 weights (E4M3 and E5M2 groups) beside a bf16 group: each FP8
-    group is one E8HF container decoded by e8huf_decode into the shared
-    buffers. Every forward equals the dense one bit for bit, the FP8 views
-    hold the original bytes, and the containers are smaller than the
-    weights."""
+    group is one E8HF container decoded into the shared buffers, as FP8
+    bytes (e8huf_decode) or widened to 16-bit floats (e8huf_decode_widen;
+    the modules' own widening is then a no-op or exact). Every forward equals
+    the dense one bit for bit, the views hold the original values, and the
+    containers are smaller than the weights."""
     shapes = [(1024, 512), (768, 1024), (512, 768), (640, 512), (512, 640)]
     fmts = ["e4m3", "e4m3", "bf16", "e5m2", "e5m2"]
     model = _fp8_stack(shapes, fmts, 1100)
     x = torch.randn(3, 512, generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).to(DEV)
     dense = [m.weight.detach().clone() for m in model]
-    say("ondemand fp8 dense forward", lookahead)
+    say("ondemand fp8 dense forward", lookahead, fp8_as)
     with torch.no_grad():
         want = model(x)
         want_last = model[4](model[3](torch.ones(2, 512, dtype=torch.bfloat16, device=DEV)))
-    od = OnDemandWeights(DEV, lookahead=lookahead)
+    od = OnDemandWeights(DEV, lookahead=lookahead, fp8_as=fp8_as)
     od.attach_group([model[0], model[1]])
     od.attach(model[2])
     od.attach_group([model[3], model[4]])
     weight_bytes = [1024 * 512 + 768 * 1024, 512 * 768 * 2, 640 * 512 * 2]
-    assert od.buffer_bytes == max(weight_bytes) * (2 if lookahead else 1)
+    wide = 1 if fp8_as is None else 2
+    buffer_bytes = [weight_bytes[0] * wide, weight_bytes[1], weight_bytes[2] * wide]
+    assert od.buffer_bytes == max(buffer_bytes) * (2 if lookahead else 1)
     assert od._groups[0]["blob"][:4].cpu().numpy().tobytes() == b"E8HF"
     assert od._groups[1]["blob"][:4].cpu().numpy().tobytes() == b"K3HF"
     fp8_blobs = od._groups[0]["blob"].numel() + od._groups[2]["blob"].numel()
     assert fp8_blobs < weight_bytes[0] + weight_bytes[2] // 2
-    say("ondemand fp8 hooked forward", lookahead)
+    say("ondemand fp8 hooked forward", lookahead, fp8_as)
     with torch.no_grad():
         got = model(x)
         got2 = model(x)
@@ -216,6 +220,11 @@ def test_on_demand_fp8_weights(lookahead):
     for (o, i), m, d in zip(shapes, model, dense):
         with torch.no_grad():
             m(torch.ones(1, i, dtype=torch.bfloat16, device=DEV))
-        assert m.weight.dtype == d.dtype and m.weight.shape == (o, i)
-        assert torch.equal(m.weight.view(torch.uint8), d.view(torch.uint8))
+        assert m.weight.shape == (o, i)
+        if d.dtype == torch.bfloat16 or fp8_as is None:
+            assert m.weight.dtype == d.dtype
+            assert torch.equal(m.weight.view(torch.uint8), d.view(torch.uint8))
+        else:
+            assert m.weight.dtype == fp8_as
+            assert torch.equal(m.weight.view(torch.int16), d.to(fp8_as).view(torch.int16))
     od.check()
