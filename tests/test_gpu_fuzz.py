@@ -61,4 +61,19 @@ def test_fuzz_e8_decode(seed):
     torch.cuda.synchronize()
     assert int(st.item()) == 0, what
     assert (dec.cpu().numpy() == x).all(), what
+    # the same container into 16-bit floats (bfloat16 on even seeds, half on
+    # odd ones) times a seeded scale, against the oracle's widening
+    kind = e8huf.OUT_BF16 if seed % 2 == 0 else e8huf.OUT_F16
+    scale = float(np.float32(2.0 ** np.random.default_rng((seed, 16)).uniform(-20, 8)))
+    wide = torch.full((x.size,), 0x5A5A, dtype=torch.int16, device=DEV)
+    print("[gpu-case] fuzz e8 widen", seed, kind, scale, flush=True)
+    e8huf.decode_widen(d_blob, d_lut, wide, out_kind=kind, scale=scale, d_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0, what
+    got = wide.cpu().numpy().view(np.uint16)
+    want = O.e8_widen(x, eb, scale, kind)
+    ex, fr = (0x7F80, 0x7F) if kind == e8huf.OUT_BF16 else (0x7C00, 0x3FF)
+    nan = ((want & ex) == ex) & ((want & fr) != 0)
+    assert np.array_equal(got[~nan], want[~nan]), what
+    assert np.all(((got[nan] & ex) == ex) & ((got[nan] & fr) != 0)), what
 
