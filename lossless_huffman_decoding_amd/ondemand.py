@@ -60,12 +60,14 @@ class OnDemandWeights:
     group on use.
 
     ``attach(module)`` makes a group of one; ``attach_group(modules)`` packs
-    the modules' weights together. ``fp8_as`` (None, torch.bfloat16,
-    torch.float16): the type FP8 weights are handed to their modules in. Attach in the order the groups run. The
-    dense weights are freed. ``buffer_bytes`` reports the decode buffers (one
-    or two of the largest group's size); ``resident_bytes`` the containers and
-    tables kept in HBM. ``status`` is the device word the decodes flag
-    malformed input in (read by ``check()``, which synchronizes).
+    the modules' weights together. Attach in the order the groups run. The
+    dense weights are freed. ``fp8_as`` (None, torch.bfloat16 or
+    torch.float16) is the type FP8 weights are handed to their modules in
+    (None: FP8 as stored). ``buffer_bytes`` reports the decode buffers (one
+    or two of the largest group's decoded size); ``resident_bytes`` the
+    containers and tables kept in HBM. ``status`` is the device word the
+    decodes flag malformed input in (read by ``check()``, which
+    synchronizes).
     """
 
     def __init__(self, device="cuda:0", lookahead: bool = False, fp8_as=None):
