@@ -228,3 +228,24 @@ def test_on_demand_fp8_weights(lookahead, fp8_as):
             assert m.weight.dtype == fp8_as
             assert torch.equal(m.weight.view(torch.int16), d.to(fp8_as).view(torch.int16))
     od.check()
+
+
+def test_on_demand_rejects_what_it_cannot_hold():
+    """Argument errors are raised at attach time, before any weight is
+    touched: a group mixing dtypes, an unsupported dtype, a weight on the
+    host, an empty group and an unsupported fp8_as."""
+    say("ondemand argument errors")
+    with pytest.raises(ValueError):
+        OnDemandWeights(DEV, fp8_as=torch.float32)
+    od = OnDemandWeights(DEV)
+    a = torch.nn.Linear(64, 32, bias=False, dtype=torch.bfloat16, device=DEV)
+    b = _FP8Linear(torch.zeros(32, 64, dtype=torch.uint8, device=DEV).view(torch.float8_e4m3fn), 1.0)
+    with pytest.raises(ValueError):
+        od.attach_group([a, b])
+    with pytest.raises(ValueError):
+        od.attach(torch.nn.Linear(64, 32, bias=False, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        od.attach(torch.nn.Linear(64, 32, bias=False, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        od.attach_group([])
+    assert od.resident_bytes == 0 and a.weight is not None and b.weight is not None
