@@ -12,7 +12,8 @@
  * 8 bits), and metadata per thread block records its bit offset and its start
  * in the symbol stream. Section 2.2: the GPU decoder gives each thread its
  * start bit from that metadata, decodes into on-chip memory and writes out
- * coalesced.
+ * coalesced; its output is 16-bit floats (e8huf_decode_widen), or here also
+ * the FP8 bytes themselves (e8huf_decode).
  *
  * All functions are plain C: pointers and sizes only. A "stream" is a
  * hipStream_t passed as void* (NULL = the null stream). Return codes are the
