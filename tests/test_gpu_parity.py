@@ -79,6 +79,52 @@ def test_edge_parity(layer):
     assert (got == want).all()
 
 
+# The decode kernel's per-wave bitstream buffer (7,680 bytes), in 16-byte
+# units: a full unit whose code span fits it is copied into LDS whole; a
+# larger one takes the per-lane gather path; the layer's partial last unit
+# runs in passes over lane ranges whose span fits the buffer.
+KERNEL_BUF_UNITS = 7680 // 16
+
+
+def unit_paths(blob):
+    """Each 256-symbol-layout unit's decode path, from the container's index
+    as include/k3huf.h lays it out: 'fill' or 'gather' for a full unit
+    (32,768 output bytes), ('tail', passes) for a partial one. A unit's span
+    runs from the 16 bytes holding the bit before its first code to two
+    dwords past the dword of its last bit, rounded up to 16 bytes."""
+    info = k3huf.layer_info(blob)
+    assert info["lane_syms"] == 256
+    first16 = lambda p: ((p - 1) >> 5) & ~3          # noqa: E731  (dwords)
+    end16 = lambda p: (((p - 1) >> 5) + 6) & ~3      # noqa: E731
+    paths = []
+    for s in range(info["n_stripes"]):
+        so = int(np.frombuffer(bytes(blob[304 + 8 * s: 312 + 8 * s]), "<u8")[0])
+        n_sub = int(np.frombuffer(bytes(blob[so + 20: so + 24]), "<u4")[0])
+        for j in range(n_sub):
+            r = so + 32 + 264 * j
+            start, nsyms = (int(v) for v in np.frombuffer(bytes(blob[r: r + 8]), "<u4"))
+            lb = np.frombuffer(bytes(blob[r + 8: r + 264]), "<u2").astype(np.int64)
+            for half in (0, 1):
+                syms = min(max(nsyms - half * 16384, 0), 16384)
+                if syms == 0:
+                    continue
+                ends = start + np.cumsum(lb)[64 * half: 64 * half + 64]
+                starts = ends - lb[64 * half: 64 * half + 64]
+                if syms == 16384:
+                    units = (end16(int(ends[63])) - first16(int(starts[0]))) // 4
+                    paths.append("fill" if units <= KERNEL_BUF_UNITS else "gather")
+                else:
+                    l0, passes = 0, 0
+                    while l0 < 64:
+                        j0 = first16(int(starts[l0]))
+                        l1 = l0 + 1
+                        while l1 < 64 and end16(int(ends[l1])) - j0 <= 4 * KERNEL_BUF_UNITS:
+                            l1 += 1
+                        l0, passes = l1, passes + 1
+                    paths.append(("tail", passes))
+    return paths
+
+
 @pytest.mark.parametrize("n_bytes", [65536, 65536 + 2 * 12000, 3 * 65536 + 2 * 20000 + 2,
                                      2 * 65536 - 2, 4 * 65536 + 2 * 7000])
 def test_units_over_the_lds_buffer(n_bytes):
@@ -88,7 +134,10 @@ def test_units_over_the_lds_buffer(n_bytes):
     decodes in several passes over lane ranges."""
     x = synth.edge_uniform(seed=700 + n_bytes % 97, n_bytes=n_bytes)
     blob = O.encode_layer(x)
-    say("over buffer", n_bytes)
+    paths = unit_paths(blob)
+    assert "gather" in paths and "fill" not in paths
+    assert paths[-1] in ("gather", ("tail", 1), ("tail", 2), ("tail", 3))
+    say("over buffer", n_bytes, paths[-1])
     got, st = gpu_decode(blob)
     assert st == 0
     assert (got == x).all()
@@ -97,17 +146,43 @@ def test_units_over_the_lds_buffer(n_bytes):
 
 def test_some_units_over_the_lds_buffer():
     """Weights with two half-subblocks of uniform high bytes: those units'
-    codes are long (the rare symbols get long codes) and exceed the buffer,
-    while their neighbours fit it."""
+    codes are long (the rare symbols get codes of 11-12 bits) and exceed the
+    buffer, while their neighbours fit it."""
     x = synth.small_random(21, 8 * 65536 + 4098).copy()
     rng = np.random.default_rng(5)
     for start in (65536 + 32768, 5 * 65536):   # a second-half and a first-half unit
         x[start + 1: start + 32768: 2] = rng.integers(0, 256, 16384, dtype=np.uint8)
     blob = O.encode_layer(x)
+    paths = unit_paths(blob)
+    assert paths.count("gather") == 2 and paths.count("fill") == len(paths) - 3
     say("some units over buffer")
     got, st = gpu_decode(blob)
     assert st == 0
     assert (got == x).all()
+
+
+@pytest.mark.parametrize("tail_syms", [3000, 9000, 12000, 15000, 16382])
+def test_partial_last_unit_in_passes(tail_syms):
+    """Weights, then a partial last unit of uniform high bytes (rare symbols
+    with codes of 11-12 bits, so 3-4 times the 8-bit case's bits per symbol):
+    it decodes in one pass when its codes fit the buffer and in two to four
+    passes over lane ranges when they do not; full units of such bytes, or
+    of half such bytes, before it take the gather path."""
+    x = synth.small_random(31, 10 * 65536 + 2 * tail_syms).copy()
+    rng = np.random.default_rng(tail_syms)
+    x[10 * 65536 + 1::2] = rng.integers(0, 256, tail_syms, dtype=np.uint8)
+    x[9 * 65536 + 32768 + 1: 10 * 65536: 2] = rng.integers(0, 256, 16384, dtype=np.uint8)
+    x[8 * 65536 + 1: 8 * 65536 + 16384: 2] = rng.integers(0, 256, 8192, dtype=np.uint8)
+    blob = O.encode_layer(x)
+    paths = unit_paths(blob)
+    want = 1 if tail_syms * 12 <= 7680 * 8 - 64 else 2
+    assert paths[-1][0] == "tail" and paths[-1][1] >= want
+    assert paths.count("gather") == 2
+    say("partial last unit in passes", tail_syms, paths[-1])
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got == x).all()
+    assert (got == O.decode_layer(blob)).all()
 
 
 def test_heavy_parity():
