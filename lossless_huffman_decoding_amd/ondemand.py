@@ -147,9 +147,15 @@ class OnDemandWeights:
              "index": len(self._groups), "dtype": dtype, "out_dtype": out_dtype, "k": k, "fn": fn,
              "fname": fname}
         self._groups.append(g)
-        for i, b in enumerate(self._bufs):
-            if off * k > b.numel():
-                self._bufs[i] = torch.empty(off * k, dtype=torch.uint8, device=self.device)
+        if any(off * k > b.numel() for b in self._bufs):
+            # a larger buffer replaces the old one: decodes and forwards still
+            # queued may use the old one (on any stream), and what it holds
+            # does not carry over
+            torch.cuda.synchronize(self.device)
+            for i, b in enumerate(self._bufs):
+                if off * k > b.numel():
+                    self._bufs[i] = torch.empty(off * k, dtype=torch.uint8, device=self.device)
+                    self._pending[i] = None
         # per buffer: the decode call's arguments and the members' weight views
         # (the hooks run per forward, so they only look these up)
         # (every decode call ends in stream, status)

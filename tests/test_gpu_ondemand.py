@@ -147,6 +147,32 @@ def test_on_demand_groups(lookahead):
     assert torch.equal(a, want) and torch.equal(b, want)
 
 
+@pytest.mark.parametrize("lookahead", [False, True])
+def test_on_demand_attach_after_a_forward(lookahead):
+    """Modules attached after forwards have run: a larger group replaces the
+    decode buffers, so the groups decoded into the old ones are decoded
+    again on their next use rather than read from the new, unwritten
+    buffers."""
+    model = _stack([(512, 256), (256, 512), (1024, 256), (256, 1024)], 1100)
+    x = torch.randn(4, 256, generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).to(DEV)
+    with torch.no_grad():
+        want01 = model[1](model[0](x))
+        want = model(x)
+    od = OnDemandWeights(DEV, lookahead=lookahead)
+    od.attach_group([model[0], model[1]])
+    say("ondemand attach after a forward", lookahead)
+    with torch.no_grad():
+        first = model[1](model[0](x))
+    small = od.buffer_bytes
+    od.attach_group([model[2], model[3]])    # twice the bytes: new buffers
+    assert od.buffer_bytes == 2 * small
+    with torch.no_grad():
+        again = model[1](model[0](x))        # group 0 again, into the new buffers
+        full = model(x)
+    od.check()
+    assert torch.equal(first, want01) and torch.equal(again, want01) and torch.equal(full, want)
+
+
 class _FP8Linear(torch.nn.Module):
     """A weight-only FP8 linear map: y = x (scale * W)^T, W held as FP8 and
     widened to bf16 on use (the ECF8 page's setting: FP8 weights, decoded
