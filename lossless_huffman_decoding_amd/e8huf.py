@@ -94,9 +94,12 @@ def decode(d_blob, d_lut, d_out, d_status=None, stream=None) -> None:
     """Queue the decode of one container: d_blob uint8 (the container),
     d_lut the table from build_table (16-bit entries), d_out uint8 of the
     tensor's value count, d_status a 32-bit device word or None."""
+    k3huf._dev(d_blob, "d_blob")
+    k3huf._dev(d_lut, "d_lut", elem=2)
+    k3huf._dev(d_out, "d_out")
     rc = lib().e8huf_decode(d_blob.data_ptr(), k3huf._nbytes(d_blob), d_lut.data_ptr(), d_lut.numel(),
-                            d_out.data_ptr(), d_out.numel(), k3huf._stream_handle(stream),
-                            d_status.data_ptr() if d_status is not None else None)
+                            d_out.data_ptr(), k3huf._nbytes(d_out), k3huf._stream_handle(stream),
+                            k3huf._status(d_status))
     k3huf._check(rc, "e8huf_decode")
 
 
@@ -116,11 +119,12 @@ def decode_widen(d_blob, d_lut, d_out, out_kind=None, scale: float = 1.0, d_stat
         out_kind = {torch.bfloat16: OUT_BF16, torch.float16: OUT_F16}.get(d_out.dtype)
         if out_kind is None:
             raise ValueError("decode_widen: d_out must be bfloat16 or float16 (or give out_kind)")
-    if d_out.element_size() != 2:
-        raise ValueError("decode_widen: d_out must hold 16-bit elements")
+    k3huf._dev(d_blob, "d_blob")
+    k3huf._dev(d_lut, "d_lut", elem=2)
+    k3huf._dev(d_out, "d_out", elem=2)
     rc = lib().e8huf_decode_widen(d_blob.data_ptr(), k3huf._nbytes(d_blob), d_lut.data_ptr(), d_lut.numel(),
                                   d_out.data_ptr(), d_out.numel(), out_kind, float(scale),
-                                  k3huf._stream_handle(stream), d_status.data_ptr() if d_status is not None else None)
+                                  k3huf._stream_handle(stream), k3huf._status(d_status))
     k3huf._check(rc, "e8huf_decode_widen")
 
 

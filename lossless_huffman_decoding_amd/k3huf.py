@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libk3huf.so")
 
 OK = 0
 HDR_BYTES = 304   # layer header size (K3HUF_HDR_BYTES)
+LUT_ENTRIES = 4096   # decode table entries (K3HUF_LUT_ENTRIES)
 E_ARG, E_EMPTY, E_OVERSUB, E_BADLEN, E_OVERLAP, E_FORMAT, E_CORRUPT, E_HIP = range(-1, -9, -1)
 DEV_HEADER, DEV_STRIPE, DEV_INDEX, DEV_CODE, DEV_LANE_END = 1, 2, 4, 8, 16
 
@@ -190,11 +191,13 @@ def encode_layer_dev(d_raw, d_out=None, d_work=None, stream=None, lane_syms: int
     encode_work_bytes) are allocated when None. Returns the container as a
     view of d_out (synchronous call)."""
     import torch
-    n = _nbytes(d_raw)
+    n = _nbytes(_dev(d_raw, "d_raw"))
     if d_out is None:
         d_out = torch.empty(encode_bound(n, lane_syms), dtype=torch.uint8, device=d_raw.device)
     if d_work is None:
         d_work = torch.empty(encode_work_bytes(n, lane_syms), dtype=torch.uint8, device=d_raw.device)
+    _dev(d_out, "d_out")
+    _dev(d_work, "d_work")
     size = _check(lib().k3huf_encode_layer_dev_lanes(d_raw.data_ptr(), n, lane_syms, d_out.data_ptr(),
                                                      _nbytes(d_out), d_work.data_ptr(), _nbytes(d_work),
                                                      _stream_handle(stream)), "k3huf_encode_layer_dev_lanes")
@@ -207,9 +210,10 @@ def encode_layer_dev_static(d_raw, d_out=None, stream=None):
     bytes). ``d_out`` is allocated here when None. Returns the container as a
     view of d_out (synchronous call)."""
     import torch
-    n = _nbytes(d_raw)
+    n = _nbytes(_dev(d_raw, "d_raw"))
     if d_out is None:
         d_out = torch.empty(encode_bound(n), dtype=torch.uint8, device=d_raw.device)
+    _dev(d_out, "d_out")
     size = _check(lib().k3huf_encode_layer_dev_static(d_raw.data_ptr(), n, d_out.data_ptr(),
                                                       _nbytes(d_out), _stream_handle(stream)),
                   "k3huf_encode_layer_dev_static")
@@ -218,6 +222,26 @@ def encode_layer_dev_static(d_raw, d_out=None, stream=None):
 
 def _nbytes(t) -> int:
     return t.numel() * t.element_size()
+
+
+def _dev(t, what: str, min_bytes: int = 0, elem: int = 0):
+    """Check a tensor handed to a kernel as a device pointer: a contiguous
+    GPU tensor of at least min_bytes (and elements of elem bytes when
+    given). The library reads or writes exactly what the call's sizes say,
+    so a host tensor, a strided view or a short buffer is refused here."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("%s: a GPU tensor is needed (got %s)" % (what, getattr(t, "device", type(t).__name__)))
+    if not t.is_contiguous():
+        raise ValueError("%s: a contiguous tensor is needed" % what)
+    if elem and t.element_size() != elem:
+        raise ValueError("%s: elements of %d bytes are needed (got %d)" % (what, elem, t.element_size()))
+    if _nbytes(t) < min_bytes:
+        raise ValueError("%s: at least %d bytes are needed (got %d)" % (what, min_bytes, _nbytes(t)))
+    return t
+
+
+def _status(d_status):
+    return _dev(d_status, "d_status", 4).data_ptr() if d_status is not None else None
 
 
 def _stream_handle(stream) -> int:
@@ -232,10 +256,12 @@ def decode_layer(d_blob, d_lut, d_out, d_status=None, stream=None) -> None:
     d_lut 4096 16-bit entries, d_out uint8 of the layer's raw size, d_status
     a 32-bit device word or None. Runs on ``stream`` (default: torch's
     current stream)."""
+    _dev(d_blob, "d_blob")
+    _dev(d_lut, "d_lut", 2 * LUT_ENTRIES)
+    _dev(d_out, "d_out")
     rc = lib().k3huf_decode_layer(
         d_blob.data_ptr(), _nbytes(d_blob), d_lut.data_ptr(),
-        d_out.data_ptr(), _nbytes(d_out), _stream_handle(stream),
-        d_status.data_ptr() if d_status is not None else None)
+        d_out.data_ptr(), _nbytes(d_out), _stream_handle(stream), _status(d_status))
     _check(rc, "k3huf_decode_layer")
 
 
@@ -249,6 +275,9 @@ def decode_layer_raw(blob_ptr: int, blob_bytes: int, lut_ptr: int, out_ptr: int,
 def stream_ref(d_in, d_out, grid: int, nontemporal: bool = False, stream=None) -> None:
     """Queue the streaming reference kernel (k3huf_stream_ref): read all of
     ``d_in`` (uint8 tensor, or None), write all of ``d_out``."""
+    if d_in is not None:
+        _dev(d_in, "d_in")
+    _dev(d_out, "d_out")
     _check(lib().k3huf_stream_ref(d_in.data_ptr() if d_in is not None else None,
                                   _nbytes(d_in) if d_in is not None else 0, d_out.data_ptr(), _nbytes(d_out),
                                   int(grid), int(bool(nontemporal)), _stream_handle(stream)),
@@ -263,14 +292,17 @@ def decode_ring(layers, slots, streams, cb=None, d_status=None) -> None:
     n = len(layers)
     arr = (RingLayer * max(n, 1))()
     for k, (blob, lut, raw) in enumerate(layers):
+        _dev(blob, "layer %d blob" % k)
+        _dev(lut, "layer %d table" % k, 2 * LUT_ENTRIES)
         arr[k] = RingLayer(blob.data_ptr(), _nbytes(blob), lut.data_ptr(), raw)
+    for i, sl in enumerate(slots):
+        _dev(sl, "slot %d" % i)
     slot_ptrs = (ctypes.c_void_p * len(slots))(*[s.data_ptr() for s in slots])
     stream_ptrs = (ctypes.c_void_p * len(streams))(*[_stream_handle(s) for s in streams])
     slot_bytes = min(_nbytes(s) for s in slots)
     c_cb = _ring_cb(cb, slots)
     rc = lib().k3huf_decode_ring(arr, n, slot_ptrs, len(slots), slot_bytes, stream_ptrs,
-                                 len(streams), c_cb, None,
-                                 d_status.data_ptr() if d_status is not None else None)
+                                 len(streams), c_cb, None, _status(d_status))
     _check(rc, "k3huf_decode_ring")
 
 
@@ -293,7 +325,12 @@ def decode_ring_host(layers, stages, slots, copy_stream, streams, cb=None, d_sta
     n = len(layers)
     arr = (HostLayer * max(n, 1))()
     for k, (blob, lut, raw) in enumerate(layers):
+        if getattr(blob, "is_cuda", True) or not blob.is_contiguous():
+            raise ValueError("layer %d blob: a contiguous host tensor is needed" % k)
+        _dev(lut, "layer %d table" % k, 2 * LUT_ENTRIES)
         arr[k] = HostLayer(blob.data_ptr(), _nbytes(blob), lut.data_ptr(), raw)
+    for i, t in enumerate(list(stages) + list(slots)):
+        _dev(t, "stage %d" % i if i < len(stages) else "slot %d" % (i - len(stages)))
     stage_ptrs = (ctypes.c_void_p * len(stages))(*[s.data_ptr() for s in stages])
     slot_ptrs = (ctypes.c_void_p * len(slots))(*[s.data_ptr() for s in slots])
     stream_ptrs = (ctypes.c_void_p * len(streams))(*[_stream_handle(s) for s in streams])
@@ -301,5 +338,5 @@ def decode_ring_host(layers, stages, slots, copy_stream, streams, cb=None, d_sta
     rc = lib().k3huf_decode_ring_host(arr, n, stage_ptrs, len(stages), min(_nbytes(s) for s in stages),
                                       slot_ptrs, len(slots), min(_nbytes(s) for s in slots),
                                       _stream_handle(copy_stream), stream_ptrs, len(streams), c_cb,
-                                      None, d_status.data_ptr() if d_status is not None else None)
+                                      None, _status(d_status))
     _check(rc, "k3huf_decode_ring_host")

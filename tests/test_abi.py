@@ -313,3 +313,47 @@ def test_gpu_packer_lane_syms_checked_before_any_device_call():
         assert L.k3huf_encode_work_bytes_lanes(1024, bad) == k3huf.E_ARG
         assert L.k3huf_encode_layer_dev_lanes(good, 1024, bad, good, 1 << 20, good, 1 << 20, None) == k3huf.E_ARG
     assert k3huf.encode_work_bytes(1 << 20, 64) > k3huf.encode_work_bytes(1 << 20)
+
+
+def test_bindings_refuse_host_and_short_tensors_before_any_device_call():
+    """The Python calls hand tensors to the kernels as device pointers: host
+    tensors, strided views, a table shorter than 4096 entries and tables of
+    other than 16-bit elements are refused with ValueError before the
+    library is called (CPU tensors here, so nothing reaches a GPU)."""
+    import torch
+    from lossless_huffman_decoding_amd import e8huf
+    blob = torch.zeros(4096, dtype=torch.uint8)
+    lut = torch.zeros(4096, dtype=torch.int16)
+    out = torch.zeros(4096, dtype=torch.uint8)
+    st = torch.zeros(1, dtype=torch.int32)
+    for call in (lambda: k3huf.decode_layer(blob, lut, out, st),
+                 lambda: k3huf.decode_ring([(blob, lut, 4096)], [out], [None]),
+                 lambda: k3huf.stream_ref(blob, out, 1),
+                 lambda: k3huf.encode_layer_dev(blob, out, out),
+                 lambda: k3huf.encode_layer_dev_static(blob, out),
+                 lambda: e8huf.decode(blob, lut, out, st),
+                 lambda: e8huf.decode_widen(blob, lut, out.view(torch.int16), out_kind=e8huf.OUT_BF16)):
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call()
+    # the checks themselves, on stand-ins that report a GPU device
+    class Fake:
+        def __init__(self, n, elem=1, contiguous=True):
+            self.is_cuda, self.n, self.elem, self.c = True, n, elem, contiguous
+
+        def is_contiguous(self):
+            return self.c
+
+        def element_size(self):
+            return self.elem
+
+        def numel(self):
+            return self.n
+    with pytest.raises(ValueError, match="at least 8192 bytes"):
+        k3huf._dev(Fake(4095, 2), "d_lut", 2 * k3huf.LUT_ENTRIES)
+    with pytest.raises(ValueError, match="contiguous"):
+        k3huf._dev(Fake(4096, 2, contiguous=False), "d_lut", 2 * k3huf.LUT_ENTRIES)
+    with pytest.raises(ValueError, match="elements of 2 bytes"):
+        k3huf._dev(Fake(8192, 1), "d_lut", elem=2)
+    with pytest.raises(ValueError, match="at least 4 bytes"):
+        k3huf._status(Fake(3, 1))
+    k3huf._dev(Fake(4096, 2), "d_lut", 2 * k3huf.LUT_ENTRIES, elem=2)
