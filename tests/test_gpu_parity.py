@@ -185,6 +185,37 @@ def test_partial_last_unit_in_passes(tail_syms):
     assert (got == O.decode_layer(blob)).all()
 
 
+def _shift_first_stripe(blob, pad=256):
+    """The same container with its stripe records and planes moved `pad`
+    bytes further from the header (stripe offsets and container size
+    adjusted): the format gives each stripe record's offset explicitly, so
+    it stays a valid container of the same layer."""
+    info = k3huf.layer_info(blob)
+    ns = info["n_stripes"]
+    so = np.frombuffer(bytes(blob[304: 304 + 8 * ns]), "<u8").astype(np.uint64)
+    out = np.concatenate([blob[: int(so[0])], np.zeros(pad, np.uint8), blob[int(so[0]):]])
+    out[304: 304 + 8 * ns] = np.frombuffer((so + np.uint64(pad)).tobytes(), np.uint8)
+    out[40:48] = np.frombuffer(np.uint64(blob.size + pad).tobytes(), np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("n_bytes,lanes", [(3 * 65536 + 514, 256), (3 * 65536 + 514, 64),
+                                           ((1 << 26) + 4 * 65536 + 6, 256)])
+def test_first_stripe_record_elsewhere(n_bytes, lanes):
+    """The packers put the first stripe record right after the padded
+    offset table, but the format gives each stripe record's offset
+    explicitly: a container that keeps them elsewhere (here 256 bytes
+    further) decodes through its stored offsets, in one-stripe and
+    two-stripe layers and both lane-chunk layouts."""
+    x = synth.small_random(n_bytes % 1000 + lanes, n_bytes)
+    blob = _shift_first_stripe(O.encode_layer(x, lanes))
+    assert (O.decode_layer(blob) == x).all()
+    say("first stripe record elsewhere", n_bytes, lanes)
+    got, st = gpu_decode(blob)
+    assert st == 0
+    assert (got == x).all()
+
+
 def test_heavy_parity():
     x, blob = oracle_container("heavy", synth.heavy)
     say("heavy", x.size)
