@@ -39,9 +39,12 @@ namespace {
 //     codes exceed the buffer, each lane gathers its own codes phase by
 //     phase instead; the layer's partial last unit is decoded in passes over
 //     consecutive lane ranges);
-//   - the even-plane bytes of all of a unit's phases (up to four: two whole
-//     128-byte lines per 256-symbol chunk) are requested together into
-//     registers as the unit starts;
+//   - the even-plane bytes of two of a unit's phases (two whole 128-byte
+//     lines per 256-symbol chunk) are requested together into registers
+//     before the first of them (all four phases' at once on the gather
+//     path; two at a time measured 5% faster on the 256 MiB heavy layer,
+//     whose first round starts every wave's loads at once, and the same on
+//     the trunk layer, but 3% slower on units that gather their codes);
 //   - each phase's 64 symbols per chunk are staged in LDS, so every output
 //     store instruction writes whole 128-byte lines.
 constexpr int kWaves = 7;
@@ -74,7 +77,10 @@ template <uint32_t L>
 struct Geo {
     static constexpr int kUnitSyms = kUnitLanes * int(L);                 // 16384 or 4096
     static constexpr int kPhases = int(L) / kPhase;                       // 4 or 1
-    static constexpr int kSuper = kPhases < 4 ? kPhases : 4;              // phases per even-plane prefetch
+    // phases per even-plane prefetch: two when the unit's codes are in the
+    // buffer, all four on the gather path
+    static constexpr int kSuperFill = kPhases < 2 ? kPhases : 2;
+    static constexpr int kSuperGather = kPhases < 4 ? kPhases : 4;
     static constexpr uint32_t kSubSyms = K3HUF_LANES * L;                 // 32768 or 8192
     static constexpr uint32_t kSubBytes = 2 * kSubSyms;
     static constexpr uint32_t kSubPerStripe = K3HUF_STRIPE_BYTES / kSubBytes;   // 1024 or 4096
@@ -106,8 +112,11 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // v * blocks + b first (consecutive positions on different CUs, so a small
 // layer spreads over the chip). Every later position is handed out on
 // demand: position T + x + G i goes to whichever wave of workgroup group x
-// (block mod G, G = min(8, blocks): one group per XCD) takes ticket i from
-// group x's counter. On-demand handout is needed because the waves of a CU
+// (block mod G, G = min(4, blocks): workgroup b runs on XCD b mod 8, so a
+// group spans two XCDs) takes ticket i from group x's counter. Four groups
+// measured best on the trunk layer (1.4% faster than one per XCD, which lets
+// one slow XCD finish late; two groups 0.5%; a single counter 27% slower, its
+// atomics queueing). On-demand handout is needed because the waves of a CU
 // do not progress at one rate: a SIMD issues from its oldest wave first (with
 // three waves per SIMD the first ran about 1.5 times as fast as the third),
 // and over many rounds the static order leaves some waves far behind. A
@@ -134,7 +143,7 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // units take the workgroup counters too, as they are as fast there.
 constexpr uint32_t kSchedSlots = 256;
 constexpr uint32_t kDynRounds = 5;   // device counters only for layers of more rounds of units than this
-constexpr uint32_t kGroupsPerSlot = 8;
+constexpr uint32_t kGroupsPerSlot = 4;
 constexpr uint32_t kCounterStride = 64;                               // words: one 256-byte line
 constexpr uint32_t kSlotWords = (kGroupsPerSlot + 1) * kCounterStride;  // tickets per group, workgroups done
 __device__ __attribute__((aligned(256))) uint32_t g_sched[kSlotWords * kSchedSlots];
@@ -318,7 +327,7 @@ template <uint32_t L, bool kGather, class After>
 __device__ __forceinline__ void decode_super(const uint32_t* tab, uint32_t* buf, uint8_t* stage,
                                              const Unit& un, int sp, int lane, LaneState& ls,
                                              After&& after) {
-    constexpr int kSuper = Geo<L>::kSuper;
+    constexpr int kSuper = kGather ? Geo<L>::kSuperGather : Geo<L>::kSuperFill;
     const int sub_line = lane >> 3, part = lane & 7;
     uint2 ev[kRounds][kSuper];
     // the super-phase's even-plane bytes: whole lines per chunk
@@ -383,7 +392,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const uint32_t*
                                             uint8_t* stage, const Unit& un, int j0,
                                             uint32_t lane_start, uint32_t lane_bits, int lane,
                                             Mid&& mid, Late&& late) {
-    constexpr int kPhases = Geo<L>::kPhases, kSuper = Geo<L>::kSuper;
+    constexpr int kPhases = Geo<L>::kPhases, kSuper = kGather ? Geo<L>::kSuperGather : Geo<L>::kSuperFill;
     // the buffer starts at least one dword before the lane's first code, so
     // pm1 >= 0
     LaneState ls = {lane_start - 32u * uint32_t(j0) - 1u, 0u, 0u, 0u, lane_start};
